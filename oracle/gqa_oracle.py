@@ -1,0 +1,259 @@
+"""Oracle: a plain, slow float64 CPU definition of rotary grouped-query causal attention.
+
+TEST INFRASTRUCTURE, NOT THE PRODUCT.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The HIP library under
+``gqa_scaled_rope_amd/`` never imports, links or calls it, and this module imports nothing from
+there: the two sides share no code.  Inputs reach both sides from ``synth/`` (seeded draws only).
+
+Every function restates a definition from one of three web pages (cited by title and section):
+
+  [Models] "42. More models: a registry, scaled RoPE, sliding windows and latent attention"
+           (a chapter of a from-scratch LLM inference-engine tutorial)
+  [Ster]   "Model resolution" (documentation of the Ster runtime), section "Overview"
+  [Guide]  "MoE, optimisers, decoding -- every line, every shape." (a study guide)
+
+Where the pages leave a step open, the reading taken is stated at the function that takes it.
+All arithmetic is numpy float64 on the exact values the GPU receives (inputs already rounded to the
+run dtype), with library matmul / exp / tanh / sin / cos as the only primitives.
+
+Pins (tests/test_oracle_pins.py, all CPU): the page's worked RoPE wavelength; position-squeezing
+of linear scaling; llama3 per-band behaviour; complex-multiplication form of the rotation; the
+half-split pairing of the study guide; deinterleave equivalence; norm preservation; relative
+position; RMS of the normed vector; soft-cap limits; integer mask probe; window and GQA
+equivalences; decode == last prefill row; chunked prefill == tail of full prefill; brute-force
+scalar loops; and torch's CPU scaled_dot_product_attention in float64.  No function here is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+ROPE_KINDS = ("default", "linear", "llama3")
+ROT_STYLES = ("half", "interleaved")
+
+
+# ----------------------------------------------------------------------------------------------
+# Rotary frequencies and angles
+# ----------------------------------------------------------------------------------------------
+def rope_inv_freq(rotary_dim, theta, kind="default", factor=1.0, low_freq_factor=1.0,
+                  high_freq_factor=4.0, original_max_position_embeddings=8192.0):
+    """Rotation frequency of each of the rotary_dim/2 feature pairs.
+
+    [Models] "Scaled RoPE": pair i turns by p * theta^(-2i/d) at position p; d here is the
+    rotated width (reading for partial rotation: [Ster] "Overview" rotates only the
+    partial_rotary_factor share of each head, so the frequencies run over that share).
+      default: theta^(-2i/d)
+      linear:  every frequency divided by the extension factor (position p looks like p/factor)
+      llama3:  pairs with wavelength shorter than original/high_freq_factor are kept, pairs longer
+               than original/low_freq_factor are divided by factor, and in between the two are
+               blended linearly with weight s = (original/wavelength - low)/(high - low) on the
+               kept value.
+    The attention factor that multiplies cos and sin is 1 for all three kinds.
+    """
+    if rotary_dim < 0 or rotary_dim % 2:
+        raise ValueError(f"rotary_dim must be even and >= 0, got {rotary_dim}")
+    if kind not in ROPE_KINDS:
+        raise ValueError(f"RoPE type {kind!r} is not implemented")
+    half = rotary_dim // 2
+    out = np.empty(half, dtype=np.float64)
+    for i in range(half):
+        base = float(theta) ** (-2.0 * i / rotary_dim)
+        if kind == "default":
+            f = base
+        elif kind == "linear":
+            f = base / factor
+        else:
+            old, low, high = (float(original_max_position_embeddings), float(low_freq_factor),
+                              float(high_freq_factor))
+            wavelength = 2.0 * math.pi / base
+            if wavelength < old / high:          # fast pair: kept
+                f = base
+            elif wavelength > old / low:         # slow pair: interpolated
+                f = base / factor
+            else:                                # between: linear blend
+                s = (old / wavelength - low) / (high - low)
+                f = (1.0 - s) * base / factor + s * base
+        out[i] = f
+    return out
+
+
+def rope_angles(positions, inv_freq):
+    """Angle of pair i at position p: p * inv_freq[i] ([Models] "Scaled RoPE", rope_tables;
+    [Guide] §4 Rotary).  Returns positions.shape + (len(inv_freq),)."""
+    return np.asarray(positions, dtype=np.float64)[..., None] * np.asarray(inv_freq, np.float64)
+
+
+# ----------------------------------------------------------------------------------------------
+# Per-row operations on head vectors
+# ----------------------------------------------------------------------------------------------
+def rms_norm(x, weight, eps):
+    """[Guide] §3.2 RMSNorm: x / sqrt(mean(x^2) + eps), times the gain, over the last axis.
+
+    Reading: the page rounds to the input dtype before the gain; the oracle keeps everything
+    in float64 (exact definition), and the rounding difference is far inside the tolerance."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(weight, dtype=np.float64)
+
+
+def rotate(x, positions, inv_freq, style="half"):
+    """Rotate the first R = 2*len(inv_freq) features of each row of x by its position.
+
+    half:        pair (i, i + R/2)      ([Guide] §4 Rotary: feature i with feature i + hd/2)
+    interleaved: pair (2i, 2i + 1)      ([Models] "Serving it": adjacent pairs; [Ster] "Overview")
+    Each pair (a, b) at angle t becomes (a cos t - b sin t, a sin t + b cos t).  Features at
+    index >= R pass through unchanged ([Ster] "Overview": only that share rotates).
+    positions must broadcast to x.shape[:-1]."""
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    half = len(inv_freq)
+    if half == 0:
+        return out
+    R = 2 * half
+    if R > x.shape[-1]:
+        raise ValueError("rotary width exceeds head_dim")
+    ang = rope_angles(np.broadcast_to(positions, x.shape[:-1]), inv_freq)
+    c, s = np.cos(ang), np.sin(ang)
+    if style == "half":
+        a, b = x[..., :half], x[..., half:R]
+        out[..., :half] = a * c - b * s
+        out[..., half:R] = a * s + b * c
+    elif style == "interleaved":
+        a, b = x[..., 0:R:2], x[..., 1:R:2]
+        out[..., 0:R:2] = a * c - b * s
+        out[..., 1:R:2] = a * s + b * c
+    else:
+        raise ValueError(f"unknown rotation style {style!r}")
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# Mask and softmax core
+# ----------------------------------------------------------------------------------------------
+def allowed_mask(query_positions, key_positions, window):
+    """May query at position qp attend key at position kp?
+
+    Causal by positions, not indices ([Models] "What differs": causal_attention takes positions
+    and key_positions).  Sliding window ([Models] "Sliding windows"): keys more than w - 1
+    positions back are masked, so a query sees at most w keys including itself; w = 0 means
+    no window.  Returns a [len(qp), len(kp)] bool array."""
+    qp = np.asarray(query_positions, dtype=np.int64)[:, None]
+    kp = np.asarray(key_positions, dtype=np.int64)[None, :]
+    ok = kp <= qp
+    if window > 0:
+        ok &= (qp - kp) <= (window - 1)
+    return ok
+
+
+def softmax_attention(q, k, v, allowed, scale, softcap=0.0):
+    """Masked softmax attention of one head: out_i = sum_j p_ij v_j with
+    p_i = softmax over allowed j of s_ij, s_ij = scale * <q_i, k_j> ([Guide] §3.4 Attention).
+
+    Soft-cap (reading; the pages name it without a formula, [Ster] "Overview"): s <- cap *
+    tanh(s / cap) after scaling and before masking; cap = 0 means off.
+    Max subtraction as in [Guide] §2.3.  A row with no allowed key has output 0 (reading:
+    [Guide] §3.7 notes that such a row would otherwise be NaN)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    s = scale * (q @ k.T)
+    if softcap > 0.0:
+        s = softcap * np.tanh(s / softcap)
+    out = np.zeros((q.shape[0], v.shape[1]), dtype=np.float64)
+    any_allowed = allowed.any(axis=1)
+    if not any_allowed.any():
+        return out
+    s_masked = np.where(allowed, s, -np.inf)
+    m = np.max(s_masked[any_allowed], axis=1, keepdims=True)
+    p = np.where(allowed[any_allowed], np.exp(s[any_allowed] - m), 0.0)
+    out[any_allowed] = (p @ v) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# The two entry points
+# ----------------------------------------------------------------------------------------------
+def _scale(head_dim, scale):
+    # [Guide] §3.4: scores divided by sqrt(head_dim); [Ster] "Overview" lets a family replace it.
+    return 1.0 / math.sqrt(head_dim) if not scale else float(scale)
+
+
+def attn_prefill(q, k, v, positions, key_positions, *, inv_freq, style="half", n_cached=0,
+                 window=0, q_norm_w=None, k_norm_w=None, eps=1e-6, scale=0.0, softcap=0.0,
+                 query_rows=None, heads=None, batches=None):
+    """Causal prefill of one layer: [Models] "What differs" (DecoderAttention.forward).
+
+    q [B, L, Hq, D], k and v [B, S, Hkv, D], positions [B, L], key_positions [B, S].
+    Steps, in the page's order: per-head RMSNorm of q and of the new keys (when weights are
+    given), then rotation of q at positions and of new keys at key_positions; keys j < n_cached
+    come from the cache and are used as stored (already normed and rotated), values are never
+    rotated.  Query head h reads KV head h // (Hq/Hkv) (reading: consecutive query heads share a
+    KV head, i.e. K/V repeated with repeat_interleave, [Guide] §1.6).  Then masked softmax
+    attention per head.  Returns out [B', L', Hq', D] for the selected batches, rows and heads.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, L, Hq, D = q.shape
+    S, Hkv = k.shape[1], k.shape[2]
+    if Hq % Hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    G = Hq // Hkv
+    positions = np.broadcast_to(np.asarray(positions, np.int64), (B, L))
+    key_positions = np.broadcast_to(np.asarray(key_positions, np.int64), (B, S))
+    batches = range(B) if batches is None else batches
+    rows = np.arange(L) if query_rows is None else np.asarray(query_rows)
+    heads = range(Hq) if heads is None else heads
+    sc = _scale(D, scale)
+    out = np.zeros((len(batches), len(rows), len(heads), D), dtype=np.float64)
+    for bi, b in enumerate(batches):
+        qb = q[b, rows]                                   # [L', Hq, D]
+        kb = k[b].copy()                                  # [S, Hkv, D]
+        if q_norm_w is not None:
+            qb = rms_norm(qb, q_norm_w, eps)
+        qb = rotate(qb, positions[b, rows][:, None], inv_freq, style)
+        new = slice(n_cached, S)
+        kn = kb[new]
+        if k_norm_w is not None:
+            kn = rms_norm(kn, k_norm_w, eps)
+        kb[new] = rotate(kn, key_positions[b, new][:, None], inv_freq, style)
+        allowed = allowed_mask(positions[b, rows], key_positions[b], window)
+        for hi, h in enumerate(heads):
+            g = h // G
+            out[bi, :, hi] = softmax_attention(qb[:, h], kb[:, g], v[b, :, g], allowed, sc, softcap)
+    return out
+
+
+def attn_decode_one(q, k, v, n, *, inv_freq, style="half", window=0, q_norm_w=None, eps=1e-6,
+                    scale=0.0, softcap=0.0, heads=None):
+    """Single-token decode of one sequence against its cache ([Guide] §3.3 KVCache, §3.7).
+
+    q [Hq, D]; k, v [Hkv, >= n, D] hold the sequence's cache rows, slot j at position j, already
+    normed and rotated (the new token's row is in slot n - 1: [Models] "What differs" rotates
+    then appends).  The query sits at position n - 1: q is normed (when weighted) and rotated
+    there; every cached key is in its past, so only the window can mask.  Returns [Hq', D]."""
+    q = np.asarray(q, np.float64)
+    Hq, D = q.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    heads = range(Hq) if heads is None else heads
+    pos = n - 1
+    qq = q if q_norm_w is None else rms_norm(q, q_norm_w, eps)
+    qq = rotate(qq, np.full(Hq, pos), inv_freq, style)
+    allowed = allowed_mask([pos], np.arange(n), window)
+    sc = _scale(D, scale)
+    out = np.zeros((len(heads), D), dtype=np.float64)
+    for hi, h in enumerate(heads):
+        g = h // G
+        kk = np.asarray(k[g, :n], np.float64)
+        vv = np.asarray(v[g, :n], np.float64)
+        out[hi] = softmax_attention(qq[h:h + 1], kk, vv, allowed, sc, softcap)[0]
+    return out
+
+
+def attn_decode(q, kcache, vcache, lens, **kw):
+    """attn_decode_one over a batch: q [B, Hq, D], caches [B, Hkv, Smax, D], lens [B]."""
+    return np.stack([attn_decode_one(q[b], kcache[b], vcache[b], int(lens[b]), **kw)
+                     for b in range(len(lens))])
