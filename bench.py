@@ -1,0 +1,301 @@
+"""Benchmark of the rotary grouped-query attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one pass of the whole hot path over one batch of synthetic input: the rotary tables
+(gqa_rope_tables) followed by the prefill attention call (gqa_attn_prefill), inputs resident in
+HBM.  The default workload is the Qwen3-style prefill (B=4, L=S=2048, Hq=32, Hkv=8, D=128,
+per-head q/k RMSNorm, full causal).  The split-KV decode workload (64 sequences, cache lengths
+U[1024, 32768], llama3 rope) is timed in the same run and reported under "decode".
+
+Prints ONE JSON line on stdout (progress goes to stderr).  FLOPs count only allowed
+(query, key) pairs, 4 * D per pair per head; decode bytes are the K and V rows each sequence
+actually reads plus q, out and lens.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
+METRIC = "prefill attn TFLOP/s (% MFMA peak); decode KV GB/s (% HBM peak)"
+
+
+# ---- work models (pure functions; pinned by tests/test_abi_cpu.py) -----------------------------
+def allowed_pairs(L, S, window, n_cached):
+    """Allowed (query, key) pairs of one (sequence, head): queries at positions S-L..S-1 when
+    keys before them are cached, else 0..L-1; keys at 0..S-1."""
+    start = S - L if n_cached else 0
+
+    def upto(n):  # sum over positions p < n of min(p + 1, w), w = infinity when 0
+        if n <= 0:
+            return 0
+        if window <= 0 or n <= window:
+            return n * (n + 1) // 2
+        return window * (window + 1) // 2 + (n - window) * window
+    return upto(start + L) - upto(start)
+
+
+def prefill_flops(wl):
+    return 4 * wl.B * wl.Hq * wl.D * allowed_pairs(wl.L, wl.S, wl.window, wl.n_cached)
+
+
+def kv_bytes_per_token_per_layer(kv_heads, head_dim, bytes_per_elem):
+    return 2 * kv_heads * head_dim * bytes_per_elem
+
+
+def decode_bytes(wl, lens):
+    eb = 2 if wl.dtype == "bf16" else 4
+    keys = sum(min(int(n), wl.window) if wl.window else int(n) for n in lens)
+    return (keys * kv_bytes_per_token_per_layer(wl.Hkv, wl.D, eb)
+            + 2 * wl.B * wl.Hq * wl.D * eb + 4 * wl.B)
+
+
+# ---- helpers ---------------------------------------------------------------------------------
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _rope_spec(g, wl):
+    return g.RopeSpec(wl.rotary_dim, wl.rope_kind, wl.theta, wl.factor, wl.low_freq_factor,
+                      wl.high_freq_factor, wl.original_max_pos)
+
+
+def _prefill_setup(wl, torch, g):
+    from synth import device_normal
+    dev = "cuda"
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    q = device_normal((wl.B, wl.L, wl.Hq, wl.D), wl.seed * 10 + 1, wl.dtype)
+    k = device_normal((wl.B, wl.S, wl.Hkv, wl.D), wl.seed * 10 + 2, wl.dtype)
+    v = device_normal((wl.B, wl.S, wl.Hkv, wl.D), wl.seed * 10 + 3, wl.dtype)
+    qw = kw = None
+    if wl.qk_norm:
+        qw = (1.0 + 0.02 * device_normal((wl.D,), wl.seed * 10 + 4, "f32")).to(dt)
+        kw = (1.0 + 0.02 * device_normal((wl.D,), wl.seed * 10 + 5, "f32")).to(dt)
+    start = wl.S - wl.L if wl.n_cached else 0
+    pos = torch.arange(start, start + wl.L, dtype=torch.int32, device=dev)
+    kpos = torch.arange(wl.S, dtype=torch.int32, device=dev)
+    table_len = wl.S
+    cos = torch.empty((table_len, wl.rotary_dim // 2), dtype=torch.float32, device=dev)
+    sin = torch.empty_like(cos)
+    cfg = g.AttnConfig(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
+                       wl.qk_norm, wl.eps, qw, kw, 0.0, wl.softcap)
+    out = torch.empty_like(q)
+    return dict(q=q, k=k, v=v, qw=qw, kw=kw, pos=pos, kpos=kpos, cos=cos, sin=sin, cfg=cfg,
+                out=out, table_len=table_len)
+
+
+def run_prefill(wl, steps, warmup, torch, g):
+    x = _prefill_setup(wl, torch, g)
+    spec = _rope_spec(g, wl)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        g.rope_tables(spec, x["table_len"], x["cos"], x["sin"])
+        g.attn_prefill(x["cfg"], x["q"], x["k"], x["v"], x["pos"], x["kpos"], wl.n_cached,
+                       wl.window, x["out"])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # whole-step timing
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    # per-launch timing of the attention kernel alone
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        g.rope_tables(spec, x["table_len"], x["cos"], x["sin"])
+        evs[i][0].record(stream)
+        g.attn_prefill(x["cfg"], x["q"], x["k"], x["v"], x["pos"], x["kpos"], wl.n_cached,
+                       wl.window, x["out"])
+        evs[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    kern_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return x, total_ms / steps, sum(kern_ms) / len(kern_ms), kern_ms[len(kern_ms) // 2]
+
+
+def run_decode(wl, steps, warmup, torch, g):
+    from synth import decode_device_inputs
+    x = decode_device_inputs(wl)
+    spec = _rope_spec(g, wl)
+    cos, sin = g.rope_tables(spec, wl.S)
+    cfg = g.AttnConfig(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
+                       wl.qk_norm, wl.eps, x.get("qw"), x.get("kw"), 0.0, wl.softcap)
+    ws = torch.empty(g.decode_workspace_bytes(cfg, wl.B, wl.S), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(x["q"])
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        g.attn_decode(cfg, x["q"], x["k"], x["v"], x["lens"], wl.window, out, ws)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        g.attn_decode(cfg, x["q"], x["k"], x["v"], x["lens"], wl.window, out, ws)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    x.update(cfg=cfg, out=out, cos=cos, sin=sin)
+    return x, sum(ms) / len(ms), ms[len(ms) // 2]
+
+
+def cpu_baseline_prefill(wl, x, torch, rows=256, max_s=30.0):
+    """Time the oracle on a bounded sample (sequence 0, the last `rows` query rows, all heads),
+    check the GPU output on the same sample, and scale the rate to TFLOP/s."""
+    import numpy as np
+    import oracle
+    b = 0
+    q = x["q"][b:b + 1].float().cpu().numpy()
+    k = x["k"][b:b + 1].float().cpu().numpy()
+    v = x["v"][b:b + 1].float().cpu().numpy()
+    qw = x["qw"].float().cpu().numpy() if x["qw"] is not None else None
+    kw = x["kw"].float().cpu().numpy() if x["kw"] is not None else None
+    pos = x["pos"].cpu().numpy()[None]
+    kpos = x["kpos"].cpu().numpy()[None]
+    sel = np.arange(wl.L - rows, wl.L)
+    inv = oracle.rope_inv_freq(wl.rotary_dim, wl.theta, wl.rope_kind, wl.factor,
+                               wl.low_freq_factor, wl.high_freq_factor, wl.original_max_pos)
+    t = time.perf_counter()
+    ref = oracle.attn_prefill(q, k, v, pos, kpos, inv_freq=inv, style=wl.style,
+                              n_cached=wl.n_cached, window=wl.window, q_norm_w=qw, k_norm_w=kw,
+                              eps=wl.eps, softcap=wl.softcap, query_rows=sel)
+    dt = time.perf_counter() - t
+    got = x["out"][b, sel].float().cpu().numpy()
+    err = np.abs(got[None] - ref)
+    ok = bool(np.all(err <= 2e-2 + 2e-2 * np.abs(ref)))
+    start = wl.S - wl.L if wl.n_cached else 0
+    qp = start + sel
+    pairs = sum(min(int(p) + 1, wl.window) if wl.window else int(p) + 1 for p in qp)
+    flops = 4 * wl.Hq * wl.D * pairs
+    threads = _blas_threads()
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"sequence 0, last {rows} query rows x {wl.Hq} heads of {wl.name} "
+                       f"({flops / 1e9:.2f} GFLOP, {dt:.1f} s)",
+                parity_ok=ok, max_abs_err=float(err.max()))
+
+
+def cpu_baseline_decode(wl, x, torch, nseq=2):
+    import numpy as np
+    import oracle
+    lens = x["lens"].cpu().numpy()
+    inv = oracle.rope_inv_freq(wl.rotary_dim, wl.theta, wl.rope_kind, wl.factor,
+                               wl.low_freq_factor, wl.high_freq_factor, wl.original_max_pos)
+    eb = 2
+    t_total, nbytes, ok, maxerr = 0.0, 0, True, 0.0
+    for b in range(nseq):
+        n = int(lens[b])
+        kk = x["k"][b, :, :n].float().cpu().numpy()
+        vv = x["v"][b, :, :n].float().cpu().numpy()
+        qq = x["q"][b].float().cpu().numpy()
+        t = time.perf_counter()
+        ref = oracle.attn_decode_one(qq, kk, vv, n, inv_freq=inv, style=wl.style,
+                                     window=wl.window, softcap=wl.softcap)
+        t_total += time.perf_counter() - t
+        got = x["out"][b].float().cpu().numpy()
+        err = np.abs(got - ref)
+        maxerr = max(maxerr, float(err.max()))
+        ok &= bool(np.all(err <= 2e-2 + 2e-2 * np.abs(ref)))
+        keys = min(n, wl.window) if wl.window else n
+        nbytes += keys * kv_bytes_per_token_per_layer(wl.Hkv, wl.D, eb)
+    return dict(value=nbytes / t_total / 1e9, unit="GB/s", cores=_blas_threads(), kind="oracle",
+                sample=f"sequences 0..{nseq - 1} of {wl.name} ({nbytes / 1e6:.0f} MB of K/V, "
+                       f"{t_total:.1f} s)", parity_ok=ok, max_abs_err=maxerr)
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        n = max((i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"), default=1)
+        return int(n)
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_prefill_bf16")
+    ap.add_argument("--decode-workload", default="llama31_decode_bf16")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus "
+              f"{args.gpus}", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import gqa_scaled_rope_amd as g
+    from synth import WORKLOADS
+
+    g.library()
+    wl = WORKLOADS[args.workload]
+    log(f"[bench] prefill workload {wl.name}: warmup {args.warmup}, steps {args.steps}")
+    x, step_ms, kern_ms, kern_med = run_prefill(wl, args.steps, args.warmup, torch, g)
+    flops = prefill_flops(wl)
+    value = flops / (step_ms * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    log(f"[bench] step {step_ms:.3f} ms, attention kernel {kern_ms:.3f} ms "
+        f"-> {achieved:.1f} TFLOP/s")
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) draws, device-generated)",
+        "config": {"workload": wl.name, "B": wl.B, "L": wl.L, "S": wl.S, "Hq": wl.Hq,
+                   "Hkv": wl.Hkv, "head_dim": wl.D, "rotary_dim": wl.rotary_dim,
+                   "rope": wl.rope_kind, "theta": wl.theta, "qk_norm": wl.qk_norm,
+                   "window": wl.window, "softcap": wl.softcap, "n_cached": wl.n_cached,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel",
+                     "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel_ms_mean": round(kern_ms, 4),
+                     "kernel_ms_median": round(kern_med, 4), "algorithmic_flop": flops},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline_prefill(wl, x, torch)
+        log(f"[bench] cpu baseline {line['cpu_baseline']['value']:.4f} TFLOP/s")
+    del x
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        dwl = WORKLOADS[args.decode_workload]
+        log(f"[bench] decode workload {dwl.name}")
+        dx, dms, dmed = run_decode(dwl, args.steps, args.warmup, torch, g)
+        lens = dx["lens"].cpu().tolist()
+        nbytes = decode_bytes(dwl, lens)
+        gbs = nbytes / (dms * 1e-3) / 1e9
+        log(f"[bench] decode {dms:.3f} ms -> {gbs:.0f} GB/s")
+        dec = {"workload": dwl.name, "value": round(gbs, 1), "unit": "GB/s",
+               "ms_per_call": round(dms, 4), "algorithmic_bytes": nbytes,
+               "roofline": {"bound": "hbm", "kernel": "decode_split_kernel + decode_combine_kernel",
+                            "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                            "kernel_ms_mean": round(dms, 4), "kernel_ms_median": round(dmed, 4)}}
+        if not args.no_cpu_baseline:
+            dec["cpu_baseline"] = cpu_baseline_decode(dwl, dx, torch)
+        line["decode"] = dec
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,289 @@
+"""Python binding of libgqa_rope (rotary grouped-query causal attention for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+``libgqa_rope.so`` behind the C ABI declared in ``include/gqa_rope.h``.  PyTorch supplies device
+memory and the current stream.  There is no fallback: if the library is not built, every call
+raises.
+
+The functions mirror the C entry points: :func:`rope_tables`, :func:`attn_prefill`,
+:func:`attn_decode`, :func:`decode_workspace_bytes`, :func:`rope_inv_freq`, :func:`last_error`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+__all__ = [
+    "GQAError", "RopeSpec", "AttnConfig", "library", "rope_inv_freq", "rope_tables",
+    "attn_prefill", "attn_decode", "decode_workspace_bytes", "last_error", "set_kernel_policy",
+    "LIB_PATH", "EXPORTS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_rope.so")
+
+GQA_F32, GQA_BF16 = 0, 1
+ROPE_KINDS = {"default": 0, "linear": 1, "llama3": 2}
+ROT_STYLES = {"half": 0, "interleaved": 1}
+STATUS = {0: "GQA_OK", 1: "GQA_E_NULL", 2: "GQA_E_SHAPE", 3: "GQA_E_DTYPE",
+          4: "GQA_E_UNSUPPORTED", 5: "GQA_E_WORKSPACE", 6: "GQA_E_HIP", 7: "GQA_E_VALUE"}
+
+
+class GQAError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class _RopeParams(ctypes.Structure):
+    _fields_ = [("rotary_dim", ctypes.c_int32), ("kind", ctypes.c_int32),
+                ("theta", ctypes.c_double), ("factor", ctypes.c_double),
+                ("low_freq_factor", ctypes.c_double), ("high_freq_factor", ctypes.c_double),
+                ("original_max_pos", ctypes.c_double)]
+
+
+class _AttnCfg(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("rotary_dim", ctypes.c_int32), ("rot_style", ctypes.c_int32),
+                ("cos_table", ctypes.c_void_p), ("sin_table", ctypes.c_void_p),
+                ("table_len", ctypes.c_int32), ("qk_norm", ctypes.c_int32),
+                ("eps", ctypes.c_double), ("q_norm_w", ctypes.c_void_p),
+                ("k_norm_w", ctypes.c_void_p), ("scale", ctypes.c_double),
+                ("softcap", ctypes.c_double)]
+
+
+_P = ctypes.c_void_p
+_I32, _I64, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+# name -> (restype, argtypes); every function declared in include/gqa_rope.h
+EXPORTS = {
+    "gqa_rope_tables": (_I32, [ctypes.POINTER(_RopeParams), _I32, _P, _P, _P]),
+    "gqa_rope_inv_freq": (_I32, [ctypes.POINTER(_RopeParams), ctypes.POINTER(ctypes.c_double)]),
+    "gqa_attn_prefill": (_I32, [ctypes.POINTER(_AttnCfg), _P, _P, _P, _P, _I64, _P, _I64, _I32,
+                                _I32, _I32, _I32, _I32, _P, _P]),
+    "gqa_decode_workspace_bytes": (_SZ, [ctypes.POINTER(_AttnCfg), _I32, _I32]),
+    "gqa_attn_decode": (_I32, [ctypes.POINTER(_AttnCfg), _P, _P, _P, _P, _I32, _I32, _I32, _P, _P,
+                               _SZ, _P]),
+    "gqa_set_kernel_policy": (_I32, [_I32]),
+    "gqa_last_error": (ctypes.c_char_p, []),
+    "gqa_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def library():
+    """Load libgqa_rope.so (built in-tree by __graft_entry__.build()); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as "
+                               f"g; g.build()'` (hipcc, gfx950)")
+        # torch ships its own HIP runtime (same soname as ROCm's).  Loading torch first makes the
+        # library resolve to that runtime, so torch's streams and allocations are valid in it; the
+        # other order would bring a second HIP runtime into the process.
+        import torch  # noqa: F401
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def last_error() -> str:
+    return library().gqa_last_error().decode()
+
+
+def _check(status):
+    if status != 0:
+        raise GQAError(status, last_error())
+
+
+def set_kernel_policy(policy: int):
+    """0: MFMA kernels where they apply (default); 1: generic kernels for everything."""
+    _check(library().gqa_set_kernel_policy(int(policy)))
+
+
+# ------------------------------------------------------------------------------------------------
+@dataclass
+class RopeSpec:
+    rotary_dim: int
+    kind: str = "default"
+    theta: float = 1e4
+    factor: float = 1.0
+    low_freq_factor: float = 1.0
+    high_freq_factor: float = 4.0
+    original_max_pos: float = 8192.0
+
+    def c_struct(self):
+        if self.kind not in ROPE_KINDS:
+            raise GQAError(4, f"RoPE type {self.kind!r} is not implemented")
+        return _RopeParams(self.rotary_dim, ROPE_KINDS[self.kind], self.theta, self.factor,
+                           self.low_freq_factor, self.high_freq_factor, self.original_max_pos)
+
+
+def rope_inv_freq(spec: RopeSpec):
+    """Host copy of the pair frequencies the tables use (list of R/2 floats)."""
+    st = spec.c_struct()
+    buf = (ctypes.c_double * max(1, spec.rotary_dim // 2))()
+    _check(library().gqa_rope_inv_freq(ctypes.byref(st), buf))
+    return list(buf)[: spec.rotary_dim // 2]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, shape, dtype, device=True):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise GQAError(2, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise GQAError(3, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise GQAError(2, f"{name} must be contiguous")
+    if device and not t.is_cuda:
+        raise GQAError(1, f"{name} must be a device tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def rope_tables(spec: RopeSpec, table_len: int, cos=None, sin=None, stream=None):
+    """cos/sin tables [table_len, R/2] fp32 on the current device (allocated if not given)."""
+    torch = _torch()
+    half = spec.rotary_dim // 2
+    if cos is None:
+        cos = torch.empty((table_len, half), dtype=torch.float32, device="cuda")
+    if sin is None:
+        sin = torch.empty((table_len, half), dtype=torch.float32, device="cuda")
+    pc = _need(cos, "cos", (table_len, half), torch.float32)
+    ps = _need(sin, "sin", (table_len, half), torch.float32)
+    st = spec.c_struct()
+    _check(library().gqa_rope_tables(ctypes.byref(st), int(table_len), pc, ps, _stream(stream)))
+    return cos, sin
+
+
+# ------------------------------------------------------------------------------------------------
+@dataclass
+class AttnConfig:
+    dtype: str                      # "bf16" | "f32"
+    head_dim: int
+    num_q_heads: int
+    num_kv_heads: int
+    rotary_dim: int = 0
+    rot_style: str = "half"
+    cos: Optional[object] = None    # device tensor [table_len, R/2] fp32
+    sin: Optional[object] = None
+    qk_norm: bool = False
+    eps: float = 1e-6
+    q_norm_w: Optional[object] = None   # device tensor [D] in dtype
+    k_norm_w: Optional[object] = None
+    scale: float = 0.0
+    softcap: float = 0.0
+
+    @property
+    def torch_dtype(self):
+        torch = _torch()
+        return {"bf16": torch.bfloat16, "f32": torch.float32}[self.dtype]
+
+    def c_struct(self):
+        torch = _torch()
+        if self.dtype not in ("bf16", "f32"):
+            raise GQAError(3, f"dtype must be 'bf16' or 'f32', got {self.dtype!r}")
+        if self.rot_style not in ROT_STYLES:
+            raise GQAError(7, f"rot_style must be 'half' or 'interleaved', got {self.rot_style!r}")
+        half = self.rotary_dim // 2
+        pc = ps = None
+        tl = 0
+        if self.rotary_dim > 0:
+            if self.cos is None or self.sin is None:
+                raise GQAError(1, "cos/sin tables are required when rotary_dim > 0")
+            tl = int(self.cos.shape[0])
+            pc = _need(self.cos, "cos", (tl, half), torch.float32).value
+            ps = _need(self.sin, "sin", (tl, half), torch.float32).value
+        qw = kw = None
+        if self.qk_norm:
+            if self.q_norm_w is None or self.k_norm_w is None:
+                raise GQAError(1, "q_norm_w and k_norm_w are required when qk_norm is set")
+            qw = _need(self.q_norm_w, "q_norm_w", (self.head_dim,), self.torch_dtype).value
+            kw = _need(self.k_norm_w, "k_norm_w", (self.head_dim,), self.torch_dtype).value
+        return _AttnCfg(GQA_BF16 if self.dtype == "bf16" else GQA_F32, self.head_dim,
+                        self.num_q_heads, self.num_kv_heads, self.rotary_dim,
+                        ROT_STYLES[self.rot_style], pc, ps, tl, int(bool(self.qk_norm)), self.eps,
+                        qw, kw, self.scale, self.softcap)
+
+
+def attn_prefill(cfg: AttnConfig, q, k, v, positions, key_positions, n_cached=0, window=0,
+                 out=None, stream=None):
+    """q [B, L, Hq, D], k/v [B, S, Hkv, D], positions [B, L] or [L], key_positions [B, S] or [S]
+    (int32, nondecreasing).  Returns out [B, L, Hq, D]."""
+    torch = _torch()
+    B, L, Hq, D = q.shape
+    S = k.shape[1]
+    dt = cfg.torch_dtype
+    pq = _need(q, "q", (B, L, cfg.num_q_heads, cfg.head_dim), dt)
+    pk = _need(k, "k", (B, S, cfg.num_kv_heads, cfg.head_dim), dt)
+    pv = _need(v, "v", (B, S, cfg.num_kv_heads, cfg.head_dim), dt)
+    if positions.dim() == 1:
+        pp, pstride = _need(positions, "positions", (L,), torch.int32), 0
+    else:
+        pp, pstride = _need(positions, "positions", (B, L), torch.int32), L
+    if key_positions.dim() == 1:
+        pkp, kstride = _need(key_positions, "key_positions", (S,), torch.int32), 0
+    else:
+        pkp, kstride = _need(key_positions, "key_positions", (B, S), torch.int32), S
+    if out is None:
+        out = torch.empty_like(q)
+    po = _need(out, "out", tuple(q.shape), dt)
+    c = cfg.c_struct()
+    _check(library().gqa_attn_prefill(ctypes.byref(c), pq, pk, pv, pp, pstride, pkp, kstride, B, L,
+                                      S, int(n_cached), int(window), po, _stream(stream)))
+    return out
+
+
+def decode_workspace_bytes(cfg: AttnConfig, B: int, Smax: int) -> int:
+    c = cfg.c_struct()
+    n = library().gqa_decode_workspace_bytes(ctypes.byref(c), int(B), int(Smax))
+    err = last_error()
+    if n == 0 and err:
+        raise GQAError(2, err)
+    return int(n)
+
+
+def attn_decode(cfg: AttnConfig, q, kcache, vcache, lens, window=0, out=None, workspace=None,
+                stream=None):
+    """q [B, Hq, D], kcache/vcache [B, Hkv, Smax, D], lens [B] int32.  Returns out [B, Hq, D]."""
+    torch = _torch()
+    B = q.shape[0]
+    Smax = kcache.shape[2]
+    dt = cfg.torch_dtype
+    pq = _need(q, "q", (B, cfg.num_q_heads, cfg.head_dim), dt)
+    pk = _need(kcache, "kcache", (B, cfg.num_kv_heads, Smax, cfg.head_dim), dt)
+    pv = _need(vcache, "vcache", (B, cfg.num_kv_heads, Smax, cfg.head_dim), dt)
+    pl = _need(lens, "lens", (B,), torch.int32)
+    if out is None:
+        out = torch.empty_like(q)
+    po = _need(out, "out", tuple(q.shape), dt)
+    need = decode_workspace_bytes(cfg, B, Smax)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    pw, nbytes = ctypes.c_void_p(None), 0
+    if workspace is not None:
+        pw = _need(workspace, "workspace", (workspace.numel(),), torch.uint8)
+        nbytes = workspace.numel()
+    c = cfg.c_struct()
+    _check(library().gqa_attn_decode(ctypes.byref(c), pq, pk, pv, pl, B, Smax, int(window), po, pw,
+                                     nbytes, _stream(stream)))
+    return out

@@ -1,0 +1,328 @@
+// C-ABI of libgqa_rope: argument validation, the rotary frequency schedule, and kernel dispatch.
+// Declarations and the contract of every entry point are in include/gqa_rope.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "gqa_rope.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+gqa_status fail(gqa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+gqa_status ok() {
+  g_err.clear();
+  return GQA_OK;
+}
+
+gqa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(GQA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool finite_nonneg(double x) { return std::isfinite(x) && x >= 0.0; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Frequencies of the rotated feature pairs ([Models] "Scaled RoPE", rope_inv_freq):
+// base_i = theta^(-2i/R); linear divides by factor; llama3 keeps pairs with wavelength below
+// original/high_freq_factor, divides pairs with wavelength above original/low_freq_factor by
+// factor, and between them blends the two linearly in original/wavelength.
+gqa_status check_rope(const gqa_rope_params* rp) {
+  if (!rp) return fail(GQA_E_NULL, "rope params pointer is null");
+  if (rp->rotary_dim < 0 || rp->rotary_dim % 2 || rp->rotary_dim > 2 * gqa::kMaxPairs)
+    return fail(GQA_E_SHAPE, "rotary_dim must be even and in [0, %d], got %d", 2 * gqa::kMaxPairs,
+                rp->rotary_dim);
+  if (!(std::isfinite(rp->theta) && rp->theta > 0.0))
+    return fail(GQA_E_VALUE, "rope theta must be finite and > 0, got %g", rp->theta);
+  switch (rp->kind) {
+    case GQA_ROPE_DEFAULT:
+      break;
+    case GQA_ROPE_LINEAR:
+      if (!(std::isfinite(rp->factor) && rp->factor > 0.0))
+        return fail(GQA_E_VALUE, "linear rope factor must be > 0, got %g", rp->factor);
+      break;
+    case GQA_ROPE_LLAMA3:
+      if (!(std::isfinite(rp->factor) && rp->factor > 0.0))
+        return fail(GQA_E_VALUE, "llama3 rope factor must be > 0, got %g", rp->factor);
+      if (!(rp->low_freq_factor > 0.0 && rp->high_freq_factor > rp->low_freq_factor &&
+            std::isfinite(rp->high_freq_factor)))
+        return fail(GQA_E_VALUE, "llama3 needs 0 < low_freq_factor < high_freq_factor, got %g, %g",
+                    rp->low_freq_factor, rp->high_freq_factor);
+      if (!(std::isfinite(rp->original_max_pos) && rp->original_max_pos > 0.0))
+        return fail(GQA_E_VALUE, "llama3 original_max_pos must be > 0, got %g", rp->original_max_pos);
+      break;
+    default:
+      return fail(GQA_E_UNSUPPORTED, "RoPE type %d is not implemented", rp->kind);
+  }
+  return ok();
+}
+
+void inv_freq_host(const gqa_rope_params* rp, double* out) {
+  const int R = rp->rotary_dim;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < R / 2; ++i) {
+    const double base = std::pow(rp->theta, -2.0 * i / R);
+    double f = base;
+    if (rp->kind == GQA_ROPE_LINEAR) {
+      f = base / rp->factor;
+    } else if (rp->kind == GQA_ROPE_LLAMA3) {
+      const double wavelength = two_pi / base;
+      const double old = rp->original_max_pos;
+      if (wavelength < old / rp->high_freq_factor) {
+        f = base;
+      } else if (wavelength > old / rp->low_freq_factor) {
+        f = base / rp->factor;
+      } else {
+        const double s = (old / wavelength - rp->low_freq_factor) /
+                         (rp->high_freq_factor - rp->low_freq_factor);
+        f = (1.0 - s) * base / rp->factor + s * base;
+      }
+    }
+    out[i] = f;
+  }
+}
+
+int g_policy = 0;  // 0 auto, 1 generic kernels only
+
+gqa_status check_cfg(const gqa_attn_cfg* c) {
+  if (!c) return fail(GQA_E_NULL, "cfg pointer is null");
+  if (c->dtype != GQA_F32 && c->dtype != GQA_BF16)
+    return fail(GQA_E_DTYPE, "dtype must be GQA_F32 (0) or GQA_BF16 (1), got %d", c->dtype);
+  if (c->head_dim < 8 || c->head_dim > 256 || c->head_dim % 8)
+    return fail(GQA_E_SHAPE, "head_dim must be a multiple of 8 in [8, 256], got %d", c->head_dim);
+  if (c->num_q_heads < 1 || c->num_kv_heads < 1)
+    return fail(GQA_E_SHAPE, "num_q_heads and num_kv_heads must be >= 1, got %d, %d",
+                c->num_q_heads, c->num_kv_heads);
+  if (c->num_q_heads % c->num_kv_heads)
+    return fail(GQA_E_SHAPE, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                c->num_q_heads, c->num_kv_heads);
+  if (c->num_q_heads > 65535) return fail(GQA_E_SHAPE, "num_q_heads must be <= 65535");
+  if (c->rotary_dim < 0 || c->rotary_dim % 2 || c->rotary_dim > c->head_dim)
+    return fail(GQA_E_SHAPE, "rotary_dim must be even and in [0, head_dim=%d], got %d",
+                c->head_dim, c->rotary_dim);
+  if (c->rot_style != GQA_ROT_HALF && c->rot_style != GQA_ROT_INTERLEAVED)
+    return fail(GQA_E_VALUE, "rot_style must be GQA_ROT_HALF (0) or GQA_ROT_INTERLEAVED (1), got %d",
+                c->rot_style);
+  if (c->rotary_dim > 0) {
+    if (!c->cos_table || !c->sin_table)
+      return fail(GQA_E_NULL, "cos_table/sin_table are required when rotary_dim > 0");
+    if (!aligned16(c->cos_table) || !aligned16(c->sin_table))
+      return fail(GQA_E_VALUE, "cos_table/sin_table must be 16-byte aligned");
+    if (c->table_len < 1) return fail(GQA_E_SHAPE, "table_len must be >= 1, got %d", c->table_len);
+  }
+  if (c->qk_norm != 0 && c->qk_norm != 1)
+    return fail(GQA_E_VALUE, "qk_norm must be 0 or 1, got %d", c->qk_norm);
+  if (c->qk_norm) {
+    if (!c->q_norm_w || !c->k_norm_w)
+      return fail(GQA_E_NULL, "q_norm_w and k_norm_w are required when qk_norm is set");
+    if (!aligned16(c->q_norm_w) || !aligned16(c->k_norm_w))
+      return fail(GQA_E_VALUE, "q_norm_w/k_norm_w must be 16-byte aligned");
+    if (!finite_nonneg(c->eps)) return fail(GQA_E_VALUE, "eps must be finite and >= 0, got %g", c->eps);
+  }
+  if (!finite_nonneg(c->scale)) return fail(GQA_E_VALUE, "scale must be finite and >= 0, got %g", c->scale);
+  if (!finite_nonneg(c->softcap))
+    return fail(GQA_E_VALUE, "softcap must be finite and >= 0, got %g", c->softcap);
+  return ok();
+}
+
+gqa::AttnArgs base_args(const gqa_attn_cfg* c) {
+  gqa::AttnArgs a{};
+  a.Hq = c->num_q_heads;
+  a.Hkv = c->num_kv_heads;
+  a.G = c->num_q_heads / c->num_kv_heads;
+  a.D = c->head_dim;
+  a.R = c->rotary_dim;
+  a.style = c->rot_style;
+  a.qk_norm = c->qk_norm;
+  a.eps = (float)c->eps;
+  a.qw = c->q_norm_w;
+  a.kw = c->k_norm_w;
+  a.cos_t = c->cos_table;
+  a.sin_t = c->sin_table;
+  a.table_len = c->table_len;
+  a.scale = (float)(c->scale > 0.0 ? c->scale : 1.0 / std::sqrt((double)c->head_dim));
+  a.softcap = (float)c->softcap;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_last_error(void) { return g_err.c_str(); }
+
+const char* gqa_version(void) { return "gqa_rope 0.1.0 (gfx950)"; }
+
+// Kernel policy for tests: 0 = automatic (MFMA kernels where they apply), 1 = generic kernels.
+gqa_status gqa_set_kernel_policy(int32_t policy) {
+  if (policy != 0 && policy != 1) return fail(GQA_E_VALUE, "policy must be 0 or 1, got %d", policy);
+  g_policy = policy;
+  return ok();
+}
+
+gqa_status gqa_rope_inv_freq(const gqa_rope_params* rope, double* inv_freq_out) {
+  gqa_status st = check_rope(rope);
+  if (st != GQA_OK) return st;
+  if (rope->rotary_dim > 0 && !inv_freq_out) return fail(GQA_E_NULL, "inv_freq_out is null");
+  inv_freq_host(rope, inv_freq_out);
+  return ok();
+}
+
+gqa_status gqa_rope_tables(const gqa_rope_params* rope, int32_t table_len, float* cos_out,
+                           float* sin_out, hipStream_t stream) {
+  gqa_status st = check_rope(rope);
+  if (st != GQA_OK) return st;
+  if (table_len < 1) return fail(GQA_E_SHAPE, "table_len must be >= 1, got %d", table_len);
+  if (rope->rotary_dim == 0) return ok();
+  if (!cos_out || !sin_out) return fail(GQA_E_NULL, "cos_out/sin_out are null");
+  double f[gqa::kMaxPairs];
+  inv_freq_host(rope, f);
+  return hip_status(gqa::launch_rope_tables(f, rope->rotary_dim / 2, table_len, cos_out, sin_out,
+                                            stream),
+                    "rope_tables launch");
+}
+
+gqa_status gqa_attn_prefill(const gqa_attn_cfg* cfg, const void* q, const void* k, const void* v,
+                            const int32_t* positions, int64_t pos_batch_stride,
+                            const int32_t* key_positions, int64_t kpos_batch_stride, int32_t B,
+                            int32_t L, int32_t S, int32_t n_cached, int32_t window, void* out,
+                            hipStream_t stream) {
+  gqa_status st = check_cfg(cfg);
+  if (st != GQA_OK) return st;
+  if (B < 0 || L < 0 || S < 0)
+    return fail(GQA_E_SHAPE, "B, L, S must be >= 0, got %d, %d, %d", B, L, S);
+  if (B > 65535) return fail(GQA_E_SHAPE, "B must be <= 65535, got %d", B);
+  if (n_cached < 0 || n_cached > S)
+    return fail(GQA_E_SHAPE, "n_cached must be in [0, S=%d], got %d", S, n_cached);
+  if (window < 0) return fail(GQA_E_SHAPE, "window must be >= 0, got %d", window);
+  if (pos_batch_stride < 0 || kpos_batch_stride < 0)
+    return fail(GQA_E_SHAPE, "position batch strides must be >= 0");
+  if (B == 0 || L == 0) return ok();
+  if (!q || !out || !positions) return fail(GQA_E_NULL, "q, out and positions are required");
+  if (S > 0 && (!k || !v || !key_positions))
+    return fail(GQA_E_NULL, "k, v and key_positions are required when S > 0");
+  if (!aligned16(q) || !aligned16(out) || (S > 0 && (!aligned16(k) || !aligned16(v))))
+    return fail(GQA_E_VALUE, "q, k, v and out must be 16-byte aligned");
+  if ((int64_t)L * cfg->num_q_heads > INT32_MAX)
+    return fail(GQA_E_SHAPE, "L * num_q_heads exceeds 2^31");
+  gqa::AttnArgs a = base_args(cfg);
+  const int64_t D = cfg->head_dim;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.q_h = D;
+  a.q_i = (int64_t)a.Hq * D;
+  a.q_b = (int64_t)L * a.q_i;
+  a.o_h = a.q_h;
+  a.o_i = a.q_i;
+  a.o_b = a.q_b;
+  a.k_h = D;
+  a.k_j = (int64_t)a.Hkv * D;
+  a.k_b = (int64_t)S * a.k_j;
+  a.qpos = positions;
+  a.qpos_b = pos_batch_stride;
+  a.kpos = key_positions;
+  a.kpos_b = kpos_batch_stride;
+  a.lens = nullptr;
+  a.B = B;
+  a.L = L;
+  a.S = S;
+  a.n_cached = n_cached;
+  a.window = window;
+  const bool bf16 = cfg->dtype == GQA_BF16;
+  if (bf16 && g_policy == 0 && S > 0 && gqa::prefill_mfma_supported(a))
+    return hip_status(gqa::launch_prefill_mfma(a, stream), "prefill (mfma) launch");
+  return hip_status(gqa::launch_attn_generic(a, bf16, stream), "prefill (generic) launch");
+}
+
+static bool decode_uses_mfma(const gqa_attn_cfg* cfg) {
+  gqa::AttnArgs a = base_args(cfg);
+  return cfg->dtype == GQA_BF16 && g_policy == 0 && gqa::decode_mfma_supported(a);
+}
+
+size_t gqa_decode_workspace_bytes(const gqa_attn_cfg* cfg, int32_t B, int32_t Smax) {
+  if (check_cfg(cfg) != GQA_OK) return 0;
+  if (B < 0 || Smax < 1) {
+    fail(GQA_E_SHAPE, "B must be >= 0 and Smax >= 1, got %d, %d", B, Smax);
+    return 0;
+  }
+  if (!decode_uses_mfma(cfg)) return 0;
+  return gqa::decode_mfma_workspace_bytes(B, cfg->num_kv_heads,
+                                          cfg->num_q_heads / cfg->num_kv_heads, cfg->head_dim,
+                                          Smax);
+}
+
+gqa_status gqa_attn_decode(const gqa_attn_cfg* cfg, const void* q, const void* kcache,
+                           const void* vcache, const int32_t* lens, int32_t B, int32_t Smax,
+                           int32_t window, void* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  gqa_status st = check_cfg(cfg);
+  if (st != GQA_OK) return st;
+  if (B < 0 || Smax < 1) return fail(GQA_E_SHAPE, "B must be >= 0 and Smax >= 1, got %d, %d", B, Smax);
+  if (B > 65535) return fail(GQA_E_SHAPE, "B must be <= 65535, got %d", B);
+  if (window < 0) return fail(GQA_E_SHAPE, "window must be >= 0, got %d", window);
+  if (B == 0) return ok();
+  if (!q || !kcache || !vcache || !lens || !out)
+    return fail(GQA_E_NULL, "q, kcache, vcache, lens and out are required");
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(out))
+    return fail(GQA_E_VALUE, "q, kcache, vcache and out must be 16-byte aligned");
+  gqa::AttnArgs a = base_args(cfg);
+  const int64_t D = cfg->head_dim;
+  a.q = q;
+  a.k = kcache;
+  a.v = vcache;
+  a.out = out;
+  a.q_h = D;
+  a.q_i = 0;
+  a.q_b = (int64_t)a.Hq * D;
+  a.o_h = D;
+  a.o_i = 0;
+  a.o_b = a.q_b;
+  a.k_j = D;
+  a.k_h = (int64_t)Smax * D;
+  a.k_b = (int64_t)a.Hkv * a.k_h;
+  a.qpos = nullptr;
+  a.kpos = nullptr;
+  a.lens = lens;
+  a.B = B;
+  a.L = 1;
+  a.S = Smax;
+  a.n_cached = Smax;  // every cache row is used as stored
+  a.window = window;
+  if (decode_uses_mfma(cfg)) {
+    const size_t need =
+        gqa::decode_mfma_workspace_bytes(B, a.Hkv, a.G, cfg->head_dim, Smax);
+    if (!workspace || workspace_bytes < need)
+      return fail(GQA_E_WORKSPACE, "decode needs a workspace of %zu bytes, got %zu%s", need,
+                  workspace_bytes, workspace ? "" : " (null)");
+    if (((uintptr_t)workspace & 255u) != 0)
+      return fail(GQA_E_WORKSPACE, "workspace must be 256-byte aligned");
+    gqa::DecodeArgs d;
+    d.a = a;
+    const int split = gqa::decode_split_keys();
+    d.nsplit = (Smax + split - 1) / split;
+    d.split_keys = split;
+    const int64_t items = (int64_t)B * a.Hkv * d.nsplit * a.G;
+    const size_t o_bytes = (size_t)items * D * sizeof(float);
+    d.part_o = (float*)workspace;
+    d.part_ml = (float*)((char*)workspace + ((o_bytes + 255) & ~(size_t)255));
+    return hip_status(gqa::launch_decode_mfma(d, stream), "decode (mfma) launch");
+  }
+  return hip_status(gqa::launch_attn_generic(a, cfg->dtype == GQA_BF16, stream),
+                    "decode (generic) launch");
+}
+
+}  // extern "C"

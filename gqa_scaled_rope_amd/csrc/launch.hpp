@@ -1,0 +1,31 @@
+// Host-side launchers of the HIP kernels (internal to libgqa_rope; the public ABI is gqa_rope.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace gqa {
+
+constexpr int kMaxPairs = 256;  // rotary_dim <= 512
+
+// cos/sin tables [table_len, half] from host-computed frequencies (double).
+hipError_t launch_rope_tables(const double* inv_freq, int half, int table_len, float* cos_out,
+                              float* sin_out, hipStream_t stream);
+
+// Any head_dim <= 256, any grouping, fp32 or bf16: one wave per (query row, head).
+// Serves fp32 problems and shapes the MFMA kernels do not cover.
+hipError_t launch_attn_generic(const AttnArgs& a, bool bf16, hipStream_t stream);
+
+// bf16 MFMA prefill for head_dim 128.  Returns hipErrorNotSupported when the shape is outside
+// what the kernel covers (the caller then uses the generic kernel).
+bool prefill_mfma_supported(const AttnArgs& a);
+hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);
+
+// bf16 split-KV decode for head_dim 128 (split kernel + combine kernel).
+bool decode_mfma_supported(const AttnArgs& a);
+size_t decode_mfma_workspace_bytes(int B, int Hkv, int G, int D, int Smax);
+hipError_t launch_decode_mfma(const DecodeArgs& d, hipStream_t stream);
+int decode_split_keys();
+
+}  // namespace gqa

@@ -1,0 +1,154 @@
+/*
+ * gqa_rope.h -- rotary grouped-query causal attention on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libgqa_rope.so.  Every pointer named "device" is HIP device memory that the caller
+ * allocated and owns; the library keeps no state between calls and never allocates, frees or
+ * synchronises in these calls.  Work is enqueued on the caller's stream and runs asynchronously.
+ *
+ * The operations restate three web pages (cited by title and section):
+ *   [Models] "42. More models: a registry, scaled RoPE, sliding windows and latent attention"
+ *   [Ster]   "Model resolution", section "Overview"
+ *   [Guide]  "MoE, optimisers, decoding -- every line, every shape."
+ *
+ * Errors: every call validates its host-side arguments (null pointers, shapes, dtype, rotary
+ * width parity, head grouping, rope kind, workspace size) before anything is launched and returns
+ * a gqa_status; gqa_last_error() then names the offending argument (thread-local string).  A HIP
+ * launch failure returns GQA_E_HIP with HIP's message.  Preconditions on device data are not
+ * checked (positions within the table, key positions nondecreasing, 1 <= lens <= Smax): device
+ * indices are clamped into their buffers so a violation yields wrong numbers, never an
+ * out-of-bounds access.
+ */
+#ifndef GQA_ROPE_H
+#define GQA_ROPE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_E_NULL = 1,        /* a required pointer is null */
+  GQA_E_SHAPE = 2,       /* a size is out of range or sizes disagree */
+  GQA_E_DTYPE = 3,       /* unknown dtype */
+  GQA_E_UNSUPPORTED = 4, /* valid request this build does not implement (e.g. head_dim > 256) */
+  GQA_E_WORKSPACE = 5,   /* workspace missing or smaller than gqa_decode_workspace_bytes() */
+  GQA_E_HIP = 6,         /* a HIP call failed; message from hipGetErrorString */
+  GQA_E_VALUE = 7        /* a scalar parameter is out of range (theta, factor, eps, ...) */
+} gqa_status;
+
+typedef enum gqa_dtype { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
+
+/* [Models] "Scaled RoPE": the three frequency schedules of rope_scaling. */
+typedef enum gqa_rope_kind { GQA_ROPE_DEFAULT = 0, GQA_ROPE_LINEAR = 1, GQA_ROPE_LLAMA3 = 2 } gqa_rope_kind;
+
+/* Pairing of rotated features: half-split pairs (i, i + R/2) ([Guide] section 4 "Rotary");
+ * interleaved pairs (2i, 2i + 1) ([Models] "Serving it: absorbing the up-projections"). */
+typedef enum gqa_rot_style { GQA_ROT_HALF = 0, GQA_ROT_INTERLEAVED = 1 } gqa_rot_style;
+
+/* Rotary frequency schedule ([Models] "Scaled RoPE", rope_inv_freq).
+ * rotary_dim R: number of rotated features, even, 0 <= R <= 512; R = head_dim *
+ * partial_rotary_factor ([Ster] "Overview": only that share of each head rotates, and the
+ * frequencies run over that share).  theta > 0.  factor > 0 (linear, llama3).  llama3 also needs
+ * 0 < low_freq_factor < high_freq_factor and original_max_pos > 0. */
+typedef struct gqa_rope_params {
+  int32_t rotary_dim;
+  int32_t kind;               /* gqa_rope_kind */
+  double theta;
+  double factor;
+  double low_freq_factor;
+  double high_freq_factor;
+  double original_max_pos;    /* original_max_position_embeddings */
+} gqa_rope_params;
+
+/* Attention configuration shared by prefill and decode. */
+typedef struct gqa_attn_cfg {
+  int32_t dtype;              /* gqa_dtype of q, k, v, out and the norm gains */
+  int32_t head_dim;           /* D: 1..256, multiple of 8 */
+  int32_t num_q_heads;        /* Hq */
+  int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0.  Query head h reads KV head h / (Hq/Hkv) */
+  int32_t rotary_dim;         /* R, must equal the R the tables were built with; 0 = no rotation */
+  int32_t rot_style;          /* gqa_rot_style */
+  const float* cos_table;     /* device [table_len, R/2] fp32 from gqa_rope_tables (may be null if R == 0) */
+  const float* sin_table;     /* device [table_len, R/2] */
+  int32_t table_len;          /* rows of the tables: valid positions are 0 .. table_len-1 */
+  int32_t qk_norm;            /* 1: per-head RMSNorm of q and new k before rotation ([Models] "What differs") */
+  double eps;                 /* RMSNorm epsilon ([Guide] section 3.2), >= 0 */
+  const void* q_norm_w;       /* device [D] gain in dtype (required when qk_norm) */
+  const void* k_norm_w;       /* device [D] gain in dtype (required when qk_norm) */
+  double scale;               /* score scale; 0 selects 1/sqrt(head_dim) ([Guide] section 3.4) */
+  double softcap;             /* > 0: scores become softcap * tanh(score / softcap); 0: off */
+} gqa_attn_cfg;
+
+/* Build cos/sin tables for positions 0 .. table_len-1 ([Models] "Scaled RoPE", rope_tables):
+ * cos_out[p*(R/2) + i] = cos(p * inv_freq[i]), sin_out likewise, attention factor 1.  inv_freq is
+ * computed on the host in double precision and the angles and their sine/cosine on the device in
+ * double precision, then stored as fp32.  cos_out, sin_out: device, table_len * R/2 floats each,
+ * caller-owned.  table_len >= 1.  R == 0 is a valid no-op. */
+gqa_status gqa_rope_tables(const gqa_rope_params* rope, int32_t table_len, float* cos_out,
+                           float* sin_out, hipStream_t stream);
+
+/* Host-side copy of the frequencies the tables use (R/2 doubles into inv_freq_out, host memory).
+ * Lets a caller inspect the schedule without a GPU. */
+gqa_status gqa_rope_inv_freq(const gqa_rope_params* rope, double* inv_freq_out);
+
+/* Causal prefill ([Models] "What differs between model families", DecoderAttention.forward;
+ * [Guide] section 3.4 "Attention").
+ *   q   device [B, L, Hq, D]  new queries (contiguous)
+ *   k,v device [B, S, Hkv, D] keys/values; rows j < n_cached are cache rows used as stored
+ *       (already normed and rotated); rows j >= n_cached are new and get the k-norm and the
+ *       rotation at key_positions[j]; values are never rotated
+ *   positions      device int32 [B, L] (pos_batch_stride = L) or [L] shared (stride 0)
+ *   key_positions  device int32 [B, S] or [S] shared; must be nondecreasing in j
+ *   window         0 = full causal; w > 0: a query at position p sees keys at positions
+ *                  p-w+1 .. p ([Models] "Sliding windows": keys more than w-1 back are masked)
+ *   out  device [B, L, Hq, D] (contiguous, caller-owned), never aliasing the inputs.
+ * Result per (b, i, h): softmax over allowed keys of scale*<q', k'> (soft-capped if set), times
+ * v; a row with no allowed key is 0.  B, L, S >= 0 (an empty problem is a no-op); n_cached in
+ * [0, S]. */
+gqa_status gqa_attn_prefill(const gqa_attn_cfg* cfg, const void* q, const void* k, const void* v,
+                            const int32_t* positions, int64_t pos_batch_stride,
+                            const int32_t* key_positions, int64_t kpos_batch_stride, int32_t B,
+                            int32_t L, int32_t S, int32_t n_cached, int32_t window, void* out,
+                            hipStream_t stream);
+
+/* Bytes of device workspace gqa_attn_decode needs for B sequences of capacity Smax (0 if the
+ * chosen kernel needs none).  Returns 0 and sets the error on invalid arguments. */
+size_t gqa_decode_workspace_bytes(const gqa_attn_cfg* cfg, int32_t B, int32_t Smax);
+
+/* Single-token decode against a KV cache ([Guide] section 3.3 "KVCache", section 3.7).
+ *   q          device [B, Hq, D], the new token's query (normed and rotated here, at lens[b]-1)
+ *   kcache     device [B, Hkv, Smax, D]: slot j of sequence b holds the key at position j,
+ *              already normed and rotated; slot lens[b]-1 holds the new token's key
+ *   vcache     device [B, Hkv, Smax, D]
+ *   lens       device int32 [B], 1 <= lens[b] <= Smax
+ *   window     0 = every cached key; w > 0: only the last w keys
+ *   out        device [B, Hq, D]
+ *   workspace  device, >= gqa_decode_workspace_bytes(cfg, B, Smax) bytes (split partials),
+ *              caller-owned; contents on entry are ignored.
+ * Two calls that share a workspace must be ordered on one stream. */
+gqa_status gqa_attn_decode(const gqa_attn_cfg* cfg, const void* q, const void* kcache,
+                           const void* vcache, const int32_t* lens, int32_t B, int32_t Smax,
+                           int32_t window, void* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Kernel selection, for tests and comparisons: 0 (default) = bf16 problems run on the MFMA
+ * kernels wherever their shape is covered; 1 = every problem runs on the generic kernel (one
+ * wavefront per query row and head, fp32 arithmetic).  Process-wide; not thread-safe. */
+gqa_status gqa_set_kernel_policy(int32_t policy);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* gqa_last_error(void);
+
+/* Library version string. */
+const char* gqa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ROPE_H */

@@ -169,3 +169,40 @@ def rope_params(wl: Workload):
     return dict(rotary_dim=wl.rotary_dim, theta=wl.theta, kind=wl.rope_kind, factor=wl.factor,
                 low_freq_factor=wl.low_freq_factor, high_freq_factor=wl.high_freq_factor,
                 original_max_position_embeddings=wl.original_max_pos)
+
+
+# ---------------------------------------------------------------------------------------------
+# Device-side draws (large workloads): torch's seeded generator on the GPU.  Tests and the bench
+# read back the sampled slices they hand to the oracle.
+# ---------------------------------------------------------------------------------------------
+def device_normal(shape, seed, dtype, device="cuda"):
+    """N(0, 1) draw of `shape` on the device from torch's generator seeded with `seed`, rounded to
+    the run dtype ("bf16" or "f32")."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    return x.to(torch.bfloat16) if dtype == "bf16" else x
+
+
+def decode_device_inputs(wl: Workload, seed=None, device="cuda"):
+    """Decode workload on the device: lens (numpy stream of `seed`), q and the full caches
+    [B, Hkv, Smax, D] drawn sequence by sequence from one seeded device generator."""
+    import torch
+    seed = wl.seed if seed is None else seed
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(wl.lens_lo, wl.lens_hi + 1, size=wl.B).astype(np.int32)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) * 7919 + 17)
+    q = torch.randn((wl.B, wl.Hq, wl.D), generator=gen, device=device).to(dt)
+    k = torch.empty((wl.B, wl.Hkv, wl.S, wl.D), dtype=dt, device=device)
+    v = torch.empty_like(k)
+    for b in range(wl.B):
+        k[b] = torch.randn((wl.Hkv, wl.S, wl.D), generator=gen, device=device).to(dt)
+        v[b] = torch.randn((wl.Hkv, wl.S, wl.D), generator=gen, device=device).to(dt)
+    out = dict(lens=torch.from_numpy(lens).to(device), q=q, k=k, v=v)
+    if wl.qk_norm:
+        out["qw"] = (1.0 + 0.02 * torch.randn((wl.D,), generator=gen, device=device)).to(dt)
+        out["kw"] = (1.0 + 0.02 * torch.randn((wl.D,), generator=gen, device=device)).to(dt)
+    return out

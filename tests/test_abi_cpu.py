@@ -1,0 +1,176 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, validates host-side
+arguments before launching anything, and computes the rotary frequency schedule on the host
+exactly as the oracle does.  No call here reaches a kernel launch."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+g = pytest.importorskip("gqa_scaled_rope_amd")
+
+if not os.path.exists(g.LIB_PATH):
+    pytest.skip("libgqa_rope.so not built", allow_module_level=True)
+
+lib = g.library()
+
+
+def test_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "gqa_rope.h")).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(gqa_[a-z_0-9]+)\s*\(", header,
+                              re.M))
+    assert declared, "no declarations parsed"
+    assert declared == set(g.EXPORTS), (declared ^ set(g.EXPORTS))
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_version():
+    assert b"gfx950" in lib.gqa_version()
+
+
+def _cfg(**kw):
+    base = dict(dtype=1, head_dim=128, num_q_heads=32, num_kv_heads=8, rotary_dim=0, rot_style=0,
+                cos_table=None, sin_table=None, table_len=0, qk_norm=0, eps=1e-6, q_norm_w=None,
+                k_norm_w=None, scale=0.0, softcap=0.0)
+    base.update(kw)
+    c = g._AttnCfg()
+    for k, v in base.items():
+        setattr(c, k, v)
+    return c
+
+
+FAKE = 1 << 20  # aligned non-null host-side stand-in; validation fails before any use
+
+
+def _prefill(c, B=1, L=4, S=4, n_cached=0, window=0, q=FAKE, k=FAKE, v=FAKE, pos=FAKE, kpos=FAKE,
+             out=FAKE):
+    return lib.gqa_attn_prefill(ctypes.byref(c) if c is not None else None, q, k, v, pos, 0, kpos,
+                                0, B, L, S, n_cached, window, out, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dtype=5), 3, "dtype"),
+    (dict(head_dim=100), 2, "head_dim"),
+    (dict(head_dim=512), 2, "head_dim"),
+    (dict(num_kv_heads=7), 2, "multiple of num_kv_heads"),
+    (dict(num_q_heads=0), 2, "num_q_heads"),
+    (dict(rotary_dim=63), 2, "rotary_dim"),
+    (dict(rotary_dim=256), 2, "rotary_dim"),
+    (dict(rotary_dim=64), 1, "cos_table"),
+    (dict(rotary_dim=64, cos_table=FAKE, sin_table=FAKE, table_len=0), 2, "table_len"),
+    (dict(rotary_dim=64, cos_table=FAKE + 4, sin_table=FAKE, table_len=8), 7, "aligned"),
+    (dict(rot_style=3), 7, "rot_style"),
+    (dict(qk_norm=1), 1, "q_norm_w"),
+    (dict(qk_norm=1, q_norm_w=FAKE, k_norm_w=FAKE, eps=-1.0), 7, "eps"),
+    (dict(scale=-1.0), 7, "scale"),
+    (dict(softcap=float("nan")), 7, "softcap"),
+])
+def test_prefill_rejects_bad_cfg(kw, status, msg):
+    st = _prefill(_cfg(**kw))
+    assert st == status
+    assert msg in g.last_error()
+
+
+def test_prefill_rejects_bad_sizes_and_pointers():
+    c = _cfg()
+    assert _prefill(None) == 1
+    assert _prefill(c, B=-1) == 2
+    assert _prefill(c, n_cached=5, S=4) == 2 and "n_cached" in g.last_error()
+    assert _prefill(c, window=-3) == 2
+    assert _prefill(c, q=None) == 1
+    assert _prefill(c, k=None) == 1
+    assert _prefill(c, q=FAKE + 2) == 7
+    # an empty problem is a no-op: returns OK without touching any pointer
+    assert _prefill(c, B=0, q=None, k=None, v=None, pos=None, kpos=None, out=None) == 0
+    assert _prefill(c, L=0, q=None, k=None, v=None, pos=None, kpos=None, out=None) == 0
+    assert g.last_error() == ""
+
+
+def test_decode_validation_and_workspace():
+    c = _cfg()
+    need = lib.gqa_decode_workspace_bytes(ctypes.byref(c), 64, 32768)
+    # split partials: B * Hkv * ceil(Smax/1024) * G * (D + 2) floats (+ alignment)
+    assert need >= 64 * 8 * 32 * 4 * 130 * 4
+    assert need < 64 * 8 * 32 * 4 * 130 * 4 + 4096
+    st = lib.gqa_attn_decode(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 64, 32768, 0, FAKE, None,
+                             0, None)
+    assert st == 5 and "workspace" in g.last_error()
+    st = lib.gqa_attn_decode(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 64, 32768, 0, FAKE, FAKE,
+                             need - 1, None)
+    assert st == 5
+    st = lib.gqa_attn_decode(ctypes.byref(c), FAKE, FAKE, FAKE, None, 2, 16, 0, FAKE, FAKE,
+                             need, None)
+    assert st == 1 and "lens" in g.last_error()
+    assert lib.gqa_attn_decode(ctypes.byref(c), None, None, None, None, 0, 16, 0, None, None, 0,
+                               None) == 0
+    assert lib.gqa_attn_decode(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 1, 0, 0, FAKE, FAKE, need,
+                               None) == 2
+    # fp32 runs on the generic kernel, which needs no workspace
+    c32 = _cfg(dtype=0)
+    assert lib.gqa_decode_workspace_bytes(ctypes.byref(c32), 64, 32768) == 0
+
+
+def test_rope_param_validation():
+    def st(**kw):
+        p = g.RopeSpec(**{**dict(rotary_dim=64), **kw}).c_struct()
+        return lib.gqa_rope_tables(ctypes.byref(p), 16, FAKE, FAKE, None)
+    assert st(rotary_dim=63) == 2
+    assert st(theta=0.0) == 7
+    assert st(kind="linear", factor=0.0) == 7
+    assert st(kind="llama3", factor=8.0, low_freq_factor=4.0, high_freq_factor=1.0) == 7
+    p = g._RopeParams(64, 9, 1e4, 1.0, 1.0, 4.0, 8192.0)
+    assert lib.gqa_rope_tables(ctypes.byref(p), 16, FAKE, FAKE, None) == 4
+    assert "not implemented" in g.last_error()
+    p = g.RopeSpec(64).c_struct()
+    assert lib.gqa_rope_tables(ctypes.byref(p), 0, FAKE, FAKE, None) == 2
+    with pytest.raises(g.GQAError):
+        g.RopeSpec(64, kind="yarn").c_struct()
+
+
+@pytest.mark.parametrize("R,kind,theta,factor", [
+    (128, "default", 1e6, 1.0), (64, "default", 1e4, 1.0), (32, "linear", 1e4, 4.0),
+    (128, "llama3", 5e5, 8.0), (64, "llama3", 5e5, 8.0), (2, "default", 1e4, 1.0),
+])
+def test_host_inv_freq_matches_oracle(R, kind, theta, factor):
+    got = np.array(g.rope_inv_freq(g.RopeSpec(R, kind, theta, factor, 1.0, 4.0, 8192.0)))
+    ref = oracle.rope_inv_freq(R, theta, kind, factor, 1.0, 4.0, 8192.0)
+    np.testing.assert_allclose(got, ref, rtol=1e-15, atol=0)
+
+
+def test_policy_switch_validates():
+    with pytest.raises(g.GQAError):
+        g.set_kernel_policy(7)
+    g.set_kernel_policy(0)
+
+
+def test_decode_byte_model_matches_page(golden):
+    # the decode traffic model used by the bench: 2 (K, V) * Hkv * D * bytes per cached token
+    # per layer; the page prints the per-token KV size of whole models
+    import bench
+    for row in golden("kv_bytes_per_token.json")["rows"]:
+        per_layer = bench.kv_bytes_per_token_per_layer(row["kv_heads"], row["head_dim"],
+                                                       row["bytes_per_elem"])
+        kib = row["layers"] * per_layer / 1024
+        assert kib == row["kv_KiB_per_token"]
+        assert row["layers"] * per_layer * 32768 / 2 ** 30 == pytest.approx(row["GiB_for_32k_tokens"])
+
+
+def test_prefill_flop_model():
+    # allowed (query, key) pairs per (b, h) for the workloads, counted by brute force over
+    # positions at a reduced size and by the closed form used in the bench
+    import bench
+    for L, S, w, nc in ((64, 64, 0, 0), (64, 64, 16, 0), (16, 64, 0, 48), (16, 64, 32, 48)):
+        qp = np.arange(S - L, S) if nc else np.arange(L)
+        brute = int(oracle.allowed_mask(qp, np.arange(S), w).sum())
+        assert bench.allowed_pairs(L, S, w, nc) == brute
+    assert bench.allowed_pairs(2048, 2048, 0, 0) == 2098176
+    assert bench.allowed_pairs(8192, 8192, 4096, 0) == 25167872
+    assert bench.allowed_pairs(512, 4096, 4096, 3584) == 1966336
+    assert bench.allowed_pairs(512, 4096, 0, 3584) == 1966336
+    assert math.isclose(4 * 4 * 32 * 128 * 2098176, 1.3751e11, rel_tol=1e-4)

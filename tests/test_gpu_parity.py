@@ -1,0 +1,332 @@
+"""GPU parity of the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances (from the arithmetic): fp32 |err| <= 1e-4; bf16 |err| <= 2e-2 + 2e-2 |ref| elementwise
+and, tighter, ||err|| / ||ref|| <= 1e-2 per (sequence, head); masks and positions bit-exact
+(probe: with q = 0 every allowed key gets weight 1/n and every masked key exactly 0, so one-hot
+values reveal the allowed set exactly).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from synth import (WORKLOADS, decode_cache_seq, decode_device_inputs, decode_lens_q,
+                   prefill_inputs)
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+g = pytest.importorskip("gqa_scaled_rope_amd")
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev(a, dt=torch.bfloat16):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt)
+
+
+def tdt(wl):
+    return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+
+def inv_freq(wl):
+    return oracle.rope_inv_freq(wl.rotary_dim, wl.theta, wl.rope_kind, wl.factor,
+                                wl.low_freq_factor, wl.high_freq_factor, wl.original_max_pos)
+
+
+def spec(wl):
+    return g.RopeSpec(wl.rotary_dim, wl.rope_kind, wl.theta, wl.factor, wl.low_freq_factor,
+                      wl.high_freq_factor, wl.original_max_pos)
+
+
+@pytest.fixture(params=[0, 1], ids=["mfma", "generic"])
+def policy(request):
+    g.set_kernel_policy(request.param)
+    yield request.param
+    g.set_kernel_policy(0)
+
+
+def gpu_prefill(wl, x, table_len=None, shared_pos=False):
+    dt = tdt(wl)
+    tl = table_len or int(max(x["positions"].max(), x["key_positions"].max())) + 1
+    cos, sin = g.rope_tables(spec(wl), tl) if wl.rotary_dim else (None, None)
+    cfg = g.AttnConfig(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
+                       wl.qk_norm, wl.eps,
+                       dev(x["q_norm_w"], dt) if wl.qk_norm else None,
+                       dev(x["k_norm_w"], dt) if wl.qk_norm else None, 0.0, wl.softcap)
+    pos = x["positions"][0] if shared_pos else x["positions"]
+    kpos = x["key_positions"][0] if shared_pos else x["key_positions"]
+    out = g.attn_prefill(cfg, dev(x["q"], dt), dev(x["k"], dt), dev(x["v"], dt),
+                         dev(pos, torch.int32), dev(kpos, torch.int32), wl.n_cached, wl.window)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def ref_prefill(wl, x, **kw):
+    return oracle.attn_prefill(x["q"], x["k"], x["v"], x["positions"], x["key_positions"],
+                               inv_freq=inv_freq(wl), style=wl.style, n_cached=wl.n_cached,
+                               window=wl.window, q_norm_w=x.get("q_norm_w"),
+                               k_norm_w=x.get("k_norm_w"), eps=wl.eps, softcap=wl.softcap, **kw)
+
+
+def check(got, ref, dtype="bf16", head_axis=2):
+    err = np.abs(got - ref)
+    if dtype == "f32":
+        assert err.max() <= 1e-4, f"fp32 max err {err.max()}"
+        return
+    bad = err > 2e-2 + 2e-2 * np.abs(ref)
+    assert not bad.any(), f"{bad.sum()} elements out of tolerance, max err {err.max()} at {np.argwhere(bad)[:3]}"
+    # relative norm per (sequence, head): all axes but batch and head reduced
+    axes = tuple(i for i in range(ref.ndim) if i not in (0, head_axis))
+    num = np.sqrt((err ** 2).sum(axis=axes))
+    den = np.sqrt((ref ** 2).sum(axis=axes)) + 1e-30
+    rel = num / den
+    assert rel.max() <= 1e-2, f"relative norm error {rel.max()}"
+
+
+# ----------------------------------------------------------------------------------------------
+def test_rope_tables_match_oracle():
+    for wl in (WORKLOADS["qwen3_prefill_bf16"], WORKLOADS["llama31_decode_bf16"],
+               WORKLOADS["chunked_prefill_bf16_full"],
+               WORKLOADS["tiny_causal_f32"].with_(rope_kind="linear", factor=4.0)):
+        say("tables", wl.name)
+        n = wl.S
+        cos, sin = g.rope_tables(spec(wl), n)
+        torch.cuda.synchronize()
+        ang = oracle.rope_angles(np.arange(n), inv_freq(wl))
+        np.testing.assert_allclose(cos.cpu().numpy(), np.cos(ang), rtol=0, atol=2e-7)
+        np.testing.assert_allclose(sin.cpu().numpy(), np.sin(ang), rtol=0, atol=2e-7)
+
+
+def test_tiny_causal_f32():
+    wl = WORKLOADS["tiny_causal_f32"]
+    x = prefill_inputs(wl)
+    check(gpu_prefill(wl, x), ref_prefill(wl, x), "f32")
+
+
+BASE = WORKLOADS["qwen3_prefill_bf16"].with_(B=2, L=300, S=300, Hq=8, Hkv=2)
+VARIANTS = {
+    "qknorm_half128": BASE,
+    "window77": BASE.with_(qk_norm=False, window=77),
+    "window1": BASE.with_(qk_norm=False, window=1),
+    "interleaved64_cap_chunk": BASE.with_(Hq=6, Hkv=2, rotary_dim=64, style="interleaved",
+                                         softcap=50.0, qk_norm=False, n_cached=180, theta=1e4),
+    "interleaved64_window_chunk": BASE.with_(Hq=6, Hkv=2, rotary_dim=64, style="interleaved",
+                                            softcap=50.0, qk_norm=False, n_cached=180,
+                                            window=100, theta=1e4),
+    "half64_partial": BASE.with_(rotary_dim=64),
+    "half32_partial": BASE.with_(rotary_dim=32, qk_norm=False),
+    "half16_partial": BASE.with_(rotary_dim=16, qk_norm=False),
+    "norope": BASE.with_(rotary_dim=0),
+    "mha_G1": BASE.with_(Hq=4, Hkv=4),
+    "G8": BASE.with_(Hq=16, Hkv=2, L=100, S=100),
+    "llama3_long_positions": BASE.with_(rope_kind="llama3", theta=5e5, factor=8.0, qk_norm=False),
+    "ragged_L257": BASE.with_(L=257, S=257),
+    "single_token": BASE.with_(L=1, S=1),
+    "chunk_L1": BASE.with_(L=1, S=300, n_cached=299, qk_norm=False),
+}
+
+
+@pytest.mark.parametrize("name", list(VARIANTS))
+def test_prefill_variants(name, policy):
+    wl = VARIANTS[name]
+    say("prefill variant", name, "policy", policy)
+    x = prefill_inputs(wl, seed=hash(name) % 1000)
+    check(gpu_prefill(wl, x), ref_prefill(wl, x))
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("peaky_q4_offset_norm", dict(q_scale=4.0, offset=0.3)),
+    ("peaky_k4", dict(k_scale=4.0)),
+])
+def test_prefill_stress_norm(name, kw, policy):
+    # non-unit RMS inputs: skipping the norm would fail; peaky logits
+    wl = BASE
+    say("stress", name, "policy", policy)
+    x = prefill_inputs(wl, seed=7, **kw)
+    check(gpu_prefill(wl, x), ref_prefill(wl, x))
+
+
+@pytest.mark.parametrize("cap", [1.0, 5.0])
+def test_prefill_stress_softcap(cap, policy):
+    # with q x 8 the cap changes the logits by O(1): a missing or misplaced cap fails
+    wl = BASE.with_(qk_norm=False, softcap=cap, rotary_dim=64, style="interleaved")
+    x = prefill_inputs(wl, seed=8, q_scale=8.0)
+    got, ref = gpu_prefill(wl, x), ref_prefill(wl, x)
+    check(got, ref)
+    ref_nocap = ref_prefill(wl.with_(softcap=0.0), x)
+    assert np.abs(ref_nocap - ref).max() > 0.1  # the stress input really exercises the cap
+
+
+def test_prefill_per_sequence_positions(policy):
+    # each sequence has its own position offsets (batch stride L / S), chunked queries
+    wl = BASE.with_(qk_norm=False, window=50, n_cached=200, L=100, S=300)
+    x = prefill_inputs(wl, seed=9)
+    for b in range(wl.B):
+        x["key_positions"][b] += 37 * b
+        x["positions"][b] += 37 * b
+    check(gpu_prefill(wl, x), ref_prefill(wl, x))
+
+
+def test_prefill_shared_positions_stride0():
+    wl = BASE.with_(qk_norm=False, window=64)
+    x = prefill_inputs(wl, seed=10)
+    check(gpu_prefill(wl, x, shared_pos=True), ref_prefill(wl, x))
+
+
+def test_prefill_no_keys_rows_are_zero():
+    # queries whose positions precede every key position see nothing -> exact zeros
+    wl = BASE.with_(qk_norm=False, L=64, S=64)
+    x = prefill_inputs(wl, seed=11)
+    x["key_positions"] += 1000
+    got = gpu_prefill(wl, x, table_len=2000)
+    ref = ref_prefill(wl, x)
+    assert np.all(ref == 0) and np.all(got == 0)
+
+
+@pytest.mark.parametrize("window,n_cached,shift", [(0, 0, 0), (1, 0, 0), (5, 0, 0), (64, 0, 3),
+                                                   (100, 120, 0), (0, 200, 5), (129, 0, 0)])
+def test_mask_probe_bitexact(window, n_cached, shift, policy):
+    wl = BASE.with_(qk_norm=False, rotary_dim=0, window=window, n_cached=n_cached, L=300 - n_cached,
+                    S=300)
+    say("mask probe", window, n_cached, shift, "policy", policy)
+    x = prefill_inputs(wl, seed=12)
+    x["q"][:] = 0.0
+    for b in range(wl.B):
+        x["key_positions"][b] += shift * b
+        x["positions"][b] += shift * b
+    allowed = [oracle.allowed_mask(x["positions"][b], x["key_positions"][b], window)
+               for b in range(wl.B)]
+    for blk in range(0, wl.S, wl.D):
+        v = np.zeros_like(x["v"])
+        n = min(wl.D, wl.S - blk)
+        for d in range(n):
+            v[:, blk + d, :, d] = 1.0
+        xx = dict(x, v=v)
+        got = gpu_prefill(wl, xx)                          # [B, L, Hq, D]
+        for b in range(wl.B):
+            nz = got[b] != 0                               # [L, Hq, D]
+            want = allowed[b][:, blk:blk + n]              # [L, n]
+            for h in range(wl.Hq):
+                np.testing.assert_array_equal(nz[:, h, :n], want)
+            assert not nz[:, :, n:].any()
+
+
+# ----------------------------------------------------------------------------------------------
+def gpu_decode(wl, q, kc, vc, lens, qw=None):
+    dt = tdt(wl)
+    cos, sin = g.rope_tables(spec(wl), kc.shape[2]) if wl.rotary_dim else (None, None)
+    cfg = g.AttnConfig(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
+                       wl.qk_norm, wl.eps, dev(qw, dt) if wl.qk_norm else None,
+                       dev(qw, dt) if wl.qk_norm else None, 0.0, wl.softcap)
+    out = g.attn_decode(cfg, dev(q, dt), dev(kc, dt), dev(vc, dt), dev(lens, torch.int32),
+                        wl.window)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+DEC = WORKLOADS["llama31_decode_bf16"].with_(B=5, S=2600, lens_lo=1, lens_hi=2600)
+DEC_VARIANTS = {
+    "llama3": DEC,
+    "window100": DEC.with_(window=100),
+    "window_big": DEC.with_(window=1500),
+    "qknorm_interleaved64_cap": DEC.with_(qk_norm=True, rotary_dim=64, style="interleaved",
+                                          softcap=5.0, rope_kind="default", theta=1e4),
+    "G3": DEC.with_(Hq=24, Hkv=8),
+    "G16": DEC.with_(Hq=32, Hkv=2),
+    "half32": DEC.with_(rotary_dim=32),
+}
+
+
+@pytest.mark.parametrize("name", list(DEC_VARIANTS))
+def test_decode_variants(name, policy):
+    wl = DEC_VARIANTS[name]
+    say("decode variant", name, "policy", policy)
+    lens, q, qw = decode_lens_q(wl, seed=21)
+    lens[0], lens[1] = 1, wl.S                # edge lengths: one key, full capacity
+    kc = np.full((wl.B, wl.Hkv, wl.S, wl.D), np.nan, np.float32)  # unread slots are NaN
+    vc = np.full_like(kc, np.nan)
+    for b in range(wl.B):
+        kk, vv = decode_cache_seq(wl, b, int(lens[b]), seed=21)
+        kc[b, :, :lens[b]] = kk
+        vc[b, :, :lens[b]] = vv
+    got = gpu_decode(wl, q, kc, vc, lens, qw)
+    ref = oracle.attn_decode(q, np.nan_to_num(kc), np.nan_to_num(vc), lens, inv_freq=inv_freq(wl),
+                             style=wl.style, window=wl.window, q_norm_w=qw, eps=wl.eps,
+                             softcap=wl.softcap)
+    check(got, ref, head_axis=1)
+
+
+def test_decode_equals_last_prefill_row():
+    # decode against a cache filled with normed, rotated keys == last row of prefill
+    wl = BASE.with_(B=2, L=333, S=333, window=0)
+    x = prefill_inputs(wl, seed=31)
+    full = gpu_prefill(wl, x)[:, -1]                                   # [B, Hq, D]
+    inv = inv_freq(wl)
+    kc = oracle.rotate(oracle.rms_norm(x["k"], x["k_norm_w"], wl.eps),
+                       x["key_positions"][:, :, None], inv, wl.style)
+    kc = kc.transpose(0, 2, 1, 3).astype(np.float32)
+    vc = x["v"].transpose(0, 2, 1, 3)
+    lens = np.full(wl.B, wl.S, np.int32)
+    dwl = wl.with_(qk_norm=True)
+    dt = torch.bfloat16
+    cos, sin = g.rope_tables(spec(wl), wl.S)
+    cfg = g.AttnConfig("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin, True,
+                       wl.eps, dev(x["q_norm_w"]), dev(x["k_norm_w"]))
+    dec = g.attn_decode(cfg, dev(x["q"][:, -1]), dev(kc), dev(vc), dev(lens, torch.int32), 0)
+    torch.cuda.synchronize()
+    del dwl
+    ref = ref_prefill(wl, x, query_rows=[wl.L - 1])[:, 0]
+    check(dec.float().cpu().numpy(), ref, head_axis=1)
+    check(full, ref, head_axis=1)
+
+
+# ----------------------------------------------------------------------------------------------
+# Full-size workloads, sampled outputs, in the launch configuration the bench times
+# ----------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name,batches,rows", [
+    ("qwen3_prefill_bf16", [0, 3], [0, 1, 63, 64, 65, 1000, 2046, 2047]),
+    ("mistral_swa_prefill_bf16", [1], [0, 4094, 4095, 4096, 4097, 6000, 8191]),
+    ("chunked_prefill_bf16_w4096", [0, 7], [0, 1, 255, 256, 511]),
+    ("chunked_prefill_bf16_full", [5], [0, 300, 511]),
+])
+def test_full_size_prefill_sampled(name, batches, rows):
+    wl = WORKLOADS[name]
+    say("full size", name)
+    x = prefill_inputs(wl)
+    got = gpu_prefill(wl, x, shared_pos=True)
+    ref = ref_prefill(wl, x, query_rows=rows, batches=batches)
+    check(got[batches][:, rows], ref)
+    assert np.isfinite(got).all()
+
+
+def test_chunked_window4096_equals_full_bitwise():
+    # max distance in the chunk is 4095 = w - 1, so the two layer kinds see the same keys
+    a = WORKLOADS["chunked_prefill_bf16_w4096"]
+    b = WORKLOADS["chunked_prefill_bf16_full"]
+    x = prefill_inputs(a)
+    np.testing.assert_array_equal(gpu_prefill(a, x, shared_pos=True),
+                                  gpu_prefill(b, x, shared_pos=True))
+
+
+def test_full_size_decode_sampled():
+    wl = WORKLOADS["llama31_decode_bf16"]
+    say("full size decode", wl.name)
+    x = decode_device_inputs(wl)
+    cos, sin = g.rope_tables(spec(wl), wl.S)
+    cfg = g.AttnConfig("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin)
+    out = g.attn_decode(cfg, x["q"], x["k"], x["v"], x["lens"], 0)
+    torch.cuda.synchronize()
+    lens = x["lens"].cpu().numpy()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    inv = inv_freq(wl)
+    for b in sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 17, 63}):
+        n = int(lens[b])
+        ref = oracle.attn_decode_one(x["q"][b].float().cpu().numpy(),
+                                     x["k"][b, :, :n].float().cpu().numpy(),
+                                     x["v"][b, :, :n].float().cpu().numpy(), n, inv_freq=inv)
+        check(got[b][None], ref[None], head_axis=1)
