@@ -2,9 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-One step = one pass of the whole hot path over one batch of synthetic input: the rotary tables
-(gqa_rope_tables) followed by the prefill attention call (gqa_attn_prefill), inputs resident in
-HBM.  The default workload is the Qwen3-style prefill (B=4, L=S=2048, Hq=32, Hkv=8, D=128,
+One step = one pass of the whole hot path over one batch of synthetic input, inputs resident in
+HBM: the rotary tables (gqa_rope_tables), the key preparation that norms and rotates the new keys
+into the K cache (gqa_prep_keys), and the attention over the cache (gqa_attn_prefill with every
+key used as stored), three launches timed separately with HIP events.  The default workload is the Qwen3-style prefill (B=4, L=S=2048, Hq=32, Hkv=8, D=128,
 per-head q/k RMSNorm, full causal).  The split-KV decode workload (64 sequences, cache lengths
 U[1024, 32768], llama3 rope) is timed in the same run and reported under "decode".
 
@@ -89,42 +90,46 @@ def _prefill_setup(wl, torch, g):
     cfg = g.AttnConfig(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
                        wl.qk_norm, wl.eps, qw, kw, 0.0, wl.softcap)
     out = torch.empty_like(q)
+    kcache = k.clone()   # rows < n_cached: the cache as stored; the rest is rewritten each step
     return dict(q=q, k=k, v=v, qw=qw, kw=kw, pos=pos, kpos=kpos, cos=cos, sin=sin, cfg=cfg,
-                out=out, table_len=table_len)
+                out=out, table_len=table_len, kcache=kcache)
 
 
 def run_prefill(wl, steps, warmup, torch, g):
     x = _prefill_setup(wl, torch, g)
     spec = _rope_spec(g, wl)
     stream = torch.cuda.current_stream()
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    def step():
+    def launches(ev=None):
+        if ev:
+            ev[0].record(stream)
         g.rope_tables(spec, x["table_len"], x["cos"], x["sin"])
-        g.attn_prefill(x["cfg"], x["q"], x["k"], x["v"], x["pos"], x["kpos"], wl.n_cached,
-                       wl.window, x["out"])
+        if ev:
+            ev[1].record(stream)
+        g.prep_keys(x["cfg"], x["k"], x["kpos"], wl.n_cached, k_out=x["kcache"])
+        if ev:
+            ev[2].record(stream)
+        g.attn_prefill(x["cfg"], x["q"], x["kcache"], x["v"], x["pos"], x["kpos"], wl.S,
+                       wl.window, x["out"], workspace=None)
+        if ev:
+            ev[3].record(stream)
 
     for _ in range(warmup):
-        step()
+        launches()
     torch.cuda.synchronize()
-    # whole-step timing
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    # per-launch timing of the attention kernel alone
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    torch.cuda.synchronize()
+    t0, t1 = E(), E()
+    evs = [[E() for _ in range(4)] for _ in range(steps)]
     t0.record(stream)
     for i in range(steps):
-        g.rope_tables(spec, x["table_len"], x["cos"], x["sin"])
-        evs[i][0].record(stream)
-        g.attn_prefill(x["cfg"], x["q"], x["k"], x["v"], x["pos"], x["kpos"], wl.n_cached,
-                       wl.window, x["out"])
-        evs[i][1].record(stream)
+        launches(evs[i])
     t1.record(stream)
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    kern_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    return x, total_ms / steps, sum(kern_ms) / len(kern_ms), kern_ms[len(kern_ms) // 2]
+    step_ms = t0.elapsed_time(t1) / steps
+    parts = {name: sorted(e[k].elapsed_time(e[k + 1]) for e in evs)
+             for k, name in enumerate(("rope_tables", "prep_keys", "attention"))}
+    stats = {name: (sum(v) / len(v), v[len(v) // 2]) for name, v in parts.items()}
+    return x, step_ms, stats
 
 
 def run_decode(wl, steps, warmup, torch, g):
@@ -152,50 +157,51 @@ def run_decode(wl, steps, warmup, torch, g):
     return x, sum(ms) / len(ms), ms[len(ms) // 2]
 
 
-def cpu_baseline_prefill(wl, x, torch, rows=256, max_s=30.0):
-    """Time the oracle on a bounded sample (sequence 0, the last `rows` query rows, all heads),
-    check the GPU output on the same sample, and scale the rate to TFLOP/s."""
+def cpu_baseline_prefill(wl, x, torch, budget_s=15.0):
+    """Time the oracle on a bounded sample -- whole sequences, in order, until about budget_s of
+    CPU time -- check the GPU output on the same sample, and report the rate in TFLOP/s."""
     import numpy as np
     import oracle
-    b = 0
-    q = x["q"][b:b + 1].float().cpu().numpy()
-    k = x["k"][b:b + 1].float().cpu().numpy()
-    v = x["v"][b:b + 1].float().cpu().numpy()
+    inv = oracle.rope_inv_freq(wl.rotary_dim, wl.theta, wl.rope_kind, wl.factor,
+                               wl.low_freq_factor, wl.high_freq_factor, wl.original_max_pos)
     qw = x["qw"].float().cpu().numpy() if x["qw"] is not None else None
     kw = x["kw"].float().cpu().numpy() if x["kw"] is not None else None
     pos = x["pos"].cpu().numpy()[None]
     kpos = x["kpos"].cpu().numpy()[None]
-    sel = np.arange(wl.L - rows, wl.L)
-    inv = oracle.rope_inv_freq(wl.rotary_dim, wl.theta, wl.rope_kind, wl.factor,
-                               wl.low_freq_factor, wl.high_freq_factor, wl.original_max_pos)
-    t = time.perf_counter()
-    ref = oracle.attn_prefill(q, k, v, pos, kpos, inv_freq=inv, style=wl.style,
-                              n_cached=wl.n_cached, window=wl.window, q_norm_w=qw, k_norm_w=kw,
-                              eps=wl.eps, softcap=wl.softcap, query_rows=sel)
-    dt = time.perf_counter() - t
-    got = x["out"][b, sel].float().cpu().numpy()
-    err = np.abs(got[None] - ref)
-    ok = bool(np.all(err <= 2e-2 + 2e-2 * np.abs(ref)))
-    start = wl.S - wl.L if wl.n_cached else 0
-    qp = start + sel
-    pairs = sum(min(int(p) + 1, wl.window) if wl.window else int(p) + 1 for p in qp)
-    flops = 4 * wl.Hq * wl.D * pairs
-    threads = _blas_threads()
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
-                sample=f"sequence 0, last {rows} query rows x {wl.Hq} heads of {wl.name} "
-                       f"({flops / 1e9:.2f} GFLOP, {dt:.1f} s)",
-                parity_ok=ok, max_abs_err=float(err.max()))
+    t_total, nseq, ok, maxerr = 0.0, 0, True, 0.0
+    for b in range(wl.B):
+        q = x["q"][b:b + 1].float().cpu().numpy()
+        k = x["k"][b:b + 1].float().cpu().numpy()
+        v = x["v"][b:b + 1].float().cpu().numpy()
+        t = time.perf_counter()
+        ref = oracle.attn_prefill(q, k, v, pos, kpos, inv_freq=inv, style=wl.style,
+                                  n_cached=wl.n_cached, window=wl.window, q_norm_w=qw,
+                                  k_norm_w=kw, eps=wl.eps, softcap=wl.softcap)
+        t_total += time.perf_counter() - t
+        got = x["out"][b:b + 1].float().cpu().numpy()
+        err = np.abs(got - ref)
+        maxerr = max(maxerr, float(err.max()))
+        ok &= bool(np.all(err <= 2e-2 + 2e-2 * np.abs(ref)))
+        nseq += 1
+        if t_total >= budget_s:
+            break
+    flops = 4 * nseq * wl.Hq * wl.D * allowed_pairs(wl.L, wl.S, wl.window, wl.n_cached)
+    return dict(value=flops / t_total / 1e12, unit="TFLOP/s", cores=_blas_threads(),
+                kind="oracle",
+                sample=f"{nseq} of {wl.B} sequences of {wl.name}, all rows and heads "
+                       f"({flops / 1e9:.1f} GFLOP in {t_total:.1f} s)",
+                parity_ok=ok, max_abs_err=maxerr)
 
 
-def cpu_baseline_decode(wl, x, torch, nseq=2):
+def cpu_baseline_decode(wl, x, torch, budget_s=15.0):
     import numpy as np
     import oracle
     lens = x["lens"].cpu().numpy()
     inv = oracle.rope_inv_freq(wl.rotary_dim, wl.theta, wl.rope_kind, wl.factor,
                                wl.low_freq_factor, wl.high_freq_factor, wl.original_max_pos)
     eb = 2
-    t_total, nbytes, ok, maxerr = 0.0, 0, True, 0.0
-    for b in range(nseq):
+    t_total, nbytes, ok, maxerr, nseq = 0.0, 0, True, 0.0, 0
+    for b in range(wl.B):
         n = int(lens[b])
         kk = x["k"][b, :, :n].float().cpu().numpy()
         vv = x["v"][b, :, :n].float().cpu().numpy()
@@ -210,9 +216,12 @@ def cpu_baseline_decode(wl, x, torch, nseq=2):
         ok &= bool(np.all(err <= 2e-2 + 2e-2 * np.abs(ref)))
         keys = min(n, wl.window) if wl.window else n
         nbytes += keys * kv_bytes_per_token_per_layer(wl.Hkv, wl.D, eb)
+        nseq += 1
+        if t_total >= budget_s:
+            break
     return dict(value=nbytes / t_total / 1e9, unit="GB/s", cores=_blas_threads(), kind="oracle",
-                sample=f"sequences 0..{nseq - 1} of {wl.name} ({nbytes / 1e6:.0f} MB of K/V, "
-                       f"{t_total:.1f} s)", parity_ok=ok, max_abs_err=maxerr)
+                sample=f"{nseq} of {wl.B} sequences of {wl.name} ({nbytes / 1e6:.0f} MB of K/V "
+                       f"in {t_total:.1f} s)", parity_ok=ok, max_abs_err=maxerr)
 
 
 def _blas_threads():
@@ -248,12 +257,13 @@ def main(argv=None):
     g.library()
     wl = WORKLOADS[args.workload]
     log(f"[bench] prefill workload {wl.name}: warmup {args.warmup}, steps {args.steps}")
-    x, step_ms, kern_ms, kern_med = run_prefill(wl, args.steps, args.warmup, torch, g)
+    x, step_ms, stats = run_prefill(wl, args.steps, args.warmup, torch, g)
+    kern_ms, kern_med = stats["attention"]
     flops = prefill_flops(wl)
     value = flops / (step_ms * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
-    log(f"[bench] step {step_ms:.3f} ms, attention kernel {kern_ms:.3f} ms "
-        f"-> {achieved:.1f} TFLOP/s")
+    log(f"[bench] step {step_ms:.3f} ms (tables {stats['rope_tables'][0]:.4f}, prep_keys "
+        f"{stats['prep_keys'][0]:.4f}, attention {kern_ms:.4f}) -> attention {achieved:.1f} TFLOP/s")
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
@@ -264,11 +274,12 @@ def main(argv=None):
                    "rope": wl.rope_kind, "theta": wl.theta, "qk_norm": wl.qk_norm,
                    "window": wl.window, "softcap": wl.softcap, "n_cached": wl.n_cached,
                    "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel",
+        "roofline": {"bound": "mfma", "kernel": "prefill_stream_kernel",
                      "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "kernel_ms_mean": round(kern_ms, 4),
                      "kernel_ms_median": round(kern_med, 4), "algorithmic_flop": flops},
+        "step_parts_ms": {k: round(v[0], 4) for k, v in stats.items()},
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) on a bounded sample ...")

@@ -17,7 +17,7 @@ from typing import Optional
 
 __all__ = [
     "GQAError", "RopeSpec", "AttnConfig", "library", "rope_inv_freq", "rope_tables",
-    "attn_prefill", "attn_decode", "decode_workspace_bytes", "last_error", "set_kernel_policy",
+    "attn_prefill", "attn_decode", "decode_workspace_bytes", "prefill_workspace_bytes", "prep_keys", "last_error", "set_kernel_policy",
     "LIB_PATH", "EXPORTS",
 ]
 
@@ -61,8 +61,10 @@ _I32, _I64, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 EXPORTS = {
     "gqa_rope_tables": (_I32, [ctypes.POINTER(_RopeParams), _I32, _P, _P, _P]),
     "gqa_rope_inv_freq": (_I32, [ctypes.POINTER(_RopeParams), ctypes.POINTER(ctypes.c_double)]),
+    "gqa_prep_keys": (_I32, [ctypes.POINTER(_AttnCfg), _P, _P, _I64, _I32, _I32, _I32, _P, _P]),
+    "gqa_prefill_workspace_bytes": (_SZ, [ctypes.POINTER(_AttnCfg), _I32, _I32, _I32]),
     "gqa_attn_prefill": (_I32, [ctypes.POINTER(_AttnCfg), _P, _P, _P, _P, _I64, _P, _I64, _I32,
-                                _I32, _I32, _I32, _I32, _P, _P]),
+                                _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "gqa_decode_workspace_bytes": (_SZ, [ctypes.POINTER(_AttnCfg), _I32, _I32]),
     "gqa_attn_decode": (_I32, [ctypes.POINTER(_AttnCfg), _P, _P, _P, _P, _I32, _I32, _I32, _P, _P,
                                _SZ, _P]),
@@ -225,10 +227,42 @@ class AttnConfig:
                         qw, kw, self.scale, self.softcap)
 
 
+def prep_keys(cfg: AttnConfig, k, key_positions, n_cached=0, k_out=None, stream=None):
+    """Norm and rotate key rows [n_cached, S) of k [B, S, Hkv, D] into k_out (same layout; may be
+    k itself).  Returns k_out."""
+    torch = _torch()
+    B, S = k.shape[0], k.shape[1]
+    dt = cfg.torch_dtype
+    pk = _need(k, "k", (B, S, cfg.num_kv_heads, cfg.head_dim), dt)
+    if key_positions.dim() == 1:
+        pkp, kstride = _need(key_positions, "key_positions", (S,), torch.int32), 0
+    else:
+        pkp, kstride = _need(key_positions, "key_positions", (B, S), torch.int32), S
+    if k_out is None:
+        k_out = k.clone()
+    po = _need(k_out, "k_out", tuple(k.shape), dt)
+    c = cfg.c_struct()
+    _check(library().gqa_prep_keys(ctypes.byref(c), pk, pkp, kstride, B, S, int(n_cached), po,
+                                   _stream(stream)))
+    return k_out
+
+
+def prefill_workspace_bytes(cfg: AttnConfig, B: int, S: int, n_cached: int = 0) -> int:
+    c = cfg.c_struct()
+    n = library().gqa_prefill_workspace_bytes(ctypes.byref(c), int(B), int(S), int(n_cached))
+    err = last_error()
+    if n == 0 and err:
+        raise GQAError(2, err)
+    return int(n)
+
+
 def attn_prefill(cfg: AttnConfig, q, k, v, positions, key_positions, n_cached=0, window=0,
-                 out=None, stream=None):
+                 out=None, workspace="auto", stream=None):
     """q [B, L, Hq, D], k/v [B, S, Hkv, D], positions [B, L] or [L], key_positions [B, S] or [S]
-    (int32, nondecreasing).  Returns out [B, L, Hq, D]."""
+    (int32, nondecreasing).  Returns out [B, L, Hq, D].
+
+    workspace: "auto" allocates the key-preparation workspace when the streaming kernel can use
+    it; None selects the fused kernel (no workspace); or a uint8 device tensor."""
     torch = _torch()
     B, L, Hq, D = q.shape
     S = k.shape[1]
@@ -247,9 +281,17 @@ def attn_prefill(cfg: AttnConfig, q, k, v, positions, key_positions, n_cached=0,
     if out is None:
         out = torch.empty_like(q)
     po = _need(out, "out", tuple(q.shape), dt)
+    if isinstance(workspace, str):
+        need = prefill_workspace_bytes(cfg, B, S, n_cached)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    pw, nbytes = ctypes.c_void_p(None), 0
+    if workspace is not None:
+        pw = _need(workspace, "workspace", (workspace.numel(),), torch.uint8)
+        nbytes = workspace.numel()
     c = cfg.c_struct()
     _check(library().gqa_attn_prefill(ctypes.byref(c), pq, pk, pv, pp, pstride, pkp, kstride, B, L,
-                                      S, int(n_cached), int(window), po, _stream(stream)))
+                                      S, int(n_cached), int(window), po, pw, nbytes,
+                                      _stream(stream)))
     return out
 
 

@@ -1,4 +1,6 @@
-// bf16 MFMA prefill of rotary grouped-query causal attention, head_dim 128, for gfx950.
+// bf16 MFMA prefill of rotary grouped-query causal attention, head_dim 128, for gfx950 -- fused
+// variant, used when the caller gives no workspace: new keys are normed and rotated in registers
+// each time their tile is staged.
 //
 // What it computes is [Models] "What differs between model families" (DecoderAttention.forward:
 // q/k norm, rotation, window mask, causal attention) with [Guide] section 3.4's softmax; how:

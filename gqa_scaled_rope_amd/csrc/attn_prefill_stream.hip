@@ -1,0 +1,536 @@
+// bf16 MFMA prefill, head_dim 128, gfx950 -- streaming variant used when the caller provides a
+// workspace for the prepared keys.
+//
+// Two launches:
+//  1. k_prep_kernel: every NEW key row (index >= n_cached) is RMS-normed and rotated once
+//     ([Models] "What differs": q/k norm then rotation; [Guide] section 3.2 and section 4) and
+//     written, rounded to bf16, to the workspace [B, S - n_cached, Hkv, D].  Cached rows are used
+//     as stored and are not copied.  This is the cache-append step of the page's flow (rotate,
+//     then cache.update) and costs one read and one write of the new keys, instead of redoing the
+//     norm and rotation each time a key tile is revisited by another query block.
+//  2. prefill_stream_kernel: the attention proper.  Same tiling and math as the fused kernel
+//     (8 wavefronts x 32 query rows of one KV head, S^T = K Q^T and O^T = V^T P^T on
+//     v_mfma_f32_32x32x16_bf16, online softmax in log2 units with lazy rescaling), but K and V
+//     tiles travel from HBM straight into LDS with buffer_load ... lds: no VGPR staging, no LDS
+//     store instructions, 32-bit offsets from a buffer descriptor, and the descriptor's range check
+//     returns zeros past the last key, which handles the ragged tail.  Each wave instruction fills
+//     1 KB of LDS in lane order; choosing the source chunk per lane produces the XOR-swizzled
+//     layout the MFMA operand reads want.
+#include "launch.hpp"
+
+namespace gqa {
+namespace {
+
+constexpr int HD = 128;
+constexpr int NW = 8;
+constexpr int NT = NW * 64;
+constexpr int ROWS = NW * 32;
+constexpr int BN = 64;
+constexpr int TILE_ELEMS = BN * HD;
+constexpr float kRescaleThreshold = 8.0f;
+constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit dwords, range checked
+
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& w) { return __builtin_bit_cast(bf16x8, w); }
+
+__device__ __forceinline__ void unpack8(const u32x4& w, float* x) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = bf16lo(w[e]);
+    x[2 * e + 1] = bf16hi(w[e]);
+  }
+}
+__device__ __forceinline__ u32x4 pack8(const float* x) {
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+  return w;
+}
+
+__device__ __forceinline__ int lower_bound_pos(const int32_t* kp, int n, int64_t x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if ((int64_t)kp[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// Rotate 8 consecutive features starting at 8*c, given the partner chunk y (half-split) or in
+// place (interleaved).  Feature pairs: half-split (d, d + R/2); interleaved (2i, 2i + 1).
+template <int ROT>
+__device__ __forceinline__ void rotate_chunk(float* x, const float* y, int c, int R,
+                                             const float* cr, const float* sr) {
+  const int d0 = 8 * c;
+  if (d0 >= R) return;
+  if (ROT == 1) {
+    const int half = R >> 1;
+    const bool first = d0 < half;
+    const int p0 = first ? d0 : d0 - half;
+    const f32x4 c0 = *(const f32x4*)(cr + p0), c1 = *(const f32x4*)(cr + p0 + 4);
+    const f32x4 s0 = *(const f32x4*)(sr + p0), s1 = *(const f32x4*)(sr + p0 + 4);
+    const float cs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+    const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      x[e] = first ? (x[e] * cs[e] - y[e] * sn[e]) : (y[e] * sn[e] + x[e] * cs[e]);
+  } else if (ROT == 2) {
+    const int p0 = d0 >> 1;
+    const f32x4 cs = *(const f32x4*)(cr + p0);
+    const f32x4 sn = *(const f32x4*)(sr + p0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = x[2 * e], b = x[2 * e + 1];
+      x[2 * e] = a * cs[e] - b * sn[e];
+      x[2 * e + 1] = a * sn[e] + b * cs[e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 1. key preparation: 16 lanes per key row (8 features each), 16 rows per 256-thread block
+// ---------------------------------------------------------------------------------------------
+// Output row (b, j, g) lands at kout + b*ob + (j - jofs)*oj + g*D: the compact workspace
+// [B, S - n_cached, Hkv, D] (jofs = n_cached) or a full [B, S, Hkv, D] buffer such as a KV cache
+// (jofs = 0), which may be k itself (each row is read completely before it is written).
+struct PrepOut {
+  uint16_t* p;
+  int64_t ob, oj;
+  int32_t jofs;
+};
+
+template <int ROT, bool NORM>
+__global__ __launch_bounds__(256) void k_prep_kernel(AttnArgs a, PrepOut po, int64_t nrows) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int c = threadIdx.x & 15;
+  const int64_t nnew = a.S - a.n_cached;
+  const bool valid = row < nrows;
+  // row enumerates (b, jn, g) in the workspace layout [B, S - n_cached, Hkv, D]
+  const int64_t r = valid ? row : 0;
+  const int g = (int)(r % a.Hkv);
+  const int64_t bj = r / a.Hkv;
+  const int64_t jn = bj % nnew;
+  const int b = (int)(bj / nnew);
+  const int64_t j = a.n_cached + jn;
+  const uint16_t* src = (const uint16_t*)a.k + (int64_t)b * a.k_b + j * a.k_j + (int64_t)g * a.k_h;
+  float x[8];
+  unpack8(ld16(src + 8 * c), x);
+  if (NORM) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    ss += __shfl_xor(ss, 4, 64);
+    ss += __shfl_xor(ss, 8, 64);
+    const float rs = rsqrtf(ss * (1.0f / HD) + a.eps);
+    float w[8];
+    unpack8(ld16((const uint16_t*)a.kw + 8 * c), w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= rs * w[e];
+  }
+  if (ROT != 0) {
+    const int32_t kp = a.kpos[(int64_t)b * a.kpos_b + j];
+    const int64_t tp = min<int64_t>(max<int64_t>(kp, 0), a.table_len - 1);
+    const int halfp = a.R >> 1;
+    const float* cr = a.cos_t + tp * halfp;
+    const float* sr = a.sin_t + tp * halfp;
+    if (ROT == 1) {
+      float y[8];
+      const int P = a.R >> 4;  // partner distance in chunks: 1, 2, 4 or 8
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = __shfl_xor(x[e], P, 64);
+      rotate_chunk<1>(x, y, c, a.R, cr, sr);
+    } else {
+      rotate_chunk<2>(x, x, c, a.R, cr, sr);
+    }
+  }
+  if (valid) {
+    uint16_t* dst = po.p + (int64_t)b * po.ob + (j - po.jofs) * po.oj + (int64_t)g * HD;
+    *(u32x4*)(dst + 8 * c) = pack8(x);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 2. attention over prepared keys
+// ---------------------------------------------------------------------------------------------
+struct Smem {
+  uint16_t k[2][TILE_ELEMS];
+  uint16_t v[2][TILE_ELEMS];
+  int32_t kpos[2][BN];
+};
+
+struct StreamArgs {
+  AttnArgs a;
+  const uint16_t* kprep;   // [B, S - n_cached, Hkv, D] prepared new keys (null if none)
+};
+
+template <int ROT, bool NORM, bool CAP>
+__global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, int nqb) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  const AttnArgs& a = sa.a;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int ql = lane & 31, hg = lane >> 5;
+  const int qb = nqb - 1 - (int)blockIdx.x;  // heaviest (latest) query blocks first
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int G = a.G;
+  const int64_t nrows = (int64_t)a.L * G;
+  const int64_t f0 = (int64_t)qb * ROWS;
+
+  // ---- this lane's query row (flattened position-major (position, head) index) ----
+  const int64_t f = f0 + w * 32 + ql;
+  const bool qvalid = f < nrows;
+  const int qi = qvalid ? (int)(f / G) : 0;
+  const int qh = g * G + (qvalid ? (int)(f % G) : 0);
+  const int32_t* qpos_b = a.qpos + (int64_t)b * a.qpos_b;
+  const int64_t qp = qvalid ? (int64_t)qpos_b[qi] : 0;
+
+  // ---- query prep: norm, rotate, scale into log2 units, keep chunks 2s + hg as bf16 ----
+  const float qscale = a.scale * kLog2e;
+  bf16x8 qop[8];
+  {
+    const uint16_t* qr = (const uint16_t*)a.q + (int64_t)b * a.q_b + (int64_t)qi * a.q_i +
+                         (int64_t)qh * a.q_h;
+    float rs = 1.f;
+    if (NORM) {
+      float ss = 0.f;
+      if (qvalid) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          float x[8];
+          unpack8(ld16(qr + 8 * c), x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+        }
+      }
+      rs = rsqrtf(ss * (1.0f / HD) + a.eps);
+    }
+    const uint16_t* qw = (const uint16_t*)a.qw;
+    const int64_t tp = ROT ? min<int64_t>(max<int64_t>(qp, 0), a.table_len - 1) : 0;
+    const int halfp = a.R >> 1;
+    const float* cr = ROT ? a.cos_t + tp * halfp : nullptr;
+    const float* sr = ROT ? a.sin_t + tp * halfp : nullptr;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int c = 2 * s + hg;
+      float x[8];
+      if (qvalid) {
+        unpack8(ld16(qr + 8 * c), x);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      }
+      if (NORM) {
+        float wv[8];
+        unpack8(ld16(qw + 8 * c), wv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= rs * wv[e];
+      }
+      if (ROT == 1 && qvalid && 8 * c < a.R) {
+        const int pc = c ^ (a.R >> 4);
+        float y[8];
+        unpack8(ld16(qr + 8 * pc), y);
+        if (NORM) {
+          float wv[8];
+          unpack8(ld16(qw + 8 * pc), wv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] *= rs * wv[e];
+        }
+        rotate_chunk<1>(x, y, c, a.R, cr, sr);
+      } else if (ROT == 2 && qvalid) {
+        rotate_chunk<2>(x, x, c, a.R, cr, sr);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= qscale;
+      qop[s] = as_bf16x8(pack8(x));
+    }
+  }
+
+  // ---- key band of the workgroup's query positions ----
+  int64_t qmin, qmax;
+  {
+    const int i_lo = (int)(f0 / G);
+    const int i_hi = (int)min<int64_t>((f0 + ROWS - 1) / G, (int64_t)a.L - 1);
+    int64_t mn = INT64_MAX, mx = INT64_MIN;
+    for (int i = i_lo + lane; i <= i_hi; i += 64) {
+      const int64_t p = qpos_b[i];
+      mn = min(mn, p);
+      mx = max(mx, p);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      mn = min(mn, (int64_t)__shfl_xor(mn, off, 64));
+      mx = max(mx, (int64_t)__shfl_xor(mx, off, 64));
+    }
+    qmin = mn;
+    qmax = mx;
+  }
+  const int32_t* kpos_b = a.kpos + (int64_t)b * a.kpos_b;
+  const int j_hi = lower_bound_pos(kpos_b, a.S, qmax + 1);
+  const int j_lo = a.window > 0 ? min(lower_bound_pos(kpos_b, a.S, qmin - a.window + 1), j_hi) : 0;
+  const int n_tiles = (j_hi - j_lo + BN - 1) / BN;
+
+  // ---- buffer descriptors of this (b, g): cached keys, prepared keys, values ----
+  const int row_bytes = (int)(a.k_j * 2);  // bytes between consecutive keys of one head
+  const int64_t kv_base = (int64_t)b * a.k_b + (int64_t)g * a.k_h;
+  // keys below nc come from k as stored; keys at or above nc from the prepared workspace (when
+  // there is none, nothing needs preparing and every key comes from k)
+  const int nc = sa.kprep ? a.n_cached : a.S;
+  const int nnew = a.S - nc;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint16_t*)a.k + kv_base), (short)0,
+      nc > 0 ? (nc - 1) * row_bytes + HD * 2 : 0, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(sa.kprep ? sa.kprep + (int64_t)b * nnew * a.k_j + (int64_t)g * a.k_h : nullptr),
+      (short)0, (sa.kprep && nnew > 0) ? (nnew - 1) * row_bytes + HD * 2 : 0, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint16_t*)a.v + kv_base), (short)0, (a.S - 1) * row_bytes + HD * 2, kBufFlags);
+
+  // Tile loader: wave w, round i fills LDS rows 4*(w + 8i) .. +3 (1 KB); lane -> row 4(w+8i) +
+  // lane/16, LDS chunk lane%16, which holds source chunk (lane%16) ^ (row & 15).
+  auto issue_tile = [&](int jt, int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 4 * (w + 8 * i) + (lane >> 4);
+      const int j = jt + r;
+      const int csrc = (lane & 15) ^ (r & 15);
+      lds_void* kdst = (lds_void*)(&sm.k[buf][4 * (w + 8 * i) * HD]);
+      lds_void* vdst = (lds_void*)(&sm.v[buf][4 * (w + 8 * i) * HD]);
+      const int vo = j * row_bytes + csrc * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vdst, 16, j < a.S ? vo : 0x7fffffff, 0, 0, 0);
+      if (j < nc) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, vo, 0, 0, 0);
+      } else {
+        const int wo = (j - nc) * row_bytes + csrc * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, kdst, 16, j < a.S ? wo : 0x7fffffff, 0, 0, 0);
+      }
+    }
+    if (tid < BN) {
+      const int j = jt + tid;
+      sm.kpos[buf][tid] = j < j_hi ? kpos_b[j] : 0x7fffffff;
+    }
+  };
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float m = kNegBig, lsum = 0.f;
+  const float cap2 = a.softcap * kLog2e;
+  const float inv_cap2 = CAP ? 1.0f / cap2 : 0.f;
+
+  // per-lane LDS read offsets (elements): K rows kb*32 + ql, chunk 2s + hg
+  const int gi = lane >> 4, s16 = lane & 15;
+  const int hgv = gi >> 1;
+
+  if (n_tiles > 0) {
+    issue_tile(j_lo, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    const int jt = j_lo + t * BN;
+    if (t + 1 < n_tiles) issue_tile(jt + BN, buf ^ 1);
+
+    const int32_t kfirst = sm.kpos[buf][0];
+    const int32_t klast = sm.kpos[buf][BN - 1];
+    const bool full = (jt + BN <= j_hi) && ((int64_t)klast <= qmin) &&
+                      (a.window == 0 || qmax - (int64_t)kfirst <= a.window - 1);
+    const uint16_t* ks = sm.k[buf];
+    const uint16_t* vs = sm.v[buf];
+
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+      const int krow = kb * 32 + ql;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int off = krow * HD + (((2 * s + hg) ^ (krow & 15)) << 3);
+        const bf16x8 ka = as_bf16x8(*(const u32x4*)(ks + off));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[s], sacc, 0, 0, 0);
+      }
+      if (CAP) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = sacc[r] * inv_cap2;
+          const float e = fast_exp2(-2.0f * kLog2e * fabsf(x));
+          sacc[r] = copysignf(cap2 * (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e), x);
+        }
+      }
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = kb * 32 + 8 * (r >> 2) + 4 * hg + (r & 3);
+          const int64_t kp = sm.kpos[buf][kk];
+          const bool ok = qvalid && kp <= qp && (a.window == 0 || qp - kp <= a.window - 1);
+          if (!ok) sacc[r] = -INFINITY;
+        }
+      }
+      float mt = sacc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
+      mt = fmaxf(mt, swap_halves(mt));
+      if (__ballot(mt > m + kRescaleThreshold) != 0) {
+        const float m_new = fmaxf(m, mt);
+        const float alpha = fast_exp2(m - m_new);
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m = m_new;
+      }
+      bf16x8 pb[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(sacc[8 * u + e] - m);
+          lsum += p[e];
+        }
+        pb[u] = as_bf16x8(pack8(p));
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int row1 = kb * 32 + 16 * u + 4 * hgv + (s16 >> 2);
+        const int row2 = row1 + 8;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int col = db * 32 + 16 * (gi & 1) + 4 * (s16 & 3);
+          const int off1 = row1 * HD + (((col >> 3) ^ (row1 & 15)) << 3) + (col & 7);
+          const int off2 = row2 * HD + (((col >> 3) ^ (row2 & 15)) << 3) + (col & 7);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vs + off1));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vs + off2));
+          const i16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pb[u],
+                                                          o[db], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  const float ltot = lsum + swap_halves(lsum);
+  const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+  if (qvalid) {
+    uint16_t* orow = (uint16_t*)a.out + (int64_t)b * a.o_b + (int64_t)qi * a.o_i +
+                     (int64_t)qh * a.o_h;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d = db * 32 + 8 * rq + 4 * hg;
+        u32x2 w2;
+        w2[0] = pack_bf16x2(o[db][4 * rq + 0] * inv, o[db][4 * rq + 1] * inv);
+        w2[1] = pack_bf16x2(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
+        *(u32x2*)(orow + d) = w2;
+      }
+  }
+}
+
+template <int ROT, bool NORM, bool CAP>
+hipError_t launch_attn(const StreamArgs& sa, hipStream_t stream) {
+  const AttnArgs& a = sa.a;
+  const int64_t nrows = (int64_t)a.L * a.G;
+  const int nqb = (int)((nrows + ROWS - 1) / ROWS);
+  hipLaunchKernelGGL((prefill_stream_kernel<ROT, NORM, CAP>), dim3(nqb, a.Hkv, a.B), dim3(NT), 0,
+                     stream, sa, nqb);
+  return hipGetLastError();
+}
+template <int ROT, bool NORM>
+hipError_t launch_attn_cap(const StreamArgs& sa, hipStream_t s) {
+  return sa.a.softcap > 0.f ? launch_attn<ROT, NORM, true>(sa, s) : launch_attn<ROT, NORM, false>(sa, s);
+}
+template <int ROT>
+hipError_t launch_attn_norm(const StreamArgs& sa, hipStream_t s) {
+  return sa.a.qk_norm ? launch_attn_cap<ROT, true>(sa, s) : launch_attn_cap<ROT, false>(sa, s);
+}
+
+template <int ROT, bool NORM>
+hipError_t launch_prep(const AttnArgs& a, const PrepOut& po, hipStream_t stream) {
+  const int64_t nrows = (int64_t)a.B * (a.S - a.n_cached) * a.Hkv;
+  if (nrows == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_prep_kernel<ROT, NORM>), dim3((unsigned)((nrows + 15) / 16)), dim3(256),
+                     0, stream, a, po, nrows);
+  return hipGetLastError();
+}
+
+hipError_t dispatch_prep(const AttnArgs& a, const PrepOut& po, hipStream_t stream) {
+  const int rot = a.R == 0 ? 0 : (a.style == 0 ? 1 : 2);
+  switch (rot * 2 + (a.qk_norm ? 1 : 0)) {
+    case 0: return hipSuccess;  // nothing to prepare
+    case 1: return launch_prep<0, true>(a, po, stream);
+    case 2: return launch_prep<1, false>(a, po, stream);
+    case 3: return launch_prep<1, true>(a, po, stream);
+    case 4: return launch_prep<2, false>(a, po, stream);
+    default: return launch_prep<2, true>(a, po, stream);
+  }
+}
+
+}  // namespace
+
+bool prep_keys_supported(const AttnArgs& a) {
+  if (a.D != HD) return false;
+  if (a.R == 0 || a.style == 1) return a.R % 8 == 0;
+  const int P = a.R / 16;
+  return a.R % 16 == 0 && (P == 1 || P == 2 || P == 4 || P == 8);
+}
+
+hipError_t launch_prep_keys(const AttnArgs& a, void* k_out, hipStream_t stream) {
+  PrepOut po;
+  po.p = (uint16_t*)k_out;
+  po.oj = a.k_j;
+  po.ob = a.k_b;
+  po.jofs = 0;
+  return dispatch_prep(a, po, stream);
+}
+
+bool prefill_needs_kprep(const AttnArgs& a) { return (a.qk_norm || a.R > 0) && a.n_cached < a.S; }
+
+size_t prefill_stream_workspace_bytes(const AttnArgs& a) {
+  if (!prefill_needs_kprep(a)) return 0;
+  return (size_t)a.B * (a.S - a.n_cached) * a.Hkv * HD * sizeof(uint16_t);
+}
+
+bool prefill_stream_supported(const AttnArgs& a) {
+  // 32-bit buffer offsets: every key row of one sequence must be addressable
+  return prefill_mfma_supported(a) && ((int64_t)a.S + BN) * a.k_j * 2 < (int64_t)INT32_MAX;
+}
+
+hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t stream) {
+  if (a.B == 0 || a.L == 0) return hipSuccess;
+  const int rot = a.R == 0 ? 0 : (a.style == 0 ? 1 : 2);
+  StreamArgs sa;
+  sa.a = a;
+  sa.kprep = nullptr;
+  if (prefill_needs_kprep(a)) {
+    PrepOut po;
+    po.p = (uint16_t*)workspace;
+    po.oj = a.k_j;
+    po.ob = (int64_t)(a.S - a.n_cached) * a.k_j;
+    po.jofs = a.n_cached;
+    hipError_t e = dispatch_prep(a, po, stream);
+    if (e != hipSuccess) return e;
+    sa.kprep = po.p;
+  }
+  switch (rot) {
+    case 0: return launch_attn_norm<0>(sa, stream);
+    case 1: return launch_attn_norm<1>(sa, stream);
+    default: return launch_attn_norm<2>(sa, stream);
+  }
+}
+
+}  // namespace gqa

@@ -194,11 +194,55 @@ gqa_status gqa_rope_tables(const gqa_rope_params* rope, int32_t table_len, float
                     "rope_tables launch");
 }
 
+static gqa::AttnArgs prefill_args(const gqa_attn_cfg* cfg, int32_t B, int32_t L, int32_t S,
+                                  int32_t n_cached) {
+  gqa::AttnArgs a = base_args(cfg);
+  const int64_t D = cfg->head_dim;
+  a.q_h = D;
+  a.q_i = (int64_t)a.Hq * D;
+  a.q_b = (int64_t)L * a.q_i;
+  a.o_h = a.q_h;
+  a.o_i = a.q_i;
+  a.o_b = a.q_b;
+  a.k_h = D;
+  a.k_j = (int64_t)a.Hkv * D;
+  a.k_b = (int64_t)S * a.k_j;
+  a.B = B;
+  a.L = L;
+  a.S = S;
+  a.n_cached = n_cached;
+  return a;
+}
+
+// Stream path (key preparation pass + streaming attention) applies to bf16 MFMA shapes; it needs
+// workspace only when some keys must be normed or rotated.
+static bool prefill_stream_applies(const gqa_attn_cfg* cfg, const gqa::AttnArgs& a) {
+  gqa::AttnArgs t = a;
+  // support checks look at the position pointers; any non-null stand-in will do here
+  static const int32_t dummy = 0;
+  t.qpos = &dummy;
+  t.kpos = &dummy;
+  return cfg->dtype == GQA_BF16 && g_policy == 0 && a.S > 0 && gqa::prefill_stream_supported(t);
+}
+
+size_t gqa_prefill_workspace_bytes(const gqa_attn_cfg* cfg, int32_t B, int32_t S, int32_t n_cached) {
+  if (check_cfg(cfg) != GQA_OK) return 0;
+  if (B < 0 || S < 0 || n_cached < 0 || n_cached > S) {
+    fail(GQA_E_SHAPE, "need B >= 0 and 0 <= n_cached <= S, got B=%d S=%d n_cached=%d", B, S,
+         n_cached);
+    return 0;
+  }
+  gqa::AttnArgs a = prefill_args(cfg, B, 1, S, n_cached);
+  if (!prefill_stream_applies(cfg, a)) return 0;
+  const size_t n = gqa::prefill_stream_workspace_bytes(a);
+  return (n + 255) & ~(size_t)255;
+}
+
 gqa_status gqa_attn_prefill(const gqa_attn_cfg* cfg, const void* q, const void* k, const void* v,
                             const int32_t* positions, int64_t pos_batch_stride,
                             const int32_t* key_positions, int64_t kpos_batch_stride, int32_t B,
                             int32_t L, int32_t S, int32_t n_cached, int32_t window, void* out,
-                            hipStream_t stream) {
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   gqa_status st = check_cfg(cfg);
   if (st != GQA_OK) return st;
   if (B < 0 || L < 0 || S < 0)
@@ -217,35 +261,56 @@ gqa_status gqa_attn_prefill(const gqa_attn_cfg* cfg, const void* q, const void* 
     return fail(GQA_E_VALUE, "q, k, v and out must be 16-byte aligned");
   if ((int64_t)L * cfg->num_q_heads > INT32_MAX)
     return fail(GQA_E_SHAPE, "L * num_q_heads exceeds 2^31");
-  gqa::AttnArgs a = base_args(cfg);
-  const int64_t D = cfg->head_dim;
+  if (workspace_bytes > 0 && !workspace)
+    return fail(GQA_E_WORKSPACE, "workspace is null but workspace_bytes is %zu", workspace_bytes);
+  if (workspace && ((uintptr_t)workspace & 255u) != 0)
+    return fail(GQA_E_WORKSPACE, "workspace must be 256-byte aligned");
+  gqa::AttnArgs a = prefill_args(cfg, B, L, S, n_cached);
   a.q = q;
   a.k = k;
   a.v = v;
   a.out = out;
-  a.q_h = D;
-  a.q_i = (int64_t)a.Hq * D;
-  a.q_b = (int64_t)L * a.q_i;
-  a.o_h = a.q_h;
-  a.o_i = a.q_i;
-  a.o_b = a.q_b;
-  a.k_h = D;
-  a.k_j = (int64_t)a.Hkv * D;
-  a.k_b = (int64_t)S * a.k_j;
   a.qpos = positions;
   a.qpos_b = pos_batch_stride;
   a.kpos = key_positions;
   a.kpos_b = kpos_batch_stride;
   a.lens = nullptr;
-  a.B = B;
-  a.L = L;
-  a.S = S;
-  a.n_cached = n_cached;
   a.window = window;
   const bool bf16 = cfg->dtype == GQA_BF16;
+  if (prefill_stream_applies(cfg, a)) {
+    const size_t need = gqa::prefill_stream_workspace_bytes(a);
+    if (need == 0 || (workspace && workspace_bytes >= need))
+      return hip_status(gqa::launch_prefill_stream(a, workspace, stream), "prefill (stream) launch");
+    if (workspace)
+      return fail(GQA_E_WORKSPACE, "prefill workspace needs %zu bytes, got %zu", need,
+                  workspace_bytes);
+  }
   if (bf16 && g_policy == 0 && S > 0 && gqa::prefill_mfma_supported(a))
-    return hip_status(gqa::launch_prefill_mfma(a, stream), "prefill (mfma) launch");
+    return hip_status(gqa::launch_prefill_mfma(a, stream), "prefill (fused) launch");
   return hip_status(gqa::launch_attn_generic(a, bf16, stream), "prefill (generic) launch");
+}
+
+gqa_status gqa_prep_keys(const gqa_attn_cfg* cfg, const void* k, const int32_t* key_positions,
+                         int64_t kpos_batch_stride, int32_t B, int32_t S, int32_t n_cached,
+                         void* k_out, hipStream_t stream) {
+  gqa_status st = check_cfg(cfg);
+  if (st != GQA_OK) return st;
+  if (B < 0 || S < 0 || n_cached < 0 || n_cached > S)
+    return fail(GQA_E_SHAPE, "need B >= 0 and 0 <= n_cached <= S, got B=%d S=%d n_cached=%d", B,
+                S, n_cached);
+  if (B > 65535) return fail(GQA_E_SHAPE, "B must be <= 65535, got %d", B);
+  if (kpos_batch_stride < 0) return fail(GQA_E_SHAPE, "kpos_batch_stride must be >= 0");
+  gqa::AttnArgs a = prefill_args(cfg, B, 1, S, n_cached);
+  if (cfg->dtype != GQA_BF16 || !gqa::prep_keys_supported(a))
+    return fail(GQA_E_UNSUPPORTED, "prep_keys covers bf16 with head_dim 128 and the MFMA rotary "
+                "widths only");
+  if (B == 0 || S == n_cached) return ok();
+  if (!k || !k_out || !key_positions) return fail(GQA_E_NULL, "k, key_positions and k_out are required");
+  if (!aligned16(k) || !aligned16(k_out)) return fail(GQA_E_VALUE, "k and k_out must be 16-byte aligned");
+  a.k = k;
+  a.kpos = key_positions;
+  a.kpos_b = kpos_batch_stride;
+  return hip_status(gqa::launch_prep_keys(a, k_out, stream), "prep_keys launch");
 }
 
 static bool decode_uses_mfma(const gqa_attn_cfg* cfg) {

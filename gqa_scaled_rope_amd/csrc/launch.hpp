@@ -22,6 +22,17 @@ hipError_t launch_attn_generic(const AttnArgs& a, bool bf16, hipStream_t stream)
 bool prefill_mfma_supported(const AttnArgs& a);
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);
 
+// bf16 MFMA prefill over prepared keys (K/V streamed HBM -> LDS): an optional key-preparation
+// pass into `workspace`, then the attention kernel.
+bool prefill_needs_kprep(const AttnArgs& a);
+bool prefill_stream_supported(const AttnArgs& a);
+size_t prefill_stream_workspace_bytes(const AttnArgs& a);
+hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t stream);
+// The key-preparation pass on its own: rows [n_cached, S) of a.k, normed and rotated, written to
+// k_out with k's layout [B, S, Hkv, D].
+bool prep_keys_supported(const AttnArgs& a);
+hipError_t launch_prep_keys(const AttnArgs& a, void* k_out, hipStream_t stream);
+
 // bf16 split-KV decode for head_dim 128 (split kernel + combine kernel).
 bool decode_mfma_supported(const AttnArgs& a);
 size_t decode_mfma_workspace_bytes(int B, int Hkv, int G, int D, int Smax);

@@ -96,6 +96,23 @@ gqa_status gqa_rope_tables(const gqa_rope_params* rope, int32_t table_len, float
  * Lets a caller inspect the schedule without a GPU. */
 gqa_status gqa_rope_inv_freq(const gqa_rope_params* rope, double* inv_freq_out);
 
+/* Prepare new keys for a cache: for every row j in [n_cached, S) of k [B, S, Hkv, D] and every KV
+ * head, RMS-norm the row (when cfg->qk_norm, gain k_norm_w) and rotate its first rotary_dim
+ * features at key_positions[b, j], then store it (dtype of cfg) at the same (b, j, g) of k_out
+ * [B, S, Hkv, D] ([Models] "What differs between model families": keys are normed and rotated,
+ * then appended to the cache by cache.update).  Rows j < n_cached of k_out are not touched.  k_out
+ * may be k itself (in place).  A following gqa_attn_prefill over k_out with n_cached = S then uses
+ * every key as stored.  bf16 with head_dim 128 and the rotary widths the MFMA kernels accept
+ * (any multiple of 8 interleaved, 16/32/64/128 half-split); otherwise GQA_E_UNSUPPORTED. */
+gqa_status gqa_prep_keys(const gqa_attn_cfg* cfg, const void* k, const int32_t* key_positions,
+                         int64_t kpos_batch_stride, int32_t B, int32_t S, int32_t n_cached,
+                         void* k_out, hipStream_t stream);
+
+/* Bytes of device workspace that lets gqa_attn_prefill prepare the new keys once instead of in
+ * every key tile (0 when nothing needs preparing: no norm and no rotation, or n_cached == S).
+ * Returns 0 and sets the error on invalid arguments. */
+size_t gqa_prefill_workspace_bytes(const gqa_attn_cfg* cfg, int32_t B, int32_t S, int32_t n_cached);
+
 /* Causal prefill ([Models] "What differs between model families", DecoderAttention.forward;
  * [Guide] section 3.4 "Attention").
  *   q   device [B, L, Hq, D]  new queries (contiguous)
@@ -107,6 +124,12 @@ gqa_status gqa_rope_inv_freq(const gqa_rope_params* rope, double* inv_freq_out);
  *   window         0 = full causal; w > 0: a query at position p sees keys at positions
  *                  p-w+1 .. p ([Models] "Sliding windows": keys more than w-1 back are masked)
  *   out  device [B, L, Hq, D] (contiguous, caller-owned), never aliasing the inputs.
+ *   workspace  optional device scratch of >= gqa_prefill_workspace_bytes() bytes, 256-byte
+ *              aligned, caller-owned, contents ignored: the new keys are normed and rotated once
+ *              into it (one pass) and the attention kernel streams them.  Null (with 0 bytes)
+ *              selects the fused kernel, which normalises and rotates new keys on the fly; both
+ *              give the same result up to rounding order.  Calls sharing a workspace must be
+ *              ordered on one stream.
  * Result per (b, i, h): softmax over allowed keys of scale*<q', k'> (soft-capped if set), times
  * v; a row with no allowed key is 0.  B, L, S >= 0 (an empty problem is a no-op); n_cached in
  * [0, S]. */
@@ -114,7 +137,7 @@ gqa_status gqa_attn_prefill(const gqa_attn_cfg* cfg, const void* q, const void* 
                             const int32_t* positions, int64_t pos_batch_stride,
                             const int32_t* key_positions, int64_t kpos_batch_stride, int32_t B,
                             int32_t L, int32_t S, int32_t n_cached, int32_t window, void* out,
-                            hipStream_t stream);
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of device workspace gqa_attn_decode needs for B sequences of capacity Smax (0 if the
  * chosen kernel needs none).  Returns 0 and sets the error on invalid arguments. */

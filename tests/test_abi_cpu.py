@@ -49,9 +49,9 @@ FAKE = 1 << 20  # aligned non-null host-side stand-in; validation fails before a
 
 
 def _prefill(c, B=1, L=4, S=4, n_cached=0, window=0, q=FAKE, k=FAKE, v=FAKE, pos=FAKE, kpos=FAKE,
-             out=FAKE):
+             out=FAKE, ws=None, ws_bytes=0):
     return lib.gqa_attn_prefill(ctypes.byref(c) if c is not None else None, q, k, v, pos, 0, kpos,
-                                0, B, L, S, n_cached, window, out, None)
+                                0, B, L, S, n_cached, window, out, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -90,6 +90,17 @@ def test_prefill_rejects_bad_sizes_and_pointers():
     assert _prefill(c, B=0, q=None, k=None, v=None, pos=None, kpos=None, out=None) == 0
     assert _prefill(c, L=0, q=None, k=None, v=None, pos=None, kpos=None, out=None) == 0
     assert g.last_error() == ""
+    # workspace: null with bytes, misaligned, too small for a shape that needs key preparation
+    assert _prefill(c, ws=None, ws_bytes=64) == 5
+    assert _prefill(c, ws=FAKE + 16, ws_bytes=1 << 20) == 5
+    cr = _cfg(rotary_dim=128, cos_table=FAKE, sin_table=FAKE, table_len=8)
+    need = lib.gqa_prefill_workspace_bytes(ctypes.byref(cr), 2, 300, 100)
+    assert need == 2 * 200 * 8 * 128 * 2                     # new keys only, bf16
+    assert _prefill(cr, B=2, L=300, S=300, n_cached=100, ws=FAKE, ws_bytes=need - 2) == 5
+    assert lib.gqa_prefill_workspace_bytes(ctypes.byref(cr), 2, 300, 300) == 0  # all cached
+    assert lib.gqa_prefill_workspace_bytes(ctypes.byref(_cfg()), 2, 300, 0) == 0  # nothing to prep
+    assert lib.gqa_prefill_workspace_bytes(ctypes.byref(cr), 2, 300, 301) == 0
+    assert "n_cached" in g.last_error()
 
 
 def test_decode_validation_and_workspace():
