@@ -16,6 +16,8 @@
 //     returns zeros past the last key, which handles the ragged tail.  Each wave instruction fills
 //     1 KB of LDS in lane order; choosing the source chunk per lane produces the XOR-swizzled
 //     layout the MFMA operand reads want.
+#include <type_traits>
+
 #include "launch.hpp"
 
 namespace gqa {
@@ -29,6 +31,7 @@ constexpr int BN = 64;
 constexpr int TILE_ELEMS = BN * HD;
 constexpr float kRescaleThreshold = 8.0f;
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit dwords, range checked
+constexpr int kXcds = 8;               // MI355X: 8 accelerator complex dies, one L2 each
 
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -50,11 +53,43 @@ __device__ __forceinline__ u32x4 pack8(const float* x) {
   return w;
 }
 
-__device__ __forceinline__ int lower_bound_pos(const int32_t* kp, int n, int64_t x) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    int mid = (lo + hi) >> 1;
-    if ((int64_t)kp[mid] < x) lo = mid + 1; else hi = mid;
+
+// LDS layout of a tile: row r's 16-byte chunk c sits at chunk position c ^ swz(r).  K tiles use
+// swz = r & 15 (conflict-free for the 16 rows one ds_read_b128 touches).  V tiles use a
+// permutation that also keeps the transposing reads conflict-free: each 16-lane group of
+// ds_read_b64_tr_b16 reads two adjacent chunks of four consecutive rows, and (r & 3) << 1 spreads
+// those eight 16-byte pieces over all eight bank groups.
+__device__ __forceinline__ int kswz(int r) { return r & 15; }
+__device__ __forceinline__ int vswz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+
+// Index j in [0, n] with kp[j-1] <= x - 1 < kp[j] (first j with kp[j] >= x), guessing that key
+// positions are consecutive from kp[0]; the guess is checked exactly and -1 returned if wrong.
+__device__ __forceinline__ int guess_lower_bound(const int32_t* kp, int n, int64_t x, int32_t kp0) {
+  const int64_t gg = x - (int64_t)kp0;
+  const int gi = (int)min<int64_t>(max<int64_t>(gg, 0), n);
+  const bool left_ok = gi == 0 || (int64_t)kp[gi - 1] < x;
+  const bool right_ok = gi == n || (int64_t)kp[gi] >= x;
+  return (left_ok && right_ok) ? gi : -1;
+}
+
+// First index j in [0, n) with kp[j] >= x for a nondecreasing kp, found by the whole wavefront:
+// each round samples 64 evenly spaced entries and keeps the one segment that contains the
+// boundary, so n keys take ceil(log64 n) dependent loads instead of log2 n.
+__device__ __forceinline__ int wave_lower_bound(const int32_t* kp, int n, int64_t x) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = n;  // answer in [lo, hi]
+  while (hi > lo) {
+    const int stride = (hi - lo + 63) >> 6;
+    const int idx = lo + lane * stride;
+    const bool below = idx < hi && (int64_t)kp[idx] < x;
+    const int cnt = __popcll(__ballot(below));
+    if (cnt == 0) {
+      hi = lo;
+    } else {
+      const int nlo = lo + (cnt - 1) * stride + 1;
+      hi = min(lo + cnt * stride, hi);
+      lo = nlo;
+    }
   }
   return lo;
 }
@@ -157,11 +192,23 @@ __global__ __launch_bounds__(256) void k_prep_kernel(AttnArgs a, PrepOut po, int
 // ---------------------------------------------------------------------------------------------
 // 2. attention over prepared keys
 // ---------------------------------------------------------------------------------------------
-struct Smem {
-  uint16_t k[2][TILE_ELEMS];
-  uint16_t v[2][TILE_ELEMS];
-  int32_t kpos[2][BN];
-};
+// Double-buffered K/V/key-position tiles.  Each buffer is its own LDS object and the tile loop
+// is unrolled by two, so every access names its buffer at compile time: the compiler can then
+// see that reads of the current tile never alias the asynchronous HBM->LDS loads of the next one
+// and does not make them wait for those loads.
+__shared__ __attribute__((aligned(16))) uint16_t g_k0[TILE_ELEMS];
+__shared__ __attribute__((aligned(16))) uint16_t g_k1[TILE_ELEMS];
+__shared__ __attribute__((aligned(16))) uint16_t g_v0[TILE_ELEMS];
+__shared__ __attribute__((aligned(16))) uint16_t g_v1[TILE_ELEMS];
+__shared__ __attribute__((aligned(16))) int32_t g_p0[BN];
+__shared__ __attribute__((aligned(16))) int32_t g_p1[BN];
+
+template <int BUF>
+__device__ __forceinline__ uint16_t* kbuf() { return BUF ? g_k1 : g_k0; }
+template <int BUF>
+__device__ __forceinline__ uint16_t* vbuf() { return BUF ? g_v1 : g_v0; }
+template <int BUF>
+__device__ __forceinline__ int32_t* pbuf() { return BUF ? g_p1 : g_p0; }
 
 struct StreamArgs {
   AttnArgs a;
@@ -170,13 +217,31 @@ struct StreamArgs {
 
 template <int ROT, bool NORM, bool CAP>
 __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, int nqb) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
   const AttnArgs& a = sa.a;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int ql = lane & 31, hg = lane >> 5;
-  const int qb = nqb - 1 - (int)blockIdx.x;  // heaviest (latest) query blocks first
-  const int g = blockIdx.y, b = blockIdx.z;
+  // Work item of this workgroup.  Workgroups are dealt to the 8 XCDs round-robin by id; map ids
+  // so that every query block of one (b, g) lands on the same XCD (its K/V then stay in that
+  // XCD's L2), heaviest (latest) query blocks first within each XCD.
+  int qb, g, b;
+  {
+    const int L = blockIdx.x;
+    const int npairs = a.B * a.Hkv;
+    int pair, rank;
+    if (npairs % kXcds == 0) {
+      const int per = npairs / kXcds;
+      const int x = L % kXcds, k = L / kXcds;
+      pair = x + kXcds * (k % per);
+      rank = k / per;
+    } else {
+      pair = L % npairs;
+      rank = L / npairs;
+    }
+    qb = nqb - 1 - rank;
+    b = pair / a.Hkv;
+    g = pair % a.Hkv;
+  }
   const int G = a.G;
   const int64_t nrows = (int64_t)a.L * G;
   const int64_t f0 = (int64_t)qb * ROWS;
@@ -189,90 +254,17 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   const int32_t* qpos_b = a.qpos + (int64_t)b * a.qpos_b;
   const int64_t qp = qvalid ? (int64_t)qpos_b[qi] : 0;
 
-  // ---- query prep: norm, rotate, scale into log2 units, keep chunks 2s + hg as bf16 ----
-  const float qscale = a.scale * kLog2e;
-  bf16x8 qop[8];
-  {
-    const uint16_t* qr = (const uint16_t*)a.q + (int64_t)b * a.q_b + (int64_t)qi * a.q_i +
-                         (int64_t)qh * a.q_h;
-    float rs = 1.f;
-    if (NORM) {
-      float ss = 0.f;
-      if (qvalid) {
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          float x[8];
-          unpack8(ld16(qr + 8 * c), x);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-        }
-      }
-      rs = rsqrtf(ss * (1.0f / HD) + a.eps);
-    }
-    const uint16_t* qw = (const uint16_t*)a.qw;
-    const int64_t tp = ROT ? min<int64_t>(max<int64_t>(qp, 0), a.table_len - 1) : 0;
-    const int halfp = a.R >> 1;
-    const float* cr = ROT ? a.cos_t + tp * halfp : nullptr;
-    const float* sr = ROT ? a.sin_t + tp * halfp : nullptr;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int c = 2 * s + hg;
-      float x[8];
-      if (qvalid) {
-        unpack8(ld16(qr + 8 * c), x);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.f;
-      }
-      if (NORM) {
-        float wv[8];
-        unpack8(ld16(qw + 8 * c), wv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] *= rs * wv[e];
-      }
-      if (ROT == 1 && qvalid && 8 * c < a.R) {
-        const int pc = c ^ (a.R >> 4);
-        float y[8];
-        unpack8(ld16(qr + 8 * pc), y);
-        if (NORM) {
-          float wv[8];
-          unpack8(ld16(qw + 8 * pc), wv);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] *= rs * wv[e];
-        }
-        rotate_chunk<1>(x, y, c, a.R, cr, sr);
-      } else if (ROT == 2 && qvalid) {
-        rotate_chunk<2>(x, x, c, a.R, cr, sr);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] *= qscale;
-      qop[s] = as_bf16x8(pack8(x));
-    }
-  }
-
-  // ---- key band of the workgroup's query positions ----
-  int64_t qmin, qmax;
-  {
-    const int i_lo = (int)(f0 / G);
-    const int i_hi = (int)min<int64_t>((f0 + ROWS - 1) / G, (int64_t)a.L - 1);
-    int64_t mn = INT64_MAX, mx = INT64_MIN;
-    for (int i = i_lo + lane; i <= i_hi; i += 64) {
-      const int64_t p = qpos_b[i];
-      mn = min(mn, p);
-      mx = max(mx, p);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      mn = min(mn, (int64_t)__shfl_xor(mn, off, 64));
-      mx = max(mx, (int64_t)__shfl_xor(mx, off, 64));
-    }
-    qmin = mn;
-    qmax = mx;
-  }
+  // ---- key band of the workgroup's query positions (loads issued here, used after Q prep) ----
   const int32_t* kpos_b = a.kpos + (int64_t)b * a.kpos_b;
-  const int j_hi = lower_bound_pos(kpos_b, a.S, qmax + 1);
-  const int j_lo = a.window > 0 ? min(lower_bound_pos(kpos_b, a.S, qmin - a.window + 1), j_hi) : 0;
-  const int n_tiles = (j_hi - j_lo + BN - 1) / BN;
+  const int i_lo = (int)(f0 / G);
+  const int i_hi = (int)min<int64_t>((f0 + ROWS - 1) / G, (int64_t)a.L - 1);
+  int64_t pmn = INT64_MAX, pmx = INT64_MIN;
+  for (int i = i_lo + lane; i <= i_hi; i += 64) {
+    const int64_t p = qpos_b[i];
+    pmn = min(pmn, p);
+    pmx = max(pmx, p);
+  }
+  const int32_t kp0 = kpos_b[0];
 
   // ---- buffer descriptors of this (b, g): cached keys, prepared keys, values ----
   const int row_bytes = (int)(a.k_j * 2);  // bytes between consecutive keys of one head
@@ -289,31 +281,121 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
       (short)0, (sa.kprep && nnew > 0) ? (nnew - 1) * row_bytes + HD * 2 : 0, kBufFlags);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const uint16_t*)a.v + kv_base), (short)0, (a.S - 1) * row_bytes + HD * 2, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.kpos + (int64_t)b * a.kpos_b), (short)0, a.S * 4, kBufFlags);
 
   // Tile loader: wave w, round i fills LDS rows 4*(w + 8i) .. +3 (1 KB); lane -> row 4(w+8i) +
   // lane/16, LDS chunk lane%16, which holds source chunk (lane%16) ^ (row & 15).
-  auto issue_tile = [&](int jt, int buf) {
+  auto issue_tile = [&](int jt, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = 4 * (w + 8 * i) + (lane >> 4);
       const int j = jt + r;
-      const int csrc = (lane & 15) ^ (r & 15);
-      lds_void* kdst = (lds_void*)(&sm.k[buf][4 * (w + 8 * i) * HD]);
-      lds_void* vdst = (lds_void*)(&sm.v[buf][4 * (w + 8 * i) * HD]);
-      const int vo = j * row_bytes + csrc * 16;
+      const int csrc = (lane & 15) ^ kswz(r);
+      const int vsrc = (lane & 15) ^ vswz(r);
+      lds_void* kdst = (lds_void*)(kbuf<buf>() + 4 * (w + 8 * i) * HD);
+      lds_void* vdst = (lds_void*)(vbuf<buf>() + 4 * (w + 8 * i) * HD);
+      const int vo = j * row_bytes + vsrc * 16;
+      const int ko = j * row_bytes + csrc * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vdst, 16, j < a.S ? vo : 0x7fffffff, 0, 0, 0);
       if (j < nc) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, vo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, ko, 0, 0, 0);
       } else {
         const int wo = (j - nc) * row_bytes + csrc * 16;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, kdst, 16, j < a.S ? wo : 0x7fffffff, 0, 0, 0);
       }
     }
-    if (tid < BN) {
-      const int j = jt + tid;
-      sm.kpos[buf][tid] = j < j_hi ? kpos_b[j] : 0x7fffffff;
-    }
+    // key positions of the tile (rows past the band are excluded by index in the mask)
+    if (w == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (lds_void*)pbuf<buf>(), 4, (jt + lane) * 4, 0,
+                                               0, 0);
   };
+
+  // Without a window the first tile starts at key 0: start its loads before the query prep.
+  if (a.window == 0) issue_tile(0, std::integral_constant<int, 0>());
+
+  // ---- query prep: norm, rotate, scale into log2 units, keep chunks 2s + hg as bf16 ----
+  // All loads are issued before any arithmetic (one memory round trip).  Lane (row, hg) loads its
+  // own chunks 2s + hg and, for half-split rotation, their partners (c ^ R/16); the row's sum of
+  // squares is its own half plus the other half from lane ^ 32.  Rows past the end read row 0
+  // and are zeroed.
+  const float qscale = a.scale * kLog2e;
+  bf16x8 qop[8];
+  {
+    const uint16_t* qr = (const uint16_t*)a.q + (int64_t)b * a.q_b + (int64_t)qi * a.q_i +
+                         (int64_t)qh * a.q_h;
+    const uint16_t* qw = (const uint16_t*)a.qw;
+    const int P = a.R >> 4;
+    u32x4 own[8], par[8], wown[8], wpar[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int c = 2 * s + hg;
+      own[s] = ld16(qr + 8 * c);
+      if (ROT == 1) par[s] = ld16(qr + 8 * (c ^ P));
+      if (NORM) wown[s] = ld16(qw + 8 * c);
+      if (NORM && ROT == 1) wpar[s] = ld16(qw + 8 * (c ^ P));
+    }
+    const int64_t tp = ROT ? min<int64_t>(max<int64_t>(qp, 0), a.table_len - 1) : 0;
+    const int halfp = a.R >> 1;
+    const float* cr = ROT ? a.cos_t + tp * halfp : nullptr;
+    const float* sr = ROT ? a.sin_t + tp * halfp : nullptr;
+    float rs = 1.f;
+    if (NORM) {
+      float ss = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        float x[8];
+        unpack8(own[s], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+      }
+      ss += swap_halves(ss);
+      rs = rsqrtf(ss * (1.0f / HD) + a.eps);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int c = 2 * s + hg;
+      float y[8];
+      unpack8(own[s], y);
+      if (NORM) {
+        float wv[8];
+        unpack8(wown[s], wv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] *= rs * wv[e];
+      }
+      if (ROT == 1) {
+        float pv[8];
+        unpack8(par[s], pv);
+        if (NORM) {
+          float wv[8];
+          unpack8(wpar[s], wv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] *= rs * wv[e];
+        }
+        rotate_chunk<1>(y, pv, c, a.R, cr, sr);
+      } else if (ROT == 2) {
+        rotate_chunk<2>(y, y, c, a.R, cr, sr);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = qvalid ? y[e] * qscale : 0.f;
+      qop[s] = as_bf16x8(pack8(y));
+    }
+  }
+
+  // ---- band: first key past the newest query, first key inside the oldest query's window ----
+  int64_t qmin = pmn, qmax = pmx;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    qmin = min(qmin, (int64_t)__shfl_xor(qmin, off, 64));
+    qmax = max(qmax, (int64_t)__shfl_xor(qmax, off, 64));
+  }
+  int j_hi = guess_lower_bound(kpos_b, a.S, qmax + 1, kp0);
+  int j_lo = a.window > 0 ? guess_lower_bound(kpos_b, a.S, qmin - a.window + 1, kp0) : 0;
+  if (j_hi < 0) j_hi = wave_lower_bound(kpos_b, a.S, qmax + 1);
+  if (j_lo < 0) j_lo = wave_lower_bound(kpos_b, a.S, qmin - a.window + 1);
+  j_lo = min(j_lo, j_hi);
+  const int n_tiles = (j_hi - j_lo + BN - 1) / BN;
 
   f32x16 o[4];
 #pragma unroll
@@ -324,40 +406,78 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   const float cap2 = a.softcap * kLog2e;
   const float inv_cap2 = CAP ? 1.0f / cap2 : 0.f;
 
-  // per-lane LDS read offsets (elements): K rows kb*32 + ql, chunk 2s + hg
+  // per-lane LDS read offsets (elements).  K: row ql (+32 for the second half), chunk 2s + hg.
+  // V^T (transposing reads): rows 4*hgv + s16/4 (+8 for items 4..7) of each 16-key group,
+  // columns db*32 + 16*(gi&1) + 4*(s16&3); both swizzles only see the row's low 4 bits, which
+  // the 16- and 32-key group offsets leave unchanged.
   const int gi = lane >> 4, s16 = lane & 15;
   const int hgv = gi >> 1;
-
-  if (n_tiles > 0) {
-    issue_tile(j_lo, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  int koff[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) koff[s] = ql * HD + (((2 * s + hg) ^ kswz(ql)) << 3);
+  int voff[2][4];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int row = 4 * hgv + (s16 >> 2) + 8 * h2;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int col = db * 32 + 16 * (gi & 1) + 4 * (s16 & 3);
+      voff[h2][db] = row * HD + (((col >> 3) ^ vswz(row)) << 3) + (col & 7);
+    }
   }
+  // mask bounds in int32: allowed <=> qlo32 <= key position <= qp32
+  const int32_t qp32 = qvalid ? (int32_t)qp : INT32_MIN;
+  const int32_t qlo32 = !qvalid ? INT32_MAX
+                        : a.window > 0 ? (int32_t)max<int64_t>(qp - a.window + 1, INT32_MIN)
+                                       : INT32_MIN;
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  // One tile: prefetch the next tile into the other buffer, compute this one, then wait for the
+  // prefetch and synchronise.
+  auto tile = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const int jt = j_lo + t * BN;
-    if (t + 1 < n_tiles) issue_tile(jt + BN, buf ^ 1);
-
-    const int32_t kfirst = sm.kpos[buf][0];
-    const int32_t klast = sm.kpos[buf][BN - 1];
+    if (t + 1 < n_tiles) issue_tile(jt + BN, std::integral_constant<int, buf ^ 1>());
+    const int32_t kfirst = pbuf<buf>()[0];
+    const int32_t klast = pbuf<buf>()[BN - 1];
     const bool full = (jt + BN <= j_hi) && ((int64_t)klast <= qmin) &&
                       (a.window == 0 || qmax - (int64_t)kfirst <= a.window - 1);
-    const uint16_t* ks = sm.k[buf];
-    const uint16_t* vs = sm.v[buf];
+    const uint16_t* ks = kbuf<buf>();
+    const uint16_t* vs = vbuf<buf>();
+
+    // K operands of the first 32-key half
+    u32x4 kop[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kop[s] = *(const u32x4*)(ks + koff[s]);
 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // ---- S^T = K Q^T for 32 keys ----
       f32x16 sacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-      const int krow = kb * 32 + ql;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int off = krow * HD + (((2 * s + hg) ^ (krow & 15)) << 3);
-        const bf16x8 ka = as_bf16x8(*(const u32x4*)(ks + off));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[s], sacc, 0, 0, 0);
+      for (int s = 0; s < 8; ++s)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[s]), qop[s], sacc, 0, 0, 0);
+      // V^T operands of this half, and the next half's K operands, in flight during the softmax
+      i16x4 vlo[2][4], vhi[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int base = (kb * 32 + 16 * u) * HD;
+          vlo[u][db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vs + base + voff[0][db]));
+          vhi[u][db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vs + base + voff[1][db]));
+        }
+      if (kb == 0) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) kop[s] = *(const u32x4*)(ks + 32 * HD + koff[s]);
       }
+
+      // ---- soft-cap and mask ----
       if (CAP) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -370,11 +490,13 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kk = kb * 32 + 8 * (r >> 2) + 4 * hg + (r & 3);
-          const int64_t kp = sm.kpos[buf][kk];
-          const bool ok = qvalid && kp <= qp && (a.window == 0 || qp - kp <= a.window - 1);
+          const int32_t kp = pbuf<buf>()[kk];
+          const bool ok = (jt + kk < j_hi) && kp <= qp32 && kp >= qlo32;
           if (!ok) sacc[r] = -INFINITY;
         }
       }
+
+      // ---- online softmax (row = this lane's query; the other 16 keys live in lane ^ 32) ----
       float mt = sacc[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
@@ -400,27 +522,28 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
         }
         pb[u] = as_bf16x8(pack8(p));
       }
+
+      // ---- O^T += V^T P^T ----
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int row1 = kb * 32 + 16 * u + 4 * hgv + (s16 >> 2);
-        const int row2 = row1 + 8;
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const int col = db * 32 + 16 * (gi & 1) + 4 * (s16 & 3);
-          const int off1 = row1 * HD + (((col >> 3) ^ (row1 & 15)) << 3) + (col & 7);
-          const int off2 = row2 * HD + (((col >> 3) ^ (row2 & 15)) << 3) + (col & 7);
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vs + off1));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vs + off2));
-          const i16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const i16x8 va = {vlo[u][db][0], vlo[u][db][1], vlo[u][db][2], vlo[u][db][3],
+                            vhi[u][db][0], vhi[u][db][1], vhi[u][db][2], vhi[u][db][3]};
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pb[u],
                                                           o[db], 0, 0, 0);
         }
-      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+
+  if (a.window > 0 && n_tiles > 0) issue_tile(j_lo, B0());
+  __builtin_amdgcn_s_waitcnt(0);  // also retires the early first-tile loads when n_tiles == 0
+  __syncthreads();
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile(t, B0());
+    if (t + 1 < n_tiles) tile(t + 1, B1());
   }
 
   const float ltot = lsum + swap_halves(lsum);
@@ -446,8 +569,8 @@ hipError_t launch_attn(const StreamArgs& sa, hipStream_t stream) {
   const AttnArgs& a = sa.a;
   const int64_t nrows = (int64_t)a.L * a.G;
   const int nqb = (int)((nrows + ROWS - 1) / ROWS);
-  hipLaunchKernelGGL((prefill_stream_kernel<ROT, NORM, CAP>), dim3(nqb, a.Hkv, a.B), dim3(NT), 0,
-                     stream, sa, nqb);
+  hipLaunchKernelGGL((prefill_stream_kernel<ROT, NORM, CAP>), dim3(nqb * a.Hkv * a.B), dim3(NT),
+                     0, stream, sa, nqb);
   return hipGetLastError();
 }
 template <int ROT, bool NORM>
