@@ -382,3 +382,19 @@ def test_prep_keys_then_cached_prefill(name):
                          wl.S, wl.window)
     torch.cuda.synchronize()
     check(out.float().cpu().numpy(), ref_prefill(wl, x))
+
+
+def test_all_scores_far_below_zero(policy):
+    # every score about -147 in log2 units: exp2 of the unshifted scores underflows, so the
+    # kernels must take the running max from the first scores they see
+    wl = BASE.with_(qk_norm=False, rotary_dim=0, L=130, S=130)
+    x = prefill_inputs(wl, seed=51)
+    r = np.random.default_rng(51)
+    u = np.ones(wl.D, np.float32)
+    x["q"] = (3.0 * u + 0.3 * r.standard_normal(x["q"].shape)).astype(np.float32)
+    x["k"] = (-3.0 * u + 0.3 * r.standard_normal(x["k"].shape)).astype(np.float32)
+    from synth import round_to
+    x["q"], x["k"] = round_to(x["q"], "bf16"), round_to(x["k"], "bf16")
+    ref = ref_prefill(wl, x)
+    assert np.abs(ref).max() > 0.05      # a real (non-degenerate) softmax
+    check(gpu_prefill(wl, x), ref)
