@@ -60,6 +60,23 @@ def decode_bytes(wl, lens):
             + 2 * wl.B * wl.Hq * wl.D * eb + 4 * wl.B)
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter runs (profiles/traffic.json:
+    FETCH_SIZE and WRITE_SIZE scaled by a known-size copy), or None when the kernel's source has
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)["kernels"][kernel]
+        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+                return None
+        return int(rec["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 # ---- helpers ---------------------------------------------------------------------------------
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -243,6 +260,9 @@ def main(argv=None):
     ap.add_argument("--decode-workload", default="llama31_decode_bf16")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (three times), the "
+                         "known-size reference for scaling HBM byte counters")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus "
@@ -250,6 +270,18 @@ def main(argv=None):
         return 2
 
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}), flush=True)
+        return 0
 
     import gqa_scaled_rope_amd as g
     from synth import WORKLOADS
@@ -277,7 +309,8 @@ def main(argv=None):
         "roofline": {"bound": "mfma", "kernel": "prefill_stream_kernel",
                      "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel_ms_mean": round(kern_ms, 4),
+                     "traffic": measured_traffic("prefill_stream_kernel"),
+                     "kernel_ms_mean": round(kern_ms, 4),
                      "kernel_ms_median": round(kern_med, 4), "algorithmic_flop": flops},
         "step_parts_ms": {k: round(v[0], 4) for k, v in stats.items()},
     }
@@ -299,7 +332,8 @@ def main(argv=None):
                "ms_per_call": round(dms, 4), "algorithmic_bytes": nbytes,
                "roofline": {"bound": "hbm", "kernel": "decode_split_kernel + decode_combine_kernel",
                             "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                            "frac": round(gbs / HBM_PEAK_GBS, 4),
+                            "traffic": measured_traffic("decode_split_kernel"),
                             "kernel_ms_mean": round(dms, 4), "kernel_ms_median": round(dmed, 4)}}
         if not args.no_cpu_baseline:
             dec["cpu_baseline"] = cpu_baseline_decode(dwl, dx, torch)
