@@ -6,17 +6,29 @@
 // rotated, so they are read as stored).
 //
 // The step is bound by HBM: every cached K and V row is read exactly once and serves all
-// G = Hq/Hkv query heads of its KV head ([Models] stretch exercise 5's "read each row once for the
-// whole head group").  Work item = (sequence b, KV head g, split of 1024 keys); a workgroup of 4
-// wavefronts streams the split, 256 keys per wavefront in blocks of 32, with the next block's
-// global loads in flight while the current one is computed.  Per block:
-//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K straight from the loaded registers as the A
-//   operand; the G query heads padded to 16 columns as the B operand);
-//   online softmax in log2 units, lazily rescaled as in the prefill kernel;
-//   O = P V on the same MFMA, P taken lane-locally from the score accumulators as the A operand
-//   and V read back from a wave-private LDS staging buffer with ds_read_b64_tr_b16.
-// The four wavefronts merge (max, sum, output) in LDS and write one partial per work item; the
-// combine kernel merges the partials of a sequence by their log-sum-exp weights.
+// G = Hq/Hkv query heads of its KV head (the grouping [Models] stretch exercise 5 asks a decode
+// kernel to exploit).  Three launches:
+//   decode_prep_q_kernel   every query row normed, rotated, scaled into log2 units, as bf16;
+//   decode_split_kernel    a persistent grid walking a dense list of work items (sequence b,
+//                          KV head g, split of 1024 keys); a workgroup's 4 wavefronts take 256
+//                          keys each, in blocks of 32:
+//                            S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K straight from the loaded
+//                            registers as the A operand, the G heads padded to 16 columns as B);
+//                            online softmax in log2 units, lazily rescaled;
+//                            O = P V on the same MFMA, P from the score accumulators, V read back
+//                            from a wave-private LDS staging buffer with ds_read_b64_tr_b16;
+//                          the wavefronts merge in LDS into one partial (O, max, sum) per item;
+//   decode_combine_kernel  merges the partials of a sequence by their log-sum-exp weights.
+//
+// Why persistent: a workgroup that ends with stores in flight holds its slot until they drain,
+// which under full read load costs several microseconds per item.  Here a workgroup issues the
+// next item's query and first K/V block, then the previous item's stores, and only then waits
+// for the new loads; the stores drain behind useful traffic.  Since the vector-memory counter
+// retires loads and stores in issue order, every load and store in that sequence is
+// unconditional (ranges that must not be touched are cut off by buffer descriptors), so the
+// compiler's wait counts are exact and no wait ever covers the stores.
+#include <algorithm>
+
 #include "launch.hpp"
 
 namespace gqa {
@@ -29,176 +41,234 @@ constexpr int SPLIT = 1024;
 constexpr int SUB = SPLIT / DWAVES;  // keys per wavefront
 constexpr int KBLK = 32;             // keys per block
 constexpr int MAXG = 16;
+constexpr int kPlanMax = 2048;       // sequences per launch of the split kernel
+constexpr int kWgPerCu = 3;          // resident split workgroups per CU (LDS and VGPR budget)
 constexpr float kRescaleThreshold = 8.0f;
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit elements
+// Cache rows are read exactly once per call, so they are loaded non-temporally (policy bit "nt"),
+// which streams measurably faster than ordinary loads on MI355X once the XCDs are evenly loaded.
+constexpr int kStreamPolicy = 2;
 
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
+struct DecodeArgs {
+  AttnArgs a;
+  float* part_o;      // [B, Hkv, nsplit, G, D] unnormalised partial outputs
+  float* part_ml;     // [B, Hkv, nsplit, G, 2] running max (log2 units) and sum
+  uint16_t* qprep;    // [B, Hq, D] prepared queries (bf16, log2 units)
+  int32_t nsplit;     // splits per (b, g) allotted in the workspace
+};
+
 __device__ __forceinline__ int vt_off(int r, int c) { return r * HD + ((c ^ (r & 15)) << 3); }
 
-__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kRsrcFlags);
+}
 
-__device__ __forceinline__ void unpack8(const u32x4& w, float* x) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[2 * e] = bf16lo(w[e]);
-    x[2 * e + 1] = bf16hi(w[e]);
+// Barrier over LDS traffic only: the fences order each wavefront's LDS accesses around
+// s_barrier without waiting for its outstanding global loads and stores.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---- query preparation --------------------------------------------------------------------------
+// One workgroup of HD threads per (query head h, sequence b), thread d = feature d: the row is
+// RMS-normed ([Guide] section 3.2) when enabled, rotated at position lens[b]-1 ([Guide] section 4;
+// half-split or adjacent pairs), multiplied by scale * log2(e) and rounded to bf16.
+template <int ROT, bool NORM>
+__global__ __launch_bounds__(HD) void decode_prep_q_kernel(AttnArgs a, uint16_t* qprep) {
+  __shared__ float red[HD / 64];
+  __shared__ float row[HD];
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const uint16_t* qr = (const uint16_t*)a.q + (int64_t)b * a.q_b + (int64_t)h * a.q_h;
+  float x = bf16_to_f32(qr[d]);
+  if (NORM) {
+    const float ss = wave_sum(x * x);
+    if ((d & 63) == 0) red[d >> 6] = ss;
+    __syncthreads();
+    const float rs = rsqrtf((red[0] + red[1]) * (1.0f / HD) + a.eps);
+    x *= rs * bf16_to_f32(((const uint16_t*)a.qw)[d]);
   }
+  if (ROT) {
+    row[d] = x;
+    __syncthreads();
+    const int n = min(max(a.lens[b], 0), a.S);
+    const int64_t tp = min<int64_t>(max<int64_t>((int64_t)n - 1, 0), a.table_len - 1);
+    const int half = a.R >> 1;
+    if (d < a.R) {
+      if (ROT == 1) {  // pairs (i, i + R/2)
+        const int p = d < half ? d : d - half;
+        const float cs = a.cos_t[tp * half + p], sn = a.sin_t[tp * half + p];
+        x = d < half ? x * cs - row[d + half] * sn : row[d - half] * sn + x * cs;
+      } else {         // pairs (2i, 2i + 1)
+        const int p = d >> 1;
+        const float cs = a.cos_t[tp * half + p], sn = a.sin_t[tp * half + p];
+        x = (d & 1) == 0 ? x * cs - row[d + 1] * sn : row[d - 1] * sn + x * cs;
+      }
+    }
+  }
+  const float qscale = a.scale * kLog2e;
+  qprep[((int64_t)b * a.Hq + h) * HD + d] = f32_to_bf16(x * qscale);
 }
-__device__ __forceinline__ u32x4 pack8(const float* x) {
-  u32x4 w;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
-  return w;
-}
+
+// ---- split kernel -------------------------------------------------------------------------------
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& w) { return __builtin_bit_cast(bf16x8, w); }
 
-struct DecodeSmem {
-  uint16_t v[DWAVES][KBLK * HD];        // wave-private V staging
-  float mo[DWAVES][MAXG][HD];           // per-wave partial outputs
-  float mm[DWAVES][MAXG];               // per-wave running max
-  float ml[DWAVES][MAXG];               // per-wave running sum
+struct SplitSmem {
+  // A wavefront's V staging buffer and, once its keys are done, its partial output share the
+  // same 8 KB (LDS operations of one wavefront complete in order, so the reuse needs no barrier).
+  union {
+    uint16_t v[DWAVES][KBLK * HD];  // wave-private V staging
+    float mo[DWAVES][MAXG][HD];     // per-wave partial outputs
+  };
+  float mm[DWAVES][MAXG];           // per-wave running max
+  float ml[DWAVES][MAXG];           // per-wave running sum
+  int plan[kPlanMax + 1];           // exclusive prefix over sequences of their work items
+  int len[kPlanMax];                // clamped sequence lengths
+  int wsum[DWAVES];
 };
+static_assert(KBLK * HD * 2 == MAXG * HD * 4, "staging and partial output share one region");
 
 struct BlockRegs {
   u32x4 k[2][4];  // [16-key half][k-step]
   u32x4 v[8];     // rows (lane>>4) + 4e, chunk lane&15
 };
 
-__device__ __forceinline__ void load_block(const uint16_t* kbase, const uint16_t* vbase, int kb0,
-                                           int kend, BlockRegs& br) {
+// Loads the block of 32 keys starting at kb0 with buffer loads: keys at or beyond the end of the
+// descriptors' range read as zero without a memory access, so no lane needs a branch.
+__device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                           int kb0, BlockRegs& br) {
   const int lane = threadIdx.x & 63;
-  const u32x4 z = {0u, 0u, 0u, 0u};
+  // unsigned: offsets of blocks past the end may exceed INT32_MAX; they are out of range either way
+  const unsigned kofs = ((unsigned)(kb0 + (lane & 15)) * HD + 8 * (lane >> 4)) * 2;
+  const unsigned vofs = ((unsigned)(kb0 + (lane >> 4)) * HD + 8 * (lane & 15)) * 2;
 #pragma unroll
-  for (int kq = 0; kq < 2; ++kq) {
-    const int key = kb0 + kq * 16 + (lane & 15);
+  for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      br.k[kq][s] = key < kend ? ld16(kbase + (int64_t)key * HD + 8 * (4 * s + (lane >> 4))) : z;
-  }
+      br.k[kq][s] = __builtin_amdgcn_raw_buffer_load_b128(
+          rk, (int)(kofs + (kq * 16 * HD + 32 * s) * 2), 0, kStreamPolicy);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int key = kb0 + (lane >> 4) + 4 * e;
-    br.v[e] = key < kend ? ld16(vbase + (int64_t)key * HD + 8 * (lane & 15)) : z;
-  }
+  for (int e = 0; e < 8; ++e)
+    br.v[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(vofs + 4 * e * HD * 2), 0,
+                                                    kStreamPolicy);
+  // keep the 16 loads together: the scheduler would otherwise start on the K operands as they
+  // arrive and issue the V loads a full memory latency later
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int ROT>
-__device__ __forceinline__ void rotate8(float* x, const float* y, int c, int R, const float* cr,
-                                        const float* sr) {
-  const int d0 = 8 * c;
-  if (d0 >= R) return;
-  if (ROT == 1) {
-    const int half = R >> 1;
-    const bool first = d0 < half;
-    const int p0 = first ? d0 : d0 - half;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float cs = cr[p0 + e], sn = sr[p0 + e];
-      x[e] = first ? (x[e] * cs - y[e] * sn) : (y[e] * sn + x[e] * cs);
-    }
-  } else if (ROT == 2) {
-    const int p0 = d0 >> 1;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float cs = cr[p0 + e], sn = sr[p0 + e];
-      const float a = x[2 * e], b = x[2 * e + 1];
-      x[2 * e] = a * cs - b * sn;
-      x[2 * e + 1] = a * sn + b * cs;
-    }
-  }
-}
+// A work item as one wavefront sees it (all fields wave-uniform).  A null item (none left) has
+// we = 0 and empty descriptor ranges.
+struct Item {
+  int b, g, sp, ws, we, nblk;
+  bool valid;
+};
 
-template <int ROT, bool NORM, bool CAP>
-__global__ __launch_bounds__(DT, 2) void decode_split_kernel(DecodeArgs da) {
-  __shared__ DecodeSmem sm;
+template <bool CAP>
+__global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs da) {
+  __shared__ SplitSmem sm;
   const AttnArgs& a = da.a;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int G = a.G;
-  const int n = min(max(a.lens[b], 0), a.S);
-  const int start = a.window > 0 ? max(0, n - a.window) : 0;
-  const int nkeys = n - start;
-  const int nsp = (nkeys + SPLIT - 1) / SPLIT;
-  if (sp >= nsp) return;
-  const int ks = start + sp * SPLIT;
-  const int ke = min(ks + SPLIT, n);
-  const int ws = ks + w * SUB;
-  const int we = min(ws + SUB, ke);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int B = a.B, Hkv = a.Hkv, G = a.G;
 
-  // ---- query operand: head slot hs = lane & 15 (zero beyond G), chunk 4s + (lane >> 4) ----
-  const int hs = lane & 15, cg = lane >> 4;
-  const bool hvalid = hs < G;
-  bf16x8 qop[4];
-  {
-    const uint16_t* qr = (const uint16_t*)a.q + (int64_t)b * a.q_b +
-                         (int64_t)(g * G + (hvalid ? hs : 0)) * a.q_h;
-    float rs = 1.f;
-    if (NORM) {
-      float ss = 0.f;
-#pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        float x[8];
-        unpack8(ld16(qr + 8 * c), x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-      }
-      rs = rsqrtf(ss * (1.0f / HD) + a.eps);
-    }
-    const uint16_t* qw = (const uint16_t*)a.qw;
-    const int halfp = a.R >> 1;
-    const int64_t tp = ROT ? min<int64_t>(max<int64_t>((int64_t)n - 1, 0), a.table_len - 1) : 0;
-    const float* cr = ROT ? a.cos_t + tp * halfp : nullptr;
-    const float* sr = ROT ? a.sin_t + tp * halfp : nullptr;
-    const float qscale = a.scale * kLog2e;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int c = 4 * s + cg;
-      float x[8];
-      unpack8(ld16(qr + 8 * c), x);
-      if (NORM) {
-        float wv[8];
-        unpack8(ld16(qw + 8 * c), wv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] *= rs * wv[e];
-      }
-      if (ROT == 1 && 8 * c < a.R) {
-        const int pc = c ^ (a.R >> 4);
-        float y[8];
-        unpack8(ld16(qr + 8 * pc), y);
-        if (NORM) {
-          float wv[8];
-          unpack8(ld16(qw + 8 * pc), wv);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] *= rs * wv[e];
-        }
-        rotate8<1>(x, y, c, a.R, cr, sr);
-      } else if (ROT == 2) {
-        rotate8<2>(x, x, c, a.R, cr, sr);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = hvalid ? x[e] * qscale : 0.f;
-      qop[s] = as_bf16x8(pack8(x));
-    }
+  // ---- plan: items of sequence i = Hkv * (splits of its window); exclusive prefix in LDS -------
+  for (int i = tid; i < B; i += DT) {
+    const int n = min(max(a.lens[i], 0), a.S);
+    const int start = a.window > 0 ? max(0, n - a.window) : 0;
+    sm.len[i] = n;
+    sm.plan[i] = ((n - start + SPLIT - 1) / SPLIT) * Hkv;
   }
-
-  const int64_t kv_base = (int64_t)b * a.k_b + (int64_t)g * a.k_h;
-  const uint16_t* kbase = (const uint16_t*)a.k + kv_base;
-  const uint16_t* vbase = (const uint16_t*)a.v + kv_base;
-  uint16_t* vs = sm.v[w];
-
-  f32x4 o[8];
+  __syncthreads();
+  {
+    const int per = (B + DT - 1) / DT;
+    const int i0 = min(tid * per, B), i1 = min(i0 + per, B);
+    int loc = 0;
+    for (int i = i0; i < i1; ++i) loc += sm.plan[i];
+    int x = loc;  // inclusive scan over the wavefront
 #pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m = kNegBig, lsum = 0.f;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) sm.wsum[w] = x;
+    __syncthreads();
+    int run = x - loc;
+    for (int ww = 0; ww < w; ++ww) run += sm.wsum[ww];
+    for (int i = i0; i < i1; ++i) {
+      const int c = sm.plan[i];
+      sm.plan[i] = run;
+      run += c;
+    }
+    if (tid == 0) sm.plan[B] = sm.wsum[0] + sm.wsum[1] + sm.wsum[2] + sm.wsum[3];
+    __syncthreads();
+  }
+  const int total = __builtin_amdgcn_readfirstlane(sm.plan[B]);
+  if ((int)blockIdx.x >= total) return;
+
+  // Item t: the sequence b with plan[b] <= t < plan[b + 1], then KV head and split within it.
+  // Consecutive items go to consecutive workgroups, hence round-robin over the XCDs.
+  auto locate = [&](int t) {
+    Item it;
+    it.valid = t < total;
+    if (!it.valid) {
+      it.b = it.g = it.sp = it.ws = it.we = it.nblk = 0;
+      return it;
+    }
+    int lo = 0, hi = B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (__builtin_amdgcn_readfirstlane(sm.plan[mid]) <= t) lo = mid;
+      else hi = mid;
+    }
+    const int p0 = __builtin_amdgcn_readfirstlane(sm.plan[lo]);
+    const int p1 = __builtin_amdgcn_readfirstlane(sm.plan[lo + 1]);
+    const int n = __builtin_amdgcn_readfirstlane(sm.len[lo]);
+    const int nsp = (p1 - p0) / Hkv;
+    const int r = t - p0;
+    it.b = lo;
+    it.g = r / nsp;
+    it.sp = r - it.g * nsp;
+    const int start = a.window > 0 ? max(0, n - a.window) : 0;
+    const int ks = start + it.sp * SPLIT;
+    const int ke = min(ks + SPLIT, n);
+    it.ws = ks + w * SUB;
+    it.we = min(it.ws + SUB, ke);
+    it.nblk = it.we > it.ws ? (it.we - it.ws + KBLK - 1) / KBLK : 0;
+    return it;
+  };
+  // Descriptors of an item: its K and V rows up to this wavefront's last key, its G prepared query
+  // rows, and its partial-output slots.  Empty ranges for a null item.
+  auto kv_rsrc = [&](const Item& it, const void* base) {
+    const int64_t off = (int64_t)it.b * a.k_b + (int64_t)it.g * a.k_h;
+    return rsrc((const uint16_t*)base + off, max(it.we, 0) * HD * 2);
+  };
+  auto q_rsrc = [&](const Item& it) {
+    return rsrc(da.qprep + ((int64_t)it.b * a.Hq + (int64_t)it.g * G) * HD,
+                it.valid ? G * HD * 2 : 0);
+  };
+  auto part_index = [&](const Item& it) {
+    return (((int64_t)it.b * Hkv + it.g) * da.nsplit + it.sp) * G;
+  };
+
+  // query operand: head slot hs = lane & 15 (zero beyond G: outside the range), chunk 4s + cg
+  const int hs = lane & 15, cg = lane >> 4;
+  auto load_q = [&](__amdgpu_buffer_rsrc_t rq, u32x4* qv) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      qv[s] = __builtin_amdgcn_raw_buffer_load_b128(rq, (hs * HD + 8 * (4 * s + cg)) * 2, 0, 0);
+  };
+
+  uint16_t* vs = sm.v[w];
   const float cap2 = a.softcap * kLog2e;
   const float inv_cap2 = CAP ? 1.0f / cap2 : 0.f;
+  f32x4 o[8];
+  float m, lsum;
+  bf16x8 qop[4];
 
-  BlockRegs cur, nxt;
-  if (ws < we) load_block(kbase, vbase, ws, we, cur);
-  for (int kb0 = ws; kb0 < we; kb0 += KBLK) {
-    const bool has_next = kb0 + KBLK < we;
-    if (has_next) load_block(kbase, vbase, kb0 + KBLK, we, nxt);
-
+  auto block = [&](const BlockRegs& cur, int kb0, int we) {
     // stage V rows of this block in the wave's LDS buffer
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -221,10 +291,10 @@ __global__ __launch_bounds__(DT, 2) void decode_split_kernel(DecodeArgs da) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float x = sk[kq][r];
-        if (CAP) {
+        if (CAP) {  // cap * tanh(x / cap) via exp2, in log2 units
           const float y = x * inv_cap2;
           const float e = fast_exp2(-2.0f * kLog2e * fabsf(y));
-          x = copysignf(cap2 * (1.0f - e) / (1.0f + e), y);
+          x = copysignf(cap2 * (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e), y);
         }
         const int key = kb0 + kq * 16 + 4 * (lane >> 4) + r;
         sk[kq][r] = key < we ? x : -INFINITY;
@@ -255,7 +325,10 @@ __global__ __launch_bounds__(DT, 2) void decode_split_kernel(DecodeArgs da) {
         p[4 * kq + r] = fast_exp2(sk[kq][r] - m);
         lsum += p[4 * kq + r];
       }
-    const bf16x8 pa = as_bf16x8(pack8(p));
+    u32x4 pw;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+    const bf16x8 pa = as_bf16x8(pw);
 
     // O = P V: B operand = V[32 keys][16 features] via transposing LDS reads
     const int gi = lane >> 4, si = lane & 15;
@@ -274,87 +347,169 @@ __global__ __launch_bounds__(DT, 2) void decode_split_kernel(DecodeArgs da) {
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, vb), o[db],
                                                       0, 0, 0);
     }
-    if (has_next) cur = nxt;
-  }
+  };
 
-  // ---- merge the four wavefronts ----
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  if (lane < 16 && hvalid) {
-    sm.mm[w][hs] = m;
-    sm.ml[w][hs] = lsum;
-  }
+  // Merge the four wavefronts' partials in LDS and store them: thread tid owns column tid & 127 of
+  // rows 2k + (tid >> 7), and row tid's (max, sum); rows at or beyond G fall outside the
+  // descriptors' ranges and are dropped.  A fixed count of unconditional stores per thread.
+  auto merge_store = [&](__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rml) {
+    const int d = tid & (HD - 1);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * (lane >> 4) + r;
-    if (row < G) {
+    for (int k = 0; k < MAXG * HD / DT; ++k) {
+      const int row = 2 * k + (tid >> 7);
+      float M = kNegBig;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) sm.mo[w][row][16 * db + (lane & 15)] = o[db][r];
+      for (int ww = 0; ww < DWAVES; ++ww) M = fmaxf(M, sm.mm[ww][row]);
+      float acc = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < DWAVES; ++ww) acc += fast_exp2(sm.mm[ww][row] - M) * sm.mo[ww][row][d];
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), ro, (row * HD + d) * 4, 0, 0);
     }
-  }
-  __syncthreads();
-  const int64_t item = (((int64_t)b * a.Hkv + g) * da.nsplit + sp) * G;
-  for (int x = tid; x < G * HD; x += DT) {
-    const int row = x / HD, d = x % HD;
+    const int row = tid & (MAXG - 1);
     float M = kNegBig;
 #pragma unroll
     for (int ww = 0; ww < DWAVES; ++ww) M = fmaxf(M, sm.mm[ww][row]);
-    float acc = 0.f, lt = 0.f;
+    float lt = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < DWAVES; ++ww) {
-      const float sc = fast_exp2(sm.mm[ww][row] - M);
-      acc += sc * sm.mo[ww][row][d];
-      lt += sc * sm.ml[ww][row];
+    for (int ww = 0; ww < DWAVES; ++ww) lt += fast_exp2(sm.mm[ww][row] - M) * sm.ml[ww][row];
+    const u32x2 mlw = {__float_as_uint(M), __float_as_uint(lt)};
+    __builtin_amdgcn_raw_buffer_store_b64(mlw, rml, tid < MAXG ? row * 8 : INT32_MIN, 0, 0);
+  };
+
+  // ---- the item loop ----
+  int t = blockIdx.x;
+  Item cur = locate(t);
+  __amdgpu_buffer_rsrc_t rk = kv_rsrc(cur, a.k), rv = kv_rsrc(cur, a.v);
+  u32x4 qv[4];
+  load_q(q_rsrc(cur), qv);
+  BlockRegs ra;
+  load_block(rk, rv, cur.ws, ra);
+  // partial-output descriptors of the previous item: none before the first
+  __amdgpu_buffer_rsrc_t ro = rsrc(da.part_o, 0), rml = rsrc(da.part_ml, 0);
+  while (true) {
+    // previous item's partial (dropped on the first pass: empty ranges)
+    lds_barrier();
+    merge_store(ro, rml);
+    lds_barrier();
+
+    // this item
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qop[s] = as_bf16x8(qv[s]);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    m = kNegBig;
+    lsum = 0.f;
+    block(ra, cur.ws, cur.we);  // (all keys masked when this wavefront has none)
+    for (int i = 1; i < cur.nblk; ++i) {
+      load_block(rk, rv, cur.ws + i * KBLK, ra);
+      block(ra, cur.ws + i * KBLK, cur.we);
     }
-    da.part_o[(item + row) * HD + d] = acc;
-    if (d == 0) {
-      da.part_ml[(item + row) * 2 + 0] = M;
-      da.part_ml[(item + row) * 2 + 1] = lt;
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (lane < MAXG) {
+      sm.mm[w][lane] = m;
+      sm.ml[w][lane] = lsum;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int db = 0; db < 8; ++db) sm.mo[w][4 * (lane >> 4) + r][16 * db + (lane & 15)] = o[db][r];
+
+    const int64_t pi = part_index(cur);
+    ro = rsrc(da.part_o + pi * HD, G * HD * 4);
+    rml = rsrc(da.part_ml + pi * 2, G * 2 * 4);
+
+    // next item: its loads go out before this item's stores
+    t += gridDim.x;
+    cur = locate(t);
+    rk = kv_rsrc(cur, a.k);
+    rv = kv_rsrc(cur, a.v);
+    load_q(q_rsrc(cur), qv);
+    load_block(rk, rv, cur.ws, ra);
+    if (!cur.valid) {
+      lds_barrier();
+      merge_store(ro, rml);
+      break;
     }
   }
 }
 
 // out[b, h, :] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the splits of sequence b.
+// The first wavefront loads the (max, sum) pairs of all splits at once, reduces them and leaves
+// the split weights 2^(m_s - M) in LDS; then each thread owns one feature and sums the weighted
+// partial outputs, four splits per step so that their loads overlap.
+constexpr int kCombineMaxSplits = 256;  // 256K keys; longer caches use the weight formula inline
 __global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs da) {
   const AttnArgs& a = da.a;
+  __shared__ float wsc[kCombineMaxSplits];
+  __shared__ float stat[2];
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int G = a.G, g = h / G, hs = h % G;
   const int n = min(max(a.lens[b], 0), a.S);
   const int start = a.window > 0 ? max(0, n - a.window) : 0;
   const int nsp = (n - start + SPLIT - 1) / SPLIT;
   const int64_t item0 = (((int64_t)b * a.Hkv + g) * da.nsplit) * G + hs;
-  float M = kNegBig;
-  for (int s = 0; s < nsp; ++s) M = fmaxf(M, da.part_ml[(item0 + (int64_t)s * G) * 2]);
-  float acc = 0.f, lt = 0.f;
-  for (int s = 0; s < nsp; ++s) {
-    const int64_t it = item0 + (int64_t)s * G;
-    const float sc = fast_exp2(da.part_ml[it * 2] - M);
-    acc += sc * da.part_o[it * HD + d];
-    lt += sc * da.part_ml[it * 2 + 1];
+  const float* ml = da.part_ml;
+  if (d < 64) {
+    float M = kNegBig;
+    for (int s = d; s < nsp; s += 64) M = fmaxf(M, ml[(item0 + (int64_t)s * G) * 2]);
+    M = wave_max(M);
+    float lt = 0.f;
+    for (int s = d; s < nsp; s += 64) {
+      const int64_t it = item0 + (int64_t)s * G;
+      const float sc = fast_exp2(ml[it * 2] - M);
+      if (s < kCombineMaxSplits) wsc[s] = sc;
+      lt += sc * ml[it * 2 + 1];
+    }
+    lt = wave_sum(lt);
+    if (d == 0) {
+      stat[0] = M;
+      stat[1] = lt;
+    }
   }
+  __syncthreads();
+  const float M = stat[0], lt = stat[1];
+  const float* po = da.part_o + item0 * HD + d;
+  const int64_t step = (int64_t)G * HD;
+  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+  int s = 0;
+  for (; s + 4 <= nsp && s + 4 <= kCombineMaxSplits; s += 4) {
+    const float o0 = po[(int64_t)s * step], o1 = po[(int64_t)(s + 1) * step];
+    const float o2 = po[(int64_t)(s + 2) * step], o3 = po[(int64_t)(s + 3) * step];
+    acc0 += wsc[s] * o0;
+    acc1 += wsc[s + 1] * o1;
+    acc2 += wsc[s + 2] * o2;
+    acc3 += wsc[s + 3] * o3;
+  }
+  for (; s < nsp; ++s) {
+    const float sc = s < kCombineMaxSplits ? wsc[s] : fast_exp2(ml[(item0 + (int64_t)s * G) * 2] - M);
+    acc0 += sc * po[(int64_t)s * step];
+  }
+  const float acc = (acc0 + acc1) + (acc2 + acc3);
   const float r = lt > 0.f ? acc / lt : 0.f;
   uint16_t* orow = (uint16_t*)a.out + (int64_t)b * a.o_b + (int64_t)h * a.o_h;
   orow[d] = f32_to_bf16(r);
 }
 
-template <int ROT, bool NORM, bool CAP>
-hipError_t launch_variant(const DecodeArgs& d, hipStream_t stream) {
-  const AttnArgs& a = d.a;
-  dim3 grid(d.nsplit, a.Hkv, a.B);
-  hipLaunchKernelGGL((decode_split_kernel<ROT, NORM, CAP>), grid, dim3(DT), 0, stream, d);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.Hq, a.B), dim3(HD), 0, stream, d);
-  return hipGetLastError();
-}
 template <int ROT, bool NORM>
-hipError_t launch_cap(const DecodeArgs& d, hipStream_t s) {
-  return d.a.softcap > 0.f ? launch_variant<ROT, NORM, true>(d, s) : launch_variant<ROT, NORM, false>(d, s);
+void launch_prep(const AttnArgs& a, uint16_t* qprep, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_prep_q_kernel<ROT, NORM>), dim3(a.Hq, a.B), dim3(HD), 0, stream, a,
+                     qprep);
 }
-template <int ROT>
-hipError_t launch_norm(const DecodeArgs& d, hipStream_t s) {
-  return d.a.qk_norm ? launch_cap<ROT, true>(d, s) : launch_cap<ROT, false>(d, s);
+
+int cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  return n;
 }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -362,30 +517,66 @@ int decode_split_keys() { return SPLIT; }
 
 bool decode_mfma_supported(const AttnArgs& a) {
   if (a.D != HD || a.G > MAXG) return false;
-  if (a.R == 0) return true;
-  if (a.style == 0) {
-    const int P = a.R / 16;
-    return a.R % 16 == 0 && (P == 1 || P == 2 || P == 4 || P == 8);
-  }
-  return a.R % 8 == 0;
+  if ((int64_t)a.S * HD * 2 > INT32_MAX) return false;  // byte offsets within one (b, g) cache
+  return true;
 }
 
 size_t decode_mfma_workspace_bytes(int B, int Hkv, int G, int D, int Smax) {
   const int64_t nsplit = (Smax + SPLIT - 1) / SPLIT;
   const int64_t items = (int64_t)B * Hkv * nsplit * G;
-  const size_t o = (size_t)items * D * sizeof(float);
-  const size_t ml = (size_t)items * 2 * sizeof(float);
-  return ((o + 255) & ~(size_t)255) + ml;
+  return align256((size_t)items * D * sizeof(float)) + align256((size_t)items * 2 * sizeof(float)) +
+         (size_t)B * Hkv * G * D * sizeof(uint16_t);
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& d, hipStream_t stream) {
-  if (d.a.B == 0) return hipSuccess;
-  const int rot = d.a.R == 0 ? 0 : (d.a.style == 0 ? 1 : 2);
-  switch (rot) {
-    case 0: return launch_norm<0>(d, stream);
-    case 1: return launch_norm<1>(d, stream);
-    default: return launch_norm<2>(d, stream);
+hipError_t launch_decode_mfma(const AttnArgs& a, void* workspace, hipStream_t stream) {
+  if (a.B == 0) return hipSuccess;
+  DecodeArgs d;
+  d.a = a;
+  d.nsplit = (a.S + SPLIT - 1) / SPLIT;
+  const int64_t items = (int64_t)a.B * a.Hkv * d.nsplit * a.G;
+  char* ws = (char*)workspace;
+  d.part_o = (float*)ws;
+  d.part_ml = (float*)(ws + align256((size_t)items * HD * sizeof(float)));
+  d.qprep = (uint16_t*)(ws + align256((size_t)items * HD * sizeof(float)) +
+                        align256((size_t)items * 2 * sizeof(float)));
+
+  const int rot = a.R == 0 ? 0 : (a.style == 0 ? 1 : 2);
+  const bool norm = a.qk_norm != 0;
+  switch (rot * 2 + (norm ? 1 : 0)) {
+    case 0: launch_prep<0, false>(a, d.qprep, stream); break;
+    case 1: launch_prep<0, true>(a, d.qprep, stream); break;
+    case 2: launch_prep<1, false>(a, d.qprep, stream); break;
+    case 3: launch_prep<1, true>(a, d.qprep, stream); break;
+    case 4: launch_prep<2, false>(a, d.qprep, stream); break;
+    default: launch_prep<2, true>(a, d.qprep, stream); break;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // The split kernel plans at most kPlanMax sequences per launch (and keeps item ids in int32).
+  const int64_t per_seq = (int64_t)a.Hkv * d.nsplit;
+  const int chunk = (int)std::min<int64_t>(kPlanMax, std::max<int64_t>(1, INT32_MAX / per_seq));
+  const int resident = cu_count() * kWgPerCu;
+  for (int b0 = 0; b0 < a.B; b0 += chunk) {
+    const int nb = std::min(chunk, a.B - b0);
+    DecodeArgs c = d;
+    c.a.B = nb;
+    c.a.k = (const uint16_t*)a.k + (int64_t)b0 * a.k_b;
+    c.a.v = (const uint16_t*)a.v + (int64_t)b0 * a.k_b;
+    c.a.lens = a.lens + b0;
+    c.part_o = d.part_o + (int64_t)b0 * per_seq * a.G * HD;
+    c.part_ml = d.part_ml + (int64_t)b0 * per_seq * a.G * 2;
+    c.qprep = d.qprep + (int64_t)b0 * a.Hq * HD;
+    const int nwg = (int)std::min<int64_t>((int64_t)nb * per_seq, resident);
+    if (a.softcap > 0.f)
+      hipLaunchKernelGGL(decode_split_kernel<true>, dim3(nwg), dim3(DT), 0, stream, c);
+    else
+      hipLaunchKernelGGL(decode_split_kernel<false>, dim3(nwg), dim3(DT), 0, stream, c);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.Hq, a.B), dim3(HD), 0, stream, d);
+  return hipGetLastError();
 }
 
 }  // namespace gqa

@@ -83,12 +83,5 @@ struct AttnArgs {
   float softcap;             // 0 = off
 };
 
-struct DecodeArgs {
-  AttnArgs a;
-  float* part_o;             // [B, Hkv, nsplit, G, D] unnormalised partial outputs
-  float* part_ml;            // [B, Hkv, nsplit, G, 2] running max (log2 units) and sum
-  int32_t nsplit;            // splits per (b, g) allotted in the workspace
-  int32_t split_keys;        // keys per split
-};
 
 }  // namespace gqa

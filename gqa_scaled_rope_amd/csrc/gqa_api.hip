@@ -375,16 +375,7 @@ gqa_status gqa_attn_decode(const gqa_attn_cfg* cfg, const void* q, const void* k
                   workspace_bytes, workspace ? "" : " (null)");
     if (((uintptr_t)workspace & 255u) != 0)
       return fail(GQA_E_WORKSPACE, "workspace must be 256-byte aligned");
-    gqa::DecodeArgs d;
-    d.a = a;
-    const int split = gqa::decode_split_keys();
-    d.nsplit = (Smax + split - 1) / split;
-    d.split_keys = split;
-    const int64_t items = (int64_t)B * a.Hkv * d.nsplit * a.G;
-    const size_t o_bytes = (size_t)items * D * sizeof(float);
-    d.part_o = (float*)workspace;
-    d.part_ml = (float*)((char*)workspace + ((o_bytes + 255) & ~(size_t)255));
-    return hip_status(gqa::launch_decode_mfma(d, stream), "decode (mfma) launch");
+    return hip_status(gqa::launch_decode_mfma(a, workspace, stream), "decode (mfma) launch");
   }
   return hip_status(gqa::launch_attn_generic(a, cfg->dtype == GQA_BF16, stream),
                     "decode (generic) launch");

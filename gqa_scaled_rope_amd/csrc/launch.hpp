@@ -33,10 +33,11 @@ hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t
 bool prep_keys_supported(const AttnArgs& a);
 hipError_t launch_prep_keys(const AttnArgs& a, void* k_out, hipStream_t stream);
 
-// bf16 split-KV decode for head_dim 128 (split kernel + combine kernel).
+// bf16 split-KV decode for head_dim 128 (query preparation, split kernel, combine kernel); the
+// workspace holds the split partials and the prepared queries.
 bool decode_mfma_supported(const AttnArgs& a);
 size_t decode_mfma_workspace_bytes(int B, int Hkv, int G, int D, int Smax);
-hipError_t launch_decode_mfma(const DecodeArgs& d, hipStream_t stream);
+hipError_t launch_decode_mfma(const AttnArgs& a, void* workspace, hipStream_t stream);
 int decode_split_keys();
 
 }  // namespace gqa

@@ -106,9 +106,11 @@ def test_prefill_rejects_bad_sizes_and_pointers():
 def test_decode_validation_and_workspace():
     c = _cfg()
     need = lib.gqa_decode_workspace_bytes(ctypes.byref(c), 64, 32768)
-    # split partials: B * Hkv * ceil(Smax/1024) * G * (D + 2) floats (+ alignment)
-    assert need >= 64 * 8 * 32 * 4 * 130 * 4
-    assert need < 64 * 8 * 32 * 4 * 130 * 4 + 4096
+    # split partials, B * Hkv * ceil(Smax/1024) * G * (D + 2) floats, each part 256-aligned,
+    # then the prepared queries, B * Hq * D bf16
+    items = 64 * 8 * 32 * 4
+    align = lambda x: (x + 255) // 256 * 256
+    assert need == align(items * 128 * 4) + align(items * 2 * 4) + 64 * 32 * 128 * 2
     st = lib.gqa_attn_decode(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 64, 32768, 0, FAKE, None,
                              0, None)
     assert st == 5 and "workspace" in g.last_error()
