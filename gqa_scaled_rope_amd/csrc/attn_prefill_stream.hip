@@ -62,16 +62,6 @@ __device__ __forceinline__ u32x4 pack8(const float* x) {
 __device__ __forceinline__ int kswz(int r) { return r & 15; }
 __device__ __forceinline__ int vswz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
 
-// Index j in [0, n] with kp[j-1] <= x - 1 < kp[j] (first j with kp[j] >= x), guessing that key
-// positions are consecutive from kp[0]; the guess is checked exactly and -1 returned if wrong.
-__device__ __forceinline__ int guess_lower_bound(const int32_t* kp, int n, int64_t x, int32_t kp0) {
-  const int64_t gg = x - (int64_t)kp0;
-  const int gi = (int)min<int64_t>(max<int64_t>(gg, 0), n);
-  const bool left_ok = gi == 0 || (int64_t)kp[gi - 1] < x;
-  const bool right_ok = gi == n || (int64_t)kp[gi] >= x;
-  return (left_ok && right_ok) ? gi : -1;
-}
-
 // First index j in [0, n) with kp[j] >= x for a nondecreasing kp, found by the whole wavefront:
 // each round samples 64 evenly spaced entries and keeps the one segment that contains the
 // boundary, so n keys take ceil(log64 n) dependent loads instead of log2 n.
@@ -192,23 +182,32 @@ __global__ __launch_bounds__(256) void k_prep_kernel(AttnArgs a, PrepOut po, int
 // ---------------------------------------------------------------------------------------------
 // 2. attention over prepared keys
 // ---------------------------------------------------------------------------------------------
-// Double-buffered K/V/key-position tiles.  Each buffer is its own LDS object and the tile loop
-// is unrolled by two, so every access names its buffer at compile time: the compiler can then
-// see that reads of the current tile never alias the asynchronous HBM->LDS loads of the next one
-// and does not make them wait for those loads.
+// Triple-buffered K/V/key-position tiles.  Each buffer is its own LDS object and the step loop
+// is unrolled over the buffer cycle, so every access names its buffer at compile time: the
+// compiler can then see that reads of the current tiles never alias the asynchronous HBM->LDS
+// loads of a later one and does not make them wait for those loads.
+constexpr int NBUF = 3;
 __shared__ __attribute__((aligned(16))) uint16_t g_k0[TILE_ELEMS];
 __shared__ __attribute__((aligned(16))) uint16_t g_k1[TILE_ELEMS];
+__shared__ __attribute__((aligned(16))) uint16_t g_k2[TILE_ELEMS];
 __shared__ __attribute__((aligned(16))) uint16_t g_v0[TILE_ELEMS];
 __shared__ __attribute__((aligned(16))) uint16_t g_v1[TILE_ELEMS];
+__shared__ __attribute__((aligned(16))) uint16_t g_v2[TILE_ELEMS];
 __shared__ __attribute__((aligned(16))) int32_t g_p0[BN];
 __shared__ __attribute__((aligned(16))) int32_t g_p1[BN];
+__shared__ __attribute__((aligned(16))) int32_t g_p2[BN];
 
 template <int BUF>
-__device__ __forceinline__ uint16_t* kbuf() { return BUF ? g_k1 : g_k0; }
+__device__ __forceinline__ uint16_t* kbuf() { return BUF == 0 ? g_k0 : BUF == 1 ? g_k1 : g_k2; }
 template <int BUF>
-__device__ __forceinline__ uint16_t* vbuf() { return BUF ? g_v1 : g_v0; }
+__device__ __forceinline__ uint16_t* vbuf() { return BUF == 0 ? g_v0 : BUF == 1 ? g_v1 : g_v2; }
 template <int BUF>
-__device__ __forceinline__ int32_t* pbuf() { return BUF ? g_p1 : g_p0; }
+__device__ __forceinline__ int32_t* pbuf() { return BUF == 0 ? g_p0 : BUF == 1 ? g_p1 : g_p2; }
+// Before tile 1 is loaded, the K and V areas of buffers 1 and 2 stage the workgroup's prepared
+// queries: rows 64k .. 64k + 63 in area k (16-byte chunk c of row r at chunk c ^ (r & 15)).
+__device__ __forceinline__ uint16_t* qstage(int k) {
+  return k == 0 ? g_k1 : k == 1 ? g_v1 : k == 2 ? g_k2 : g_v2;
+}
 
 struct StreamArgs {
   AttnArgs a;
@@ -252,17 +251,23 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   const int qi = qvalid ? (int)(f / G) : 0;
   const int qh = g * G + (qvalid ? (int)(f % G) : 0);
   const int32_t* qpos_b = a.qpos + (int64_t)b * a.qpos_b;
-  const int64_t qp = qvalid ? (int64_t)qpos_b[qi] : 0;
+  const int32_t qp_raw = qpos_b[qi];  // qi is a valid index even for rows past the end
+  const int32_t qp = qvalid ? qp_raw : 0;
 
   // ---- key band of the workgroup's query positions (loads issued here, used after Q prep) ----
   const int32_t* kpos_b = a.kpos + (int64_t)b * a.kpos_b;
   const int i_lo = (int)(f0 / G);
   const int i_hi = (int)min<int64_t>((f0 + ROWS - 1) / G, (int64_t)a.L - 1);
-  int64_t pmn = INT64_MAX, pmx = INT64_MIN;
-  for (int i = i_lo + lane; i <= i_hi; i += 64) {
-    const int64_t p = qpos_b[i];
-    pmn = min(pmn, p);
-    pmx = max(pmx, p);
+  // (at most ROWS positions; every load is issued, at a clamped index, before any is used)
+  int32_t prange[ROWS / 64];
+#pragma unroll
+  for (int k = 0; k < ROWS / 64; ++k) prange[k] = qpos_b[min(i_lo + lane + 64 * k, i_hi)];
+  int32_t pmn = INT32_MAX, pmx = INT32_MIN;
+#pragma unroll
+  for (int k = 0; k < ROWS / 64; ++k) {
+    const bool in = i_lo + lane + 64 * k <= i_hi;
+    pmn = min(pmn, in ? prange[k] : INT32_MAX);
+    pmx = max(pmx, in ? prange[k] : INT32_MIN);
   }
   const int32_t kp0 = kpos_b[0];
 
@@ -284,6 +289,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.kpos + (int64_t)b * a.kpos_b), (short)0, a.S * 4, kBufFlags);
 
+  uint32_t kp_pend = 0;
+  bool kp_pend_ok = false;
   // Tile loader: wave w, round i fills LDS rows 4*(w + 8i) .. +3 (1 KB); lane -> row 4(w+8i) +
   // lane/16, LDS chunk lane%16, which holds source chunk (lane%16) ^ (row & 15).
   auto issue_tile = [&](int jt, auto bufc) {
@@ -306,94 +313,136 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, kdst, 16, j < a.S ? wo : 0x7fffffff, 0, 0, 0);
       }
     }
-    // key positions of the tile (rows past the band are excluded by index in the mask)
-    if (w == 0)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (lds_void*)pbuf<buf>(), 4, (jt + lane) * 4, 0,
-                                               0, 0);
+    // key positions of the tile: loaded by wave 0 into a register and written to LDS by
+    // commit_kpos once the tile's loads are complete, with INT32_MAX past the last key so that the
+    // position test alone masks the ragged tail
+    if (w == 0) {
+      kp_pend = __builtin_amdgcn_raw_buffer_load_b32(rp, (jt + lane) * 4, 0, 0);
+      kp_pend_ok = jt + lane < a.S;
+    }
+  };
+  auto commit_kpos = [&](auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    if (w == 0) pbuf<buf>()[lane] = kp_pend_ok ? (int32_t)kp_pend : INT32_MAX;
   };
 
   // Without a window the first tile starts at key 0: start its loads before the query prep.
   if (a.window == 0) issue_tile(0, std::integral_constant<int, 0>());
 
-  // ---- query prep: norm, rotate, scale into log2 units, keep chunks 2s + hg as bf16 ----
-  // All loads are issued before any arithmetic (one memory round trip).  Lane (row, hg) loads its
-  // own chunks 2s + hg and, for half-split rotation, their partners (c ^ R/16); the row's sum of
-  // squares is its own half plus the other half from lane ^ 32.  Rows past the end read row 0
-  // and are zeroed.
-  const float qscale = a.scale * kLog2e;
-  bf16x8 qop[8];
-  {
-    const uint16_t* qr = (const uint16_t*)a.q + (int64_t)b * a.q_b + (int64_t)qi * a.q_i +
-                         (int64_t)qh * a.q_h;
-    const uint16_t* qw = (const uint16_t*)a.qw;
-    const int P = a.R >> 4;
-    u32x4 own[8], par[8], wown[8], wpar[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int c = 2 * s + hg;
-      own[s] = ld16(qr + 8 * c);
-      if (ROT == 1) par[s] = ld16(qr + 8 * (c ^ P));
-      if (NORM) wown[s] = ld16(qw + 8 * c);
-      if (NORM && ROT == 1) wpar[s] = ld16(qw + 8 * (c ^ P));
-    }
-    const int64_t tp = ROT ? min<int64_t>(max<int64_t>(qp, 0), a.table_len - 1) : 0;
-    const int halfp = a.R >> 1;
-    const float* cr = ROT ? a.cos_t + tp * halfp : nullptr;
-    const float* sr = ROT ? a.sin_t + tp * halfp : nullptr;
-    float rs = 1.f;
-    if (NORM) {
-      float ss = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        float x[8];
-        unpack8(own[s], x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-      }
-      ss += swap_halves(ss);
-      rs = rsqrtf(ss * (1.0f / HD) + a.eps);
-    }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int c = 2 * s + hg;
-      float y[8];
-      unpack8(own[s], y);
-      if (NORM) {
-        float wv[8];
-        unpack8(wown[s], wv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] *= rs * wv[e];
-      }
-      if (ROT == 1) {
-        float pv[8];
-        unpack8(par[s], pv);
-        if (NORM) {
-          float wv[8];
-          unpack8(wpar[s], wv);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pv[e] *= rs * wv[e];
-        }
-        rotate_chunk<1>(y, pv, c, a.R, cr, sr);
-      } else if (ROT == 2) {
-        rotate_chunk<2>(y, y, c, a.R, cr, sr);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = qvalid ? y[e] * qscale : 0.f;
-      qop[s] = as_bf16x8(pack8(y));
-    }
-  }
-
-  // ---- band: first key past the newest query, first key inside the oldest query's window ----
-  int64_t qmin = pmn, qmax = pmx;
+  // ---- band guesses: with consecutive key positions the band edges are known from the query
+  // positions; the two keys around each guess are loaded now (clamped indices) and checked below
+  int32_t qmn = pmn, qmx = pmx;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    qmin = min(qmin, (int64_t)__shfl_xor(qmin, off, 64));
-    qmax = max(qmax, (int64_t)__shfl_xor(qmax, off, 64));
+    qmn = min(qmn, __shfl_xor(qmn, off, 64));
+    qmx = max(qmx, __shfl_xor(qmx, off, 64));
   }
-  int j_hi = guess_lower_bound(kpos_b, a.S, qmax + 1, kp0);
-  int j_lo = a.window > 0 ? guess_lower_bound(kpos_b, a.S, qmin - a.window + 1, kp0) : 0;
-  if (j_hi < 0) j_hi = wave_lower_bound(kpos_b, a.S, qmax + 1);
-  if (j_lo < 0) j_lo = wave_lower_bound(kpos_b, a.S, qmin - a.window + 1);
+  // wave-uniform from here on: scalar registers
+  const int64_t qmin = __builtin_amdgcn_readfirstlane(qmn), qmax = __builtin_amdgcn_readfirstlane(qmx);
+  const int64_t x_hi = qmax + 1, x_lo = qmin - a.window + 1;
+  const int g_hi = (int)min<int64_t>(max<int64_t>(x_hi - kp0, 0), a.S);
+  const int g_lo = (int)min<int64_t>(max<int64_t>(x_lo - kp0, 0), a.S);
+  const int32_t hi_l = kpos_b[max(g_hi - 1, 0)], hi_r = kpos_b[min(g_hi, a.S - 1)];
+  const int32_t lo_l = kpos_b[max(g_lo - 1, 0)], lo_r = kpos_b[min(g_lo, a.S - 1)];
+
+  // ---- query prep, shared by the workgroup: 16 lanes per query row, 8 features per lane (32 rows
+  // per pass, 8 passes, in two batches whose loads all go out before their arithmetic).  Each
+  // row is RMS-normed, rotated at its position and scaled into log2 units, then stored as bf16 in
+  // the staging area; rows past the end are stored as zeros ----
+  {
+    const int grp = tid >> 4, c = tid & 15;
+    const uint16_t* qw = (const uint16_t*)a.qw;
+    const int P = a.R >> 4;
+    const int halfp = a.R >> 1;
+    const bool rot = 8 * c < a.R;
+    const bool first = 8 * c < halfp;
+    const int p0 = ROT == 1 ? (!rot ? 0 : (first ? 8 * c : 8 * c - halfp)) : (rot ? 4 * c : 0);
+    const float qscale = a.scale * kLog2e;
+    float wv[8];
+    if (NORM) unpack8(ld16(qw + 8 * c), wv);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      u32x4 xw[4];
+      int32_t pw[4];
+      bool vw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t f = f0 + 32 * (4 * hb + j) + grp;
+        vw[j] = f < nrows;
+        const int ri = vw[j] ? (int)(f / G) : 0;
+        const int rh = g * G + (vw[j] ? (int)(f % G) : 0);
+        xw[j] = ld16((const uint16_t*)a.q + (int64_t)b * a.q_b + (int64_t)ri * a.q_i +
+                     (int64_t)rh * a.q_h + 8 * c);
+        pw[j] = qpos_b[ri];
+      }
+      f32x4 tc[4][2], ts[4][2];
+      if (ROT) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t tp = min<int64_t>(max<int64_t>(pw[j], 0), a.table_len - 1);
+          const float* cr = a.cos_t + tp * halfp + p0;
+          const float* sr = a.sin_t + tp * halfp + p0;
+          tc[j][0] = *(const f32x4*)cr;
+          ts[j][0] = *(const f32x4*)sr;
+          if (ROT == 1) {
+            tc[j][1] = *(const f32x4*)(cr + 4);
+            ts[j][1] = *(const f32x4*)(sr + 4);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float x[8];
+        unpack8(xw[j], x);
+        if (NORM) {
+          float ss = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+          ss += __shfl_xor(ss, 1, 64);
+          ss += __shfl_xor(ss, 2, 64);
+          ss += __shfl_xor(ss, 4, 64);
+          ss += __shfl_xor(ss, 8, 64);
+          const float rs = rsqrtf(ss * (1.0f / HD) + a.eps);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] *= rs * wv[e];
+        }
+        if (ROT == 1) {
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = __shfl_xor(x[e], P, 64);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float cs = tc[j][e >> 2][e & 3], sn = ts[j][e >> 2][e & 3];
+            const float r = first ? (x[e] * cs - y[e] * sn) : (y[e] * sn + x[e] * cs);
+            x[e] = rot ? r : x[e];
+          }
+        } else if (ROT == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float cs = tc[j][0][e], sn = ts[j][0][e];
+            const float u = x[2 * e], v = x[2 * e + 1];
+            x[2 * e] = rot ? u * cs - v * sn : u;
+            x[2 * e + 1] = rot ? u * sn + v * cs : v;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = vw[j] ? x[e] * qscale : 0.f;
+        const int row = 32 * (4 * hb + j) + grp;  // 0 .. 255
+        const int rr = row & 63;
+        *(u32x4*)(qstage(row >> 6) + rr * HD + ((c ^ (rr & 15)) << 3)) = pack8(x);
+      }
+    }
+  }
+  __syncthreads();  // staging complete
+  bf16x8 qop[8];  // read from the staging area just before the loop
+
+  // ---- band: first key past the newest query, first key inside the oldest query's window ----
+  // (a guess is right when the key before it is below the target and the key at it is not; if
+  // positions are not consecutive the wavefront searches)
+  const bool ok_hi = (g_hi == 0 || (int64_t)hi_l < x_hi) && (g_hi == a.S || (int64_t)hi_r >= x_hi);
+  const bool ok_lo = (g_lo == 0 || (int64_t)lo_l < x_lo) && (g_lo == a.S || (int64_t)lo_r >= x_lo);
+  int j_hi = ok_hi ? g_hi : wave_lower_bound(kpos_b, a.S, x_hi);
+  int j_lo = a.window == 0 ? 0 : ok_lo ? g_lo : wave_lower_bound(kpos_b, a.S, x_lo);
   j_lo = min(j_lo, j_hi);
   const int n_tiles = (j_hi - j_lo + BN - 1) / BN;
 
@@ -402,6 +451,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  // Running max m (log2 units; kNegBig until the row has seen an allowed key) and sum.  Scores
+  // are kept relative to m_eff = (m set ? m : 0): the S^T accumulators start at -m_eff, so the
+  // MFMAs deliver s - m_eff directly.  (Soft-capping needs the raw score: there they start at 0
+  // and m_eff is subtracted after the cap.)
   float m = kNegBig, lsum = 0.f;
   const float cap2 = a.softcap * kLog2e;
   const float inv_cap2 = CAP ? 1.0f / cap2 : 0.f;
@@ -425,125 +478,162 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
       voff[h2][db] = row * HD + (((col >> 3) ^ vswz(row)) << 3) + (col & 7);
     }
   }
-  // mask bounds in int32: allowed <=> qlo32 <= key position <= qp32
+  // mask bounds in int32: allowed <=> qlo32 <= key position <= qp32 (key positions past the last
+  // key read INT32_MAX, so the ragged tail fails the first test)
   const int32_t qp32 = qvalid ? (int32_t)qp : INT32_MIN;
   const int32_t qlo32 = !qvalid ? INT32_MAX
                         : a.window > 0 ? (int32_t)max<int64_t>(qp - a.window + 1, INT32_MIN)
                                        : INT32_MIN;
 
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  // One tile: prefetch the next tile into the other buffer, compute this one, then wait for the
-  // prefetch and synchronise.
-  auto tile = [&](int t, auto bufc) {
+  // S^T - m_eff for the 32 keys of half kb of a buffered tile
+  auto qk = [&](auto bufc, auto kbc) {
     constexpr int buf = decltype(bufc)::value;
-    const int jt = j_lo + t * BN;
-    if (t + 1 < n_tiles) issue_tile(jt + BN, std::integral_constant<int, buf ^ 1>());
-    const int32_t kfirst = pbuf<buf>()[0];
-    const int32_t klast = pbuf<buf>()[BN - 1];
-    const bool full = (jt + BN <= j_hi) && ((int64_t)klast <= qmin) &&
-                      (a.window == 0 || qmax - (int64_t)kfirst <= a.window - 1);
-    const uint16_t* ks = kbuf<buf>();
-    const uint16_t* vs = vbuf<buf>();
-
-    // K operands of the first 32-key half
+    constexpr int kb = decltype(kbc)::value;
+    const uint16_t* ks = kbuf<buf>() + kb * 32 * HD;
     u32x4 kop[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) kop[s] = *(const u32x4*)(ks + koff[s]);
-
+    for (int st = 0; st < 8; ++st) kop[st] = *(const u32x4*)(ks + koff[st]);
+    const float init = (CAP || m == kNegBig) ? 0.f : -m;
+    f32x16 acc;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // ---- S^T = K Q^T for 32 keys ----
-      f32x16 sacc;
+    for (int r = 0; r < 16; ++r) acc[r] = init;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[s]), qop[s], sacc, 0, 0, 0);
-      // V^T operands of this half, and the next half's K operands, in flight during the softmax
-      i16x4 vlo[2][4], vhi[2][4];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int base = (kb * 32 + 16 * u) * HD;
-          vlo[u][db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vs + base + voff[0][db]));
-          vhi[u][db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vs + base + voff[1][db]));
-        }
-      if (kb == 0) {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) kop[s] = *(const u32x4*)(ks + 32 * HD + koff[s]);
-      }
-
-      // ---- soft-cap and mask ----
-      if (CAP) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = sacc[r] * inv_cap2;
-          const float e = fast_exp2(-2.0f * kLog2e * fabsf(x));
-          sacc[r] = copysignf(cap2 * (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e), x);
-        }
-      }
-      if (!full) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = kb * 32 + 8 * (r >> 2) + 4 * hg + (r & 3);
-          const int32_t kp = pbuf<buf>()[kk];
-          const bool ok = (jt + kk < j_hi) && kp <= qp32 && kp >= qlo32;
-          if (!ok) sacc[r] = -INFINITY;
-        }
-      }
-
-      // ---- online softmax (row = this lane's query; the other 16 keys live in lane ^ 32) ----
-      float mt = sacc[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
-      mt = fmaxf(mt, swap_halves(mt));
-      if (__ballot(mt > m + kRescaleThreshold) != 0) {
-        const float m_new = fmaxf(m, mt);
-        const float alpha = fast_exp2(m - m_new);
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-        m = m_new;
-      }
-      bf16x8 pb[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(sacc[8 * u + e] - m);
-          lsum += p[e];
-        }
-        pb[u] = as_bf16x8(pack8(p));
-      }
-
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const i16x8 va = {vlo[u][db][0], vlo[u][db][1], vlo[u][db][2], vlo[u][db][3],
-                            vhi[u][db][0], vhi[u][db][1], vhi[u][db][2], vhi[u][db][3]};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pb[u],
-                                                          o[db], 0, 0, 0);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    for (int st = 0; st < 8; ++st)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[st]), qop[st], acc, 0, 0, 0);
+    return acc;
   };
 
-  if (a.window > 0 && n_tiles > 0) issue_tile(j_lo, B0());
+  // One step = one 32-key half of a tile, software-pipelined: the step's own S^T was computed by
+  // the previous step; here the mask and running max come first, then the NEXT step's S^T MFMAs
+  // are issued, then this step's exponentials and P V.  In program order the next S^T MFMAs
+  // therefore sit beside this step's exponentials, and this step's P V MFMAs beside the next
+  // step's mask and max, so the matrix unit and the vector ALU work at the same time.
+  // Tiles live in NBUF = 3 buffers: the barrier before the first S^T of tile t+1 (issued during
+  // the second half of tile t) waits for tile t+1's loads, and once every wavefront is past it the
+  // buffer of tile t-1 is free for tile t+2's loads.
+  const int nsteps = 2 * n_tiles;
+  f32x16 s_cur;
+  auto step = [&](int s, auto phc) {
+    constexpr int PH = decltype(phc)::value;  // position in the 6-step buffer cycle
+    constexpr int buf = PH >> 1;
+    constexpr int kb = PH & 1;
+    constexpr int nbuf = kb ? (buf + 1) % NBUF : buf;
+    constexpr int nkb = kb ^ 1;
+    const int t = s >> 1;
+    const int jt = j_lo + t * BN;
+    const int32_t* kpt = pbuf<buf>();
+    const int32_t kfirst = kpt[0];
+    const int32_t klast = kpt[BN - 1];
+    const bool full = (jt + BN <= j_hi) && ((int64_t)klast <= qmin) &&
+                      (a.window == 0 || qmax - (int64_t)kfirst <= a.window - 1);
+    f32x16 sc = s_cur;
+
+    // ---- soft-cap, mask, running max ----
+    const bool unset = m == kNegBig;
+    if (CAP) {
+      const float meff = unset ? 0.f : m;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = sc[r] * inv_cap2;
+        const float e = fast_exp2(-2.0f * kLog2e * fabsf(x));
+        sc[r] = copysignf(cap2 * (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e), x) - meff;
+      }
+    }
+    if (!full) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int32_t kp = kpt[kb * 32 + 8 * (r >> 2) + 4 * hg + (r & 3)];
+        if (!(kp <= qp32 && kp >= qlo32)) sc[r] = -INFINITY;
+      }
+    }
+    float mt = sc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+    mt = fmaxf(mt, swap_halves(mt));
+    // lazy rescale: the reference moves only when a score exceeds it by more than the threshold
+    // (or on the row's first allowed key)
+    const bool upd = unset ? (mt > -INFINITY) : (mt > kRescaleThreshold);
+    if (__ballot(upd) != 0) {
+      const float delta = unset ? (mt > -INFINITY ? mt : 0.f) : fmaxf(mt, 0.f);
+      const float alpha = unset ? 1.f : fast_exp2(-delta);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m = unset ? (mt > -INFINITY ? mt : kNegBig) : m + delta;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] -= delta;
+    }
+
+    // ---- the next step's S^T (first crossing into the next tile when kb == 1) ----
+    if (kb == 1 && s + 1 < nsteps) {
+      __builtin_amdgcn_s_waitcnt(0);
+      commit_kpos(std::integral_constant<int, nbuf>());
+      __syncthreads();
+      if (t + 2 < n_tiles) issue_tile(jt + 2 * BN, std::integral_constant<int, (buf + 2) % NBUF>());
+    }
+    // Issued unconditionally so that it shares one basic block with the exponentials and P V
+    // below (the scheduler interleaves only within a block); after the last step it reads a
+    // stale buffer and its result is unused.
+    s_cur = qk(std::integral_constant<int, nbuf>(), std::integral_constant<int, nkb>());
+
+    // ---- P = exp2(s - m), row sums ----
+    bf16x8 pb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(sc[8 * u + e]);
+        lsum += p[e];
+      }
+      pb[u] = as_bf16x8(pack8(p));
+    }
+
+    // ---- O^T += V^T P^T ----
+    const uint16_t* vs = vbuf<buf>();
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int base = (kb * 32 + 16 * u) * HD;
+        const i16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vs + base + voff[0][db]));
+        const i16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vs + base + voff[1][db]));
+        const i16x8 va = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pb[u],
+                                                        o[db], 0, 0, 0);
+      }
+  };
+
+  if (a.window > 0 && n_tiles > 0) issue_tile(j_lo, std::integral_constant<int, 0>());
+  // this lane's query operands from the staging rows (chunk 2s + hg of row 32w + ql)
+  {
+    const int rr = ((w & 1) << 5) + ql;
+    const uint16_t* st = qstage(w >> 1) + rr * HD;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qop[s] = as_bf16x8(*(const u32x4*)(st + (((2 * s + hg) ^ (rr & 15)) << 3)));
+  }
   __builtin_amdgcn_s_waitcnt(0);  // also retires the early first-tile loads when n_tiles == 0
-  __syncthreads();
-  for (int t = 0; t < n_tiles; t += 2) {
-    tile(t, B0());
-    if (t + 1 < n_tiles) tile(t + 1, B1());
+  commit_kpos(std::integral_constant<int, 0>());
+  __syncthreads();  // staging read by every wave: buffer 1 is free for tile 1
+  if (n_tiles > 1) issue_tile(j_lo + BN, std::integral_constant<int, 1>());
+  if (nsteps > 0) s_cur = qk(std::integral_constant<int, 0>(), std::integral_constant<int, 0>());
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+  using P4 = std::integral_constant<int, 4>;
+  using P5 = std::integral_constant<int, 5>;
+  for (int s = 0; s < nsteps; s += 6) {
+    step(s, P0());
+    if (s + 1 < nsteps) step(s + 1, P1());
+    if (s + 2 < nsteps) step(s + 2, P2());
+    if (s + 3 < nsteps) step(s + 3, P3());
+    if (s + 4 < nsteps) step(s + 4, P4());
+    if (s + 5 < nsteps) step(s + 5, P5());
   }
 
   const float ltot = lsum + swap_halves(lsum);
@@ -635,7 +725,6 @@ bool prefill_stream_supported(const AttnArgs& a) {
 
 hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t stream) {
   if (a.B == 0 || a.L == 0) return hipSuccess;
-  const int rot = a.R == 0 ? 0 : (a.style == 0 ? 1 : 2);
   StreamArgs sa;
   sa.a = a;
   sa.kprep = nullptr;
@@ -649,7 +738,7 @@ hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t
     if (e != hipSuccess) return e;
     sa.kprep = po.p;
   }
-  switch (rot) {
+  switch (a.R == 0 ? 0 : (a.style == 0 ? 1 : 2)) {
     case 0: return launch_attn_norm<0>(sa, stream);
     case 1: return launch_attn_norm<1>(sa, stream);
     default: return launch_attn_norm<2>(sa, stream);
