@@ -330,7 +330,9 @@ def main(argv=None):
         log(f"[bench] decode {dms:.3f} ms -> {gbs:.0f} GB/s")
         dec = {"workload": dwl.name, "value": round(gbs, 1), "unit": "GB/s",
                "ms_per_call": round(dms, 4), "algorithmic_bytes": nbytes,
-               "roofline": {"bound": "hbm", "kernel": "decode_split_kernel + decode_combine_kernel",
+               "roofline": {"bound": "hbm",
+                            "kernel": "decode_prep_q_kernel + decode_split_kernel + "
+                                      "decode_combine_kernel (one gqa_attn_decode call)",
                             "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(gbs / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic("decode_split_kernel"),
