@@ -293,24 +293,32 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   bool kp_pend_ok = false;
   // Tile loader: wave w, round i fills LDS rows 4*(w + 8i) .. +3 (1 KB); lane -> row 4(w+8i) +
   // lane/16, LDS chunk lane%16, which holds source chunk (lane%16) ^ (row & 15).
+  // Lane constants of the tile loader (offset of the lane's 16 bytes within a tile); a tile adds
+  // jt rows.  Rows at or past S fall outside the descriptors' ranges and read as zero.
+  int lk[2], lv[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 4 * (w + 8 * i) + (lane >> 4);
+    lk[i] = r * row_bytes + (((lane & 15) ^ kswz(r)) << 4);
+    lv[i] = r * row_bytes + (((lane & 15) ^ vswz(r)) << 4);
+  }
   auto issue_tile = [&](int jt, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
+    const int tb = jt * row_bytes;         // cached keys and values: rows from 0
+    const int wb = (jt - nc) * row_bytes;  // prepared keys: rows from nc
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int r = 4 * (w + 8 * i) + (lane >> 4);
-      const int j = jt + r;
-      const int csrc = (lane & 15) ^ kswz(r);
-      const int vsrc = (lane & 15) ^ vswz(r);
       lds_void* kdst = (lds_void*)(kbuf<buf>() + 4 * (w + 8 * i) * HD);
       lds_void* vdst = (lds_void*)(vbuf<buf>() + 4 * (w + 8 * i) * HD);
-      const int vo = j * row_bytes + vsrc * 16;
-      const int ko = j * row_bytes + csrc * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vdst, 16, j < a.S ? vo : 0x7fffffff, 0, 0, 0);
-      if (j < nc) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, ko, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vdst, 16, lv[i] + tb, 0, 0, 0);
+      if (jt + BN <= nc) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, lk[i] + tb, 0, 0, 0);
+      } else if (jt >= nc) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, kdst, 16, lk[i] + wb, 0, 0, 0);
+      } else if (jt + 4 * (w + 8 * i) + (lane >> 4) < nc) {  // a tile straddling nc
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, lk[i] + tb, 0, 0, 0);
       } else {
-        const int wo = (j - nc) * row_bytes + csrc * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, kdst, 16, j < a.S ? wo : 0x7fffffff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, kdst, 16, lk[i] + wb, 0, 0, 0);
       }
     }
     // key positions of the tile: loaded by wave 0 into a register and written to LDS by
@@ -493,10 +501,12 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     u32x4 kop[8];
 #pragma unroll
     for (int st = 0; st < 8; ++st) kop[st] = *(const u32x4*)(ks + koff[st]);
+    // all eight operand reads in flight before the first MFMA waits on one
+    __builtin_amdgcn_sched_barrier(0);
     const float init = (CAP || m == kNegBig) ? 0.f : -m;
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = init;
+    const uint64_t init2 = ((uint64_t)__float_as_uint(init) << 32) | __float_as_uint(init);
+    const u64x8 seed = {init2, init2, init2, init2, init2, init2, init2, init2};
+    f32x16 acc = __builtin_bit_cast(f32x16, seed);
 #pragma unroll
     for (int st = 0; st < 8; ++st)
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[st]), qop[st], acc, 0, 0, 0);
@@ -578,17 +588,24 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     // stale buffer and its result is unused.
     s_cur = qk(std::integral_constant<int, nbuf>(), std::integral_constant<int, nkb>());
 
-    // ---- P = exp2(s - m), row sums ----
+    // ---- P = exp2(s - m); row sums of the bf16 weights the P V product uses, two per
+    // v_dot2_f32_bf16 against (1, 1) ----
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
     bf16x8 pb[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = fast_exp2(sc[8 * u + e]);
-        lsum += p[e];
-      }
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(sc[8 * u + e]);
       pb[u] = as_bf16x8(pack8(p));
+      // (each pair is built from its two floats: taking it out of the packed vector with a bit
+      // cast made the compiler feed the first pair to all four dot products)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {(__bf16)p[2 * e], (__bf16)p[2 * e + 1]};
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, lsum, false);
+      }
     }
 
     // ---- O^T += V^T P^T ----
