@@ -17,7 +17,9 @@ All arithmetic is numpy float64 on the exact values the GPU receives (inputs alr
 run dtype), with library matmul / exp / tanh / sin / cos as the only primitives.
 
 Pins (tests/test_oracle_pins.py, all CPU): the page's worked RoPE wavelength; position-squeezing
-of linear scaling; llama3 per-band behaviour; complex-multiplication form of the rotation; the
+of linear scaling; llama3 per-band behaviour; YaRN's rotation-count split, ramp monotonicity,
+reduction to plain RoPE at factor 1 and its sharpening values; LongRoPE's reduction to plain and
+linear RoPE and its short/long switch; the attention factor on the table norm; complex-multiplication form of the rotation; the
 half-split pairing of the study guide; deinterleave equivalence; norm preservation; relative
 position; RMS of the normed vector; soft-cap limits; integer mask probe; window and GQA
 equivalences; decode == last prefill row; chunked prefill == tail of full prefill; brute-force
@@ -30,7 +32,7 @@ import math
 
 import numpy as np
 
-ROPE_KINDS = ("default", "linear", "llama3")
+ROPE_KINDS = ("default", "linear", "llama3", "yarn", "longrope")
 ROT_STYLES = ("half", "interleaved")
 
 
@@ -38,7 +40,9 @@ ROT_STYLES = ("half", "interleaved")
 # Rotary frequencies and angles
 # ----------------------------------------------------------------------------------------------
 def rope_inv_freq(rotary_dim, theta, kind="default", factor=1.0, low_freq_factor=1.0,
-                  high_freq_factor=4.0, original_max_position_embeddings=8192.0):
+                  high_freq_factor=4.0, original_max_position_embeddings=8192.0, *,
+                  beta_fast=None, beta_slow=None, truncate=True, short_factor=None,
+                  long_factor=None, seq_len=None):
     """Rotation frequency of each of the rotary_dim/2 feature pairs.
 
     [Models] "Scaled RoPE": pair i turns by p * theta^(-2i/d) at position p; d here is the
@@ -50,7 +54,18 @@ def rope_inv_freq(rotary_dim, theta, kind="default", factor=1.0, low_freq_factor
                than original/low_freq_factor are divided by factor, and in between the two are
                blended linearly with weight s = (original/wavelength - low)/(high - low) on the
                kept value.
-    The attention factor that multiplies cos and sin is 1 for all three kinds.
+      yarn:    the same split chosen by counting rotations over the original context: pairs
+               that turn more than beta_fast (default 32) times keep their frequency, pairs that
+               turn fewer than beta_slow (default 1) times are divided by factor, with a linear
+               ramp over the pair index between the two (ends rounded outwards unless
+               truncate is false).  The pair index that turns r times over the original context
+               solves original * theta^(-2x/d) = 2*pi*r for x.
+      longrope ([Ster] "Overview", [Ster] phimoe paragraph): per-pair factors, the short table
+               while the sequence is within original_max_position_embeddings and the long one
+               once it goes past; frequency i is divided by the table's entry i.  Reading: the
+               sequence length that decides is seq_len (positions 0 .. seq_len-1).
+    The attention factor that multiplies cos and sin is rope_attention_factor(); it is 1 for the
+    first three kinds.
     """
     if rotary_dim < 0 or rotary_dim % 2:
         raise ValueError(f"rotary_dim must be even and >= 0, got {rotary_dim}")
@@ -58,6 +73,32 @@ def rope_inv_freq(rotary_dim, theta, kind="default", factor=1.0, low_freq_factor
         raise ValueError(f"RoPE type {kind!r} is not implemented")
     half = rotary_dim // 2
     out = np.empty(half, dtype=np.float64)
+    if kind == "yarn":
+        old = float(original_max_position_embeddings)
+
+        def pair_turning(rotations):
+            return rotary_dim * math.log(old / (rotations * 2.0 * math.pi)) / (2.0 * math.log(theta))
+
+        lo = pair_turning(float(beta_fast or 32.0))
+        hi = pair_turning(float(beta_slow or 1.0))
+        if truncate:
+            lo, hi = math.floor(lo), math.ceil(hi)
+        lo, hi = max(lo, 0), min(hi, rotary_dim - 1)
+        width = (hi - lo) or 0.001
+        for i in range(half):
+            base = float(theta) ** (-2.0 * i / rotary_dim)
+            interp = min(max((i - lo) / width, 0.0), 1.0)   # 0: kept, 1: divided by factor
+            out[i] = base / factor * interp + base * (1.0 - interp)
+        return out
+    if kind == "longrope":
+        old = float(original_max_position_embeddings)
+        table = long_factor if (seq_len is not None and seq_len > old) else short_factor
+        table = np.asarray(table, np.float64)
+        if table.shape != (half,):
+            raise ValueError(f"longrope factor tables must have {half} entries")
+        for i in range(half):
+            out[i] = float(theta) ** (-2.0 * i / rotary_dim) / table[i]
+        return out
     for i in range(half):
         base = float(theta) ** (-2.0 * i / rotary_dim)
         if kind == "default":
@@ -79,6 +120,41 @@ def rope_inv_freq(rotary_dim, theta, kind="default", factor=1.0, low_freq_factor
     return out
 
 
+def _mscale(scale, m=1.0):
+    # [Models] "Scaled RoPE": the sharpening 0.1 * m * ln(s) + 1, and 1 for s <= 1
+    return 1.0 if scale <= 1 else 0.1 * m * math.log(scale) + 1.0
+
+
+def rope_attention_factor(kind="default", factor=1.0, *, mscale=None, mscale_all_dim=None,
+                          attention_factor=None):
+    """Factor multiplying cos and sin ([Models] "Scaled RoPE", rope_inv_freq and rope_tables).
+
+    yarn: the given attention_factor, else mscale(factor, mscale) / mscale(factor, mscale_all_dim)
+    when both are given and nonzero, else mscale(factor) = 0.1 ln(factor) + 1 (1 for factor <= 1).
+    longrope: [Ster] scales both tables by "the attention factor" without a formula; reading: the
+    given attention_factor, 1 when absent.  Other kinds: 1."""
+    if kind == "yarn":
+        if attention_factor is not None:
+            return float(attention_factor)
+        if mscale and mscale_all_dim:
+            return _mscale(factor, mscale) / _mscale(factor, mscale_all_dim)
+        return _mscale(factor)
+    if kind == "longrope":
+        return 1.0 if attention_factor is None else float(attention_factor)
+    return 1.0
+
+
+def yarn_softmax_scale(qk_dim, factor, mscale_all_dim=None):
+    """Softmax scale with YaRN's temperature ([Models] "Multi-head latent attention": DeepSeek
+    applies it to the scale): qk_dim^-0.5 times m^2, m = 0.1 * mscale_all_dim * ln(factor) + 1
+    when mscale_all_dim is given and factor > 1, else m = 1."""
+    sc = float(qk_dim) ** -0.5
+    if mscale_all_dim:
+        m = 0.1 * mscale_all_dim * math.log(factor) + 1.0 if factor > 1 else 1.0
+        sc *= m * m
+    return sc
+
+
 def rope_angles(positions, inv_freq):
     """Angle of pair i at position p: p * inv_freq[i] ([Models] "Scaled RoPE", rope_tables;
     [Guide] §4 Rotary).  Returns positions.shape + (len(inv_freq),)."""
@@ -98,12 +174,13 @@ def rms_norm(x, weight, eps):
     return x / np.sqrt(ms + eps) * np.asarray(weight, dtype=np.float64)
 
 
-def rotate(x, positions, inv_freq, style="half"):
+def rotate(x, positions, inv_freq, style="half", attention_factor=1.0):
     """Rotate the first R = 2*len(inv_freq) features of each row of x by its position.
 
     half:        pair (i, i + R/2)      ([Guide] §4 Rotary: feature i with feature i + hd/2)
     interleaved: pair (2i, 2i + 1)      ([Models] "Serving it": adjacent pairs; [Ster] "Overview")
-    Each pair (a, b) at angle t becomes (a cos t - b sin t, a sin t + b cos t).  Features at
+    Each pair (a, b) at angle t becomes (a cos t - b sin t, a sin t + b cos t), with cos and sin
+    multiplied by the attention factor ([Models] "Scaled RoPE", rope_tables).  Features at
     index >= R pass through unchanged ([Ster] "Overview": only that share rotates).
     positions must broadcast to x.shape[:-1]."""
     x = np.asarray(x, dtype=np.float64)
@@ -115,7 +192,7 @@ def rotate(x, positions, inv_freq, style="half"):
     if R > x.shape[-1]:
         raise ValueError("rotary width exceeds head_dim")
     ang = rope_angles(np.broadcast_to(positions, x.shape[:-1]), inv_freq)
-    c, s = np.cos(ang), np.sin(ang)
+    c, s = attention_factor * np.cos(ang), attention_factor * np.sin(ang)
     if style == "half":
         a, b = x[..., :half], x[..., half:R]
         out[..., :half] = a * c - b * s
@@ -182,7 +259,7 @@ def _scale(head_dim, scale):
 
 def attn_prefill(q, k, v, positions, key_positions, *, inv_freq, style="half", n_cached=0,
                  window=0, q_norm_w=None, k_norm_w=None, eps=1e-6, scale=0.0, softcap=0.0,
-                 query_rows=None, heads=None, batches=None):
+                 query_rows=None, heads=None, batches=None, attention_factor=1.0):
     """Causal prefill of one layer: [Models] "What differs" (DecoderAttention.forward).
 
     q [B, L, Hq, D], k and v [B, S, Hkv, D], positions [B, L], key_positions [B, S].
@@ -213,12 +290,12 @@ def attn_prefill(q, k, v, positions, key_positions, *, inv_freq, style="half", n
         kb = k[b].copy()                                  # [S, Hkv, D]
         if q_norm_w is not None:
             qb = rms_norm(qb, q_norm_w, eps)
-        qb = rotate(qb, positions[b, rows][:, None], inv_freq, style)
+        qb = rotate(qb, positions[b, rows][:, None], inv_freq, style, attention_factor)
         new = slice(n_cached, S)
         kn = kb[new]
         if k_norm_w is not None:
             kn = rms_norm(kn, k_norm_w, eps)
-        kb[new] = rotate(kn, key_positions[b, new][:, None], inv_freq, style)
+        kb[new] = rotate(kn, key_positions[b, new][:, None], inv_freq, style, attention_factor)
         allowed = allowed_mask(positions[b, rows], key_positions[b], window)
         for hi, h in enumerate(heads):
             g = h // G
@@ -227,7 +304,7 @@ def attn_prefill(q, k, v, positions, key_positions, *, inv_freq, style="half", n
 
 
 def attn_decode_one(q, k, v, n, *, inv_freq, style="half", window=0, q_norm_w=None, eps=1e-6,
-                    scale=0.0, softcap=0.0, heads=None):
+                    scale=0.0, softcap=0.0, heads=None, attention_factor=1.0):
     """Single-token decode of one sequence against its cache ([Guide] §3.3 KVCache, §3.7).
 
     q [Hq, D]; k, v [Hkv, >= n, D] hold the sequence's cache rows, slot j at position j, already
@@ -241,7 +318,7 @@ def attn_decode_one(q, k, v, n, *, inv_freq, style="half", window=0, q_norm_w=No
     heads = range(Hq) if heads is None else heads
     pos = n - 1
     qq = q if q_norm_w is None else rms_norm(q, q_norm_w, eps)
-    qq = rotate(qq, np.full(Hq, pos), inv_freq, style)
+    qq = rotate(qq, np.full(Hq, pos), inv_freq, style, attention_factor)
     allowed = allowed_mask([pos], np.arange(n), window)
     sc = _scale(D, scale)
     out = np.zeros((len(heads), D), dtype=np.float64)

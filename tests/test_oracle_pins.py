@@ -103,9 +103,115 @@ def test_llama3_is_continuous_at_band_edges():
             assert f[1] == pytest.approx(f0[1], rel=1e-7)
 
 
+def _rotations_over(old, inv_freq):
+    # full turns a pair makes over the original context: old * frequency / (2 pi)
+    return old * np.asarray(inv_freq) / (2 * math.pi)
+
+
+@pytest.mark.parametrize("d,theta,old,factor", [(128, 1e4, 4096, 4.0), (128, 1e6, 32768, 4.0),
+                                                (64, 5e5, 8192, 16.0)])
+def test_yarn_split_follows_rotation_counts(d, theta, old, factor):
+    # [Models] Scaled RoPE: YaRN keeps pairs that turn more than beta_fast (32) times over the
+    # original context, interpolates pairs that turn fewer than beta_slow (1) times, and ramps
+    # linearly in between.  The turn counts here come from the plain frequencies, not from the
+    # oracle's ramp; rounding the ramp ends outwards keeps these two sets exact.
+    base = oracle.rope_inv_freq(d, theta)
+    f = oracle.rope_inv_freq(d, theta, "yarn", factor, original_max_position_embeddings=old)
+    turns = _rotations_over(old, base)
+    fast, slow = turns >= 32, turns <= 1
+    assert fast.any() and slow.any()
+    np.testing.assert_array_equal(f[fast], base[fast])
+    np.testing.assert_allclose(f[slow], base[slow] / factor, rtol=1e-15)
+    ratio = f / base
+    assert np.all(ratio <= 1 + 1e-15) and np.all(ratio >= 1 / factor - 1e-15)
+    assert np.all(np.diff(ratio) <= 1e-15)                 # never rises from fast to slow pairs
+    mid = ~fast & ~slow
+    assert np.all(ratio[mid][1:-1] < 1) and np.all(ratio[mid][1:-1] > 1 / factor)
+    # other beta thresholds move the split accordingly
+    f2 = oracle.rope_inv_freq(d, theta, "yarn", factor, original_max_position_embeddings=old,
+                              beta_fast=8, beta_slow=2)
+    np.testing.assert_array_equal(f2[turns >= 8], base[turns >= 8])
+    np.testing.assert_allclose(f2[turns <= 2], base[turns <= 2] / factor, rtol=1e-15)
+
+
+def test_yarn_truncate_only_widens_the_ramp_ends():
+    # truncate=False keeps the continuous ramp ends; the rounded ends can only widen the kept and
+    # the interpolated sets, so each frequency moves toward the nearer end
+    base = oracle.rope_inv_freq(128, 1e4)
+    t = oracle.rope_inv_freq(128, 1e4, "yarn", 4.0, original_max_position_embeddings=4096)
+    c = oracle.rope_inv_freq(128, 1e4, "yarn", 4.0, original_max_position_embeddings=4096,
+                             truncate=False)
+    turns = _rotations_over(4096, base)
+    np.testing.assert_array_equal(c[turns >= 32], base[turns >= 32])
+    np.testing.assert_allclose(c[turns <= 1], base[turns <= 1] / 4, rtol=1e-15)
+    assert not np.array_equal(t, c)
+
+
+def test_yarn_and_longrope_reduce_to_plain_rope():
+    base = oracle.rope_inv_freq(128, 1e6)
+    np.testing.assert_allclose(
+        oracle.rope_inv_freq(128, 1e6, "yarn", 1.0, original_max_position_embeddings=8192), base,
+        rtol=1e-15)
+    assert oracle.rope_attention_factor("yarn", 1.0) == 1.0
+    ones = np.ones(64)
+    np.testing.assert_allclose(
+        oracle.rope_inv_freq(128, 1e6, "longrope", original_max_position_embeddings=4096,
+                             short_factor=ones, long_factor=ones * 3, seq_len=100), base, rtol=0)
+    # all long factors equal to s: linear scaling by s once the sequence passes the original
+    np.testing.assert_allclose(
+        oracle.rope_inv_freq(128, 1e6, "longrope", original_max_position_embeddings=4096,
+                             short_factor=ones, long_factor=ones * 3, seq_len=4097),
+        oracle.rope_inv_freq(128, 1e6, "linear", 3.0), rtol=1e-15)
+
+
+def test_longrope_switches_past_the_original_context():
+    # [Ster] Overview: short factors while the sequence is within original_max_position_embeddings,
+    # long ones once it goes past
+    short, long_ = np.linspace(1, 2, 32), np.linspace(1, 8, 32)
+    kw = dict(original_max_position_embeddings=4096, short_factor=short, long_factor=long_)
+    base = oracle.rope_inv_freq(64, 1e4)
+    np.testing.assert_allclose(oracle.rope_inv_freq(64, 1e4, "longrope", seq_len=4096, **kw),
+                               base / short, rtol=1e-15)
+    np.testing.assert_allclose(oracle.rope_inv_freq(64, 1e4, "longrope", seq_len=4097, **kw),
+                               base / long_, rtol=1e-15)
+
+
+def test_yarn_sharpening_values():
+    # [Models] Scaled RoPE: cos and sin multiplied by 0.1 ln s + 1; with both mscale and
+    # mscale_all_dim given (DeepSeek) the factor is their ratio, which is 1 when they are equal;
+    # a stated attention_factor is used as is.  Checked at s = e^5 (0.1 * 5 + 1 = 1.5).
+    assert oracle.rope_attention_factor("yarn", math.exp(5.0)) == pytest.approx(1.5, rel=1e-15)
+    assert oracle.rope_attention_factor("yarn", 40.0, mscale=1.0, mscale_all_dim=1.0) == 1.0
+    assert oracle.rope_attention_factor("yarn", 40.0, mscale=0.707, mscale_all_dim=0.707) == 1.0
+    assert oracle.rope_attention_factor("yarn", 40.0, attention_factor=1.25) == 1.25
+    assert oracle.rope_attention_factor("longrope", 8.0) == 1.0
+    assert oracle.rope_attention_factor("llama3", 8.0) == 1.0
+    # temperature on the softmax scale ([Models] MLA): 1/sqrt(qk) times m^2 with
+    # m = 0.1 * mscale_all_dim * ln(factor) + 1; at factor e^10 and mscale_all_dim 1, m = 2
+    assert oracle.yarn_softmax_scale(192, math.exp(10.0), 1.0) == pytest.approx(4 / math.sqrt(192),
+                                                                              rel=1e-14)
+    assert oracle.yarn_softmax_scale(192, 1.0, 1.0) == 192 ** -0.5
+    assert oracle.yarn_softmax_scale(128, 40.0) == 128 ** -0.5
+
+
+@pytest.mark.parametrize("style", ["half", "interleaved"])
+def test_attention_factor_scales_rotated_norm(style):
+    # cos and sin both multiplied by a: each rotated pair's length is multiplied by a, the
+    # features past the rotary width are untouched
+    x = rng.standard_normal((5, 3, 96))
+    f = oracle.rope_inv_freq(64, 1e4, "yarn", 8.0, original_max_position_embeddings=2048)
+    a = oracle.rope_attention_factor("yarn", 8.0)
+    y = oracle.rotate(x, np.arange(5)[:, None] * 997, f, style, attention_factor=a)
+    np.testing.assert_allclose(np.linalg.norm(y[..., :64], axis=-1),
+                               a * np.linalg.norm(x[..., :64], axis=-1), rtol=1e-12)
+    np.testing.assert_array_equal(y[..., 64:], x[..., 64:])
+
+
 def test_unknown_rope_kind_raises():
     with pytest.raises(ValueError):
         oracle.rope_inv_freq(64, 1e4, "dynamic")
+    with pytest.raises(ValueError):
+        oracle.rope_inv_freq(64, 1e4, "longrope", short_factor=np.ones(3), seq_len=1)
     with pytest.raises(ValueError):
         oracle.rope_inv_freq(63, 1e4)
 
