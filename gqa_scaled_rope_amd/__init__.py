@@ -6,17 +6,19 @@ memory and the current stream.  There is no fallback: if the library is not buil
 raises.
 
 The functions mirror the C entry points: :func:`rope_tables`, :func:`attn_prefill`,
-:func:`attn_decode`, :func:`decode_workspace_bytes`, :func:`rope_inv_freq`, :func:`last_error`.
+:func:`attn_decode`, :func:`decode_workspace_bytes`, :func:`rope_inv_freq`,
+:func:`rope_attention_factor`, :func:`rope_softmax_scale`, :func:`last_error`.
 """
 from __future__ import annotations
 
 import ctypes
 import os
 from dataclasses import dataclass
-from typing import Optional
+from typing import Optional, Sequence
 
 __all__ = [
     "GQAError", "RopeSpec", "AttnConfig", "library", "rope_inv_freq", "rope_tables",
+    "rope_attention_factor", "rope_softmax_scale",
     "attn_prefill", "attn_decode", "decode_workspace_bytes", "prefill_workspace_bytes", "prep_keys", "last_error", "set_kernel_policy",
     "LIB_PATH", "EXPORTS",
 ]
@@ -24,7 +26,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_rope.so")
 
 GQA_F32, GQA_BF16 = 0, 1
-ROPE_KINDS = {"default": 0, "linear": 1, "llama3": 2}
+ROPE_KINDS = {"default": 0, "linear": 1, "llama3": 2, "yarn": 3, "longrope": 4}
 ROT_STYLES = {"half": 0, "interleaved": 1}
 STATUS = {0: "GQA_OK", 1: "GQA_E_NULL", 2: "GQA_E_SHAPE", 3: "GQA_E_DTYPE",
           4: "GQA_E_UNSUPPORTED", 5: "GQA_E_WORKSPACE", 6: "GQA_E_HIP", 7: "GQA_E_VALUE"}
@@ -41,7 +43,12 @@ class _RopeParams(ctypes.Structure):
     _fields_ = [("rotary_dim", ctypes.c_int32), ("kind", ctypes.c_int32),
                 ("theta", ctypes.c_double), ("factor", ctypes.c_double),
                 ("low_freq_factor", ctypes.c_double), ("high_freq_factor", ctypes.c_double),
-                ("original_max_pos", ctypes.c_double)]
+                ("original_max_pos", ctypes.c_double), ("beta_fast", ctypes.c_double),
+                ("beta_slow", ctypes.c_double), ("yarn_no_truncate", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("mscale", ctypes.c_double),
+                ("mscale_all_dim", ctypes.c_double), ("attention_factor", ctypes.c_double),
+                ("short_factor", ctypes.POINTER(ctypes.c_double)),
+                ("long_factor", ctypes.POINTER(ctypes.c_double)), ("seq_len", ctypes.c_int64)]
 
 
 class _AttnCfg(ctypes.Structure):
@@ -61,6 +68,10 @@ _I32, _I64, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 EXPORTS = {
     "gqa_rope_tables": (_I32, [ctypes.POINTER(_RopeParams), _I32, _P, _P, _P]),
     "gqa_rope_inv_freq": (_I32, [ctypes.POINTER(_RopeParams), ctypes.POINTER(ctypes.c_double)]),
+    "gqa_rope_attention_factor": (_I32, [ctypes.POINTER(_RopeParams),
+                                         ctypes.POINTER(ctypes.c_double)]),
+    "gqa_rope_softmax_scale": (_I32, [ctypes.POINTER(_RopeParams), _I32,
+                                      ctypes.POINTER(ctypes.c_double)]),
     "gqa_prep_keys": (_I32, [ctypes.POINTER(_AttnCfg), _P, _P, _I64, _I32, _I32, _I32, _P, _P]),
     "gqa_prefill_workspace_bytes": (_SZ, [ctypes.POINTER(_AttnCfg), _I32, _I32, _I32]),
     "gqa_attn_prefill": (_I32, [ctypes.POINTER(_AttnCfg), _P, _P, _P, _P, _I64, _P, _I64, _I32,
@@ -120,12 +131,41 @@ class RopeSpec:
     low_freq_factor: float = 1.0
     high_freq_factor: float = 4.0
     original_max_pos: float = 8192.0
+    # yarn (None selects the schedule's default or "absent")
+    beta_fast: Optional[float] = None
+    beta_slow: Optional[float] = None
+    truncate: bool = True
+    mscale: Optional[float] = None
+    mscale_all_dim: Optional[float] = None
+    # yarn and longrope
+    attention_factor: Optional[float] = None
+    # longrope: per-pair factor tables (R/2 each) and the sequence length that picks one
+    short_factor: Optional[Sequence[float]] = None
+    long_factor: Optional[Sequence[float]] = None
+    seq_len: int = 0
 
     def c_struct(self):
         if self.kind not in ROPE_KINDS:
             raise GQAError(4, f"RoPE type {self.kind!r} is not implemented")
-        return _RopeParams(self.rotary_dim, ROPE_KINDS[self.kind], self.theta, self.factor,
-                           self.low_freq_factor, self.high_freq_factor, self.original_max_pos)
+
+        def table(v):
+            return None if v is None else (ctypes.c_double * len(v))(*[float(x) for x in v])
+
+        short, long_ = table(self.short_factor), table(self.long_factor)
+        dbl = ctypes.POINTER(ctypes.c_double)
+        st = _RopeParams(
+            self.rotary_dim, ROPE_KINDS[self.kind], self.theta, self.factor,
+            self.low_freq_factor, self.high_freq_factor, self.original_max_pos,
+            self.beta_fast or 0.0, self.beta_slow or 0.0, 0 if self.truncate else 1, 0,
+            self.mscale or 0.0, self.mscale_all_dim or 0.0, self.attention_factor or 0.0,
+            ctypes.cast(short, dbl) if short is not None else dbl(),
+            ctypes.cast(long_, dbl) if long_ is not None else dbl(), int(self.seq_len))
+        half = self.rotary_dim // 2
+        for name, t in (("short_factor", short), ("long_factor", long_)):
+            if t is not None and len(t) != half:
+                raise GQAError(2, f"{name} has {len(t)} entries, expected {half}")
+        st._tables = (short, long_)   # the arrays live as long as the struct
+        return st
 
 
 def rope_inv_freq(spec: RopeSpec):
@@ -134,6 +174,22 @@ def rope_inv_freq(spec: RopeSpec):
     buf = (ctypes.c_double * max(1, spec.rotary_dim // 2))()
     _check(library().gqa_rope_inv_freq(ctypes.byref(st), buf))
     return list(buf)[: spec.rotary_dim // 2]
+
+
+def rope_attention_factor(spec: RopeSpec) -> float:
+    """Factor the cos/sin tables are multiplied by (1 unless yarn or longrope)."""
+    st = spec.c_struct()
+    out = ctypes.c_double()
+    _check(library().gqa_rope_attention_factor(ctypes.byref(st), ctypes.byref(out)))
+    return out.value
+
+
+def rope_softmax_scale(spec: RopeSpec, qk_dim: int) -> float:
+    """qk_dim^-0.5, with YaRN's temperature when the schedule is yarn with mscale_all_dim."""
+    st = spec.c_struct()
+    out = ctypes.c_double()
+    _check(library().gqa_rope_softmax_scale(ctypes.byref(st), int(qk_dim), ctypes.byref(out)))
+    return out.value
 
 
 def _torch():

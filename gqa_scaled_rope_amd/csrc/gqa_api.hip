@@ -1,5 +1,6 @@
 // C-ABI of libgqa_rope: argument validation, the rotary frequency schedule, and kernel dispatch.
 // Declarations and the contract of every entry point are in include/gqa_rope.h.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -35,10 +36,14 @@ gqa_status hip_status(hipError_t e, const char* what) {
 bool finite_nonneg(double x) { return std::isfinite(x) && x >= 0.0; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+bool finite_pos(double x) { return std::isfinite(x) && x > 0.0; }
+
 // Frequencies of the rotated feature pairs ([Models] "Scaled RoPE", rope_inv_freq):
 // base_i = theta^(-2i/R); linear divides by factor; llama3 keeps pairs with wavelength below
 // original/high_freq_factor, divides pairs with wavelength above original/low_freq_factor by
-// factor, and between them blends the two linearly in original/wavelength.
+// factor, and between them blends the two linearly in original/wavelength.  yarn makes the same
+// split by rotation counts over the original context, with a ramp over the pair index; longrope
+// ([Ster] "Overview") divides by a per-pair table chosen by the sequence length.
 gqa_status check_rope(const gqa_rope_params* rp) {
   if (!rp) return fail(GQA_E_NULL, "rope params pointer is null");
   if (rp->rotary_dim < 0 || rp->rotary_dim % 2 || rp->rotary_dim > 2 * gqa::kMaxPairs)
@@ -63,15 +68,87 @@ gqa_status check_rope(const gqa_rope_params* rp) {
       if (!(std::isfinite(rp->original_max_pos) && rp->original_max_pos > 0.0))
         return fail(GQA_E_VALUE, "llama3 original_max_pos must be > 0, got %g", rp->original_max_pos);
       break;
+    case GQA_ROPE_YARN: {
+      if (!finite_pos(rp->factor))
+        return fail(GQA_E_VALUE, "yarn rope factor must be > 0, got %g", rp->factor);
+      if (!finite_pos(rp->original_max_pos))
+        return fail(GQA_E_VALUE, "yarn original_max_pos must be > 0, got %g", rp->original_max_pos);
+      const double bf = rp->beta_fast != 0.0 ? rp->beta_fast : 32.0;
+      const double bs = rp->beta_slow != 0.0 ? rp->beta_slow : 1.0;
+      if (!(finite_pos(bf) && finite_pos(bs) && bf > bs))
+        return fail(GQA_E_VALUE, "yarn needs beta_fast > beta_slow > 0, got %g, %g", bf, bs);
+      if (!finite_nonneg(rp->mscale) || !finite_nonneg(rp->mscale_all_dim))
+        return fail(GQA_E_VALUE, "yarn mscale and mscale_all_dim must be finite and >= 0");
+      if (!finite_nonneg(rp->attention_factor))
+        return fail(GQA_E_VALUE, "attention_factor must be finite and >= 0, got %g",
+                    rp->attention_factor);
+      break;
+    }
+    case GQA_ROPE_LONGROPE: {
+      if (!finite_pos(rp->original_max_pos))
+        return fail(GQA_E_VALUE, "longrope original_max_pos must be > 0, got %g",
+                    rp->original_max_pos);
+      if (!finite_nonneg(rp->attention_factor))
+        return fail(GQA_E_VALUE, "attention_factor must be finite and >= 0, got %g",
+                    rp->attention_factor);
+      if (rp->seq_len < 0) return fail(GQA_E_VALUE, "longrope seq_len must be >= 0");
+      const bool use_long = (double)rp->seq_len > rp->original_max_pos;
+      const double* table = use_long ? rp->long_factor : rp->short_factor;
+      if (rp->rotary_dim > 0 && !table)
+        return fail(GQA_E_NULL, "longrope needs the %s_factor table", use_long ? "long" : "short");
+      for (int i = 0; i < rp->rotary_dim / 2; ++i)
+        if (!finite_pos(table[i]))
+          return fail(GQA_E_VALUE, "longrope factor %d must be finite and > 0, got %g", i,
+                      table[i]);
+      break;
+    }
     default:
       return fail(GQA_E_UNSUPPORTED, "RoPE type %d is not implemented", rp->kind);
   }
+  if (rp->reserved != 0) return fail(GQA_E_VALUE, "rope params reserved field must be 0");
   return ok();
+}
+
+// YaRN's sharpening ([Models] "Scaled RoPE"): 0.1 * m * ln(s) + 1, 1 for s <= 1.
+double yarn_mscale(double s, double m) { return s <= 1.0 ? 1.0 : 0.1 * m * std::log(s) + 1.0; }
+
+// Factor multiplying cos and sin: yarn's given or derived one, longrope's given one or 1.
+double attention_factor_host(const gqa_rope_params* rp) {
+  if (rp->kind == GQA_ROPE_YARN) {
+    if (rp->attention_factor > 0.0) return rp->attention_factor;
+    if (rp->mscale > 0.0 && rp->mscale_all_dim > 0.0)
+      return yarn_mscale(rp->factor, rp->mscale) / yarn_mscale(rp->factor, rp->mscale_all_dim);
+    return yarn_mscale(rp->factor, 1.0);
+  }
+  if (rp->kind == GQA_ROPE_LONGROPE && rp->attention_factor > 0.0) return rp->attention_factor;
+  return 1.0;
 }
 
 void inv_freq_host(const gqa_rope_params* rp, double* out) {
   const int R = rp->rotary_dim;
   const double two_pi = 6.283185307179586476925286766559;
+  // yarn: the (fractional) pair index that turns r times over the original context solves
+  // original * theta^(-2x/R) = 2 pi r; the ramp runs from the beta_fast pair to the beta_slow one.
+  double ramp_lo = 0.0, ramp_w = 1.0;
+  if (rp->kind == GQA_ROPE_YARN) {
+    const double old = rp->original_max_pos;
+    auto pair_turning = [&](double r) {
+      return R * std::log(old / (r * two_pi)) / (2.0 * std::log(rp->theta));
+    };
+    double lo = pair_turning(rp->beta_fast != 0.0 ? rp->beta_fast : 32.0);
+    double hi = pair_turning(rp->beta_slow != 0.0 ? rp->beta_slow : 1.0);
+    if (!rp->yarn_no_truncate) {
+      lo = std::floor(lo);
+      hi = std::ceil(hi);
+    }
+    lo = std::max(lo, 0.0);
+    hi = std::min(hi, (double)(R - 1));
+    ramp_lo = lo;
+    ramp_w = hi != lo ? hi - lo : 0.001;
+  }
+  const double* table = nullptr;
+  if (rp->kind == GQA_ROPE_LONGROPE)
+    table = (double)rp->seq_len > rp->original_max_pos ? rp->long_factor : rp->short_factor;
   for (int i = 0; i < R / 2; ++i) {
     const double base = std::pow(rp->theta, -2.0 * i / R);
     double f = base;
@@ -89,6 +166,11 @@ void inv_freq_host(const gqa_rope_params* rp, double* out) {
                          (rp->high_freq_factor - rp->low_freq_factor);
         f = (1.0 - s) * base / rp->factor + s * base;
       }
+    } else if (rp->kind == GQA_ROPE_YARN) {
+      const double w = std::min(std::max((i - ramp_lo) / ramp_w, 0.0), 1.0);  // 1: divided
+      f = base / rp->factor * w + base * (1.0 - w);
+    } else if (rp->kind == GQA_ROPE_LONGROPE) {
+      f = base / table[i];
     }
     out[i] = f;
   }
@@ -180,6 +262,28 @@ gqa_status gqa_rope_inv_freq(const gqa_rope_params* rope, double* inv_freq_out) 
   return ok();
 }
 
+gqa_status gqa_rope_attention_factor(const gqa_rope_params* rope, double* out) {
+  gqa_status st = check_rope(rope);
+  if (st != GQA_OK) return st;
+  if (!out) return fail(GQA_E_NULL, "out is null");
+  *out = attention_factor_host(rope);
+  return ok();
+}
+
+gqa_status gqa_rope_softmax_scale(const gqa_rope_params* rope, int32_t qk_dim, double* out) {
+  gqa_status st = check_rope(rope);
+  if (st != GQA_OK) return st;
+  if (!out) return fail(GQA_E_NULL, "out is null");
+  if (qk_dim < 1) return fail(GQA_E_SHAPE, "qk_dim must be >= 1, got %d", qk_dim);
+  double sc = 1.0 / std::sqrt((double)qk_dim);
+  if (rope->kind == GQA_ROPE_YARN && rope->mscale_all_dim > 0.0) {
+    const double m = yarn_mscale(rope->factor, rope->mscale_all_dim);
+    sc *= m * m;
+  }
+  *out = sc;
+  return ok();
+}
+
 gqa_status gqa_rope_tables(const gqa_rope_params* rope, int32_t table_len, float* cos_out,
                            float* sin_out, hipStream_t stream) {
   gqa_status st = check_rope(rope);
@@ -189,8 +293,8 @@ gqa_status gqa_rope_tables(const gqa_rope_params* rope, int32_t table_len, float
   if (!cos_out || !sin_out) return fail(GQA_E_NULL, "cos_out/sin_out are null");
   double f[gqa::kMaxPairs];
   inv_freq_host(rope, f);
-  return hip_status(gqa::launch_rope_tables(f, rope->rotary_dim / 2, table_len, cos_out, sin_out,
-                                            stream),
+  return hip_status(gqa::launch_rope_tables(f, attention_factor_host(rope), rope->rotary_dim / 2,
+                                            table_len, cos_out, sin_out, stream),
                     "rope_tables launch");
 }
 

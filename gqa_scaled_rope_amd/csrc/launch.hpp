@@ -9,9 +9,10 @@ namespace gqa {
 
 constexpr int kMaxPairs = 256;  // rotary_dim <= 512
 
-// cos/sin tables [table_len, half] from host-computed frequencies (double).
-hipError_t launch_rope_tables(const double* inv_freq, int half, int table_len, float* cos_out,
-                              float* sin_out, hipStream_t stream);
+// cos/sin tables [table_len, half] from host-computed frequencies (double), both scaled by the
+// attention factor.
+hipError_t launch_rope_tables(const double* inv_freq, double attention_factor, int half,
+                              int table_len, float* cos_out, float* sin_out, hipStream_t stream);
 
 // Any head_dim <= 256, any grouping, fp32 or bf16: one wave per (query row, head).
 // Serves fp32 problems and shapes the MFMA kernels do not cover.

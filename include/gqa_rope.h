@@ -43,18 +43,37 @@ typedef enum gqa_status {
 
 typedef enum gqa_dtype { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
 
-/* [Models] "Scaled RoPE": the three frequency schedules of rope_scaling. */
-typedef enum gqa_rope_kind { GQA_ROPE_DEFAULT = 0, GQA_ROPE_LINEAR = 1, GQA_ROPE_LLAMA3 = 2 } gqa_rope_kind;
+/* [Models] "Scaled RoPE": the frequency schedules of rope_scaling (yarn included), and LongRoPE's
+ * per-pair factor tables ([Ster] "Overview"). */
+typedef enum gqa_rope_kind {
+  GQA_ROPE_DEFAULT = 0,
+  GQA_ROPE_LINEAR = 1,
+  GQA_ROPE_LLAMA3 = 2,
+  GQA_ROPE_YARN = 3,
+  GQA_ROPE_LONGROPE = 4
+} gqa_rope_kind;
 
 /* Pairing of rotated features: half-split pairs (i, i + R/2) ([Guide] section 4 "Rotary");
  * interleaved pairs (2i, 2i + 1) ([Models] "Serving it: absorbing the up-projections"). */
 typedef enum gqa_rot_style { GQA_ROT_HALF = 0, GQA_ROT_INTERLEAVED = 1 } gqa_rot_style;
 
-/* Rotary frequency schedule ([Models] "Scaled RoPE", rope_inv_freq).
+/* Rotary frequency schedule ([Models] "Scaled RoPE", rope_inv_freq).  A zero-initialised struct
+ * with rotary_dim, kind and theta set selects the pages' defaults for every other field.
  * rotary_dim R: number of rotated features, even, 0 <= R <= 512; R = head_dim *
  * partial_rotary_factor ([Ster] "Overview": only that share of each head rotates, and the
- * frequencies run over that share).  theta > 0.  factor > 0 (linear, llama3).  llama3 also needs
- * 0 < low_freq_factor < high_freq_factor and original_max_pos > 0. */
+ * frequencies run over that share).  theta > 0.  factor > 0 (linear, llama3, yarn; yarn callers
+ * whose config omits it pass max_positions / original_max_pos, as the page does).  llama3 also
+ * needs 0 < low_freq_factor < high_freq_factor; llama3, yarn and longrope need
+ * original_max_pos > 0.
+ *   yarn: pairs turning more than beta_fast times over original_max_pos keep their frequency,
+ *     pairs turning fewer than beta_slow times are divided by factor, a linear ramp over the pair
+ *     index in between, its ends rounded outwards unless yarn_no_truncate.  Attention factor:
+ *     attention_factor when > 0, else mscale(factor, mscale) / mscale(factor, mscale_all_dim)
+ *     when both are > 0, else mscale(factor), with mscale(s, m) = 0.1 m ln s + 1 (1 for s <= 1).
+ *   longrope: frequency i divided by short_factor[i] while seq_len <= original_max_pos, by
+ *     long_factor[i] once seq_len goes past ([Ster] "Overview"); both tables host memory, R/2
+ *     positive doubles, read during the call only.  Attention factor: attention_factor when > 0,
+ *     else 1 (the pages give the factor no formula). */
 typedef struct gqa_rope_params {
   int32_t rotary_dim;
   int32_t kind;               /* gqa_rope_kind */
@@ -63,6 +82,16 @@ typedef struct gqa_rope_params {
   double low_freq_factor;
   double high_freq_factor;
   double original_max_pos;    /* original_max_position_embeddings */
+  double beta_fast;           /* yarn: 0 selects 32 */
+  double beta_slow;           /* yarn: 0 selects 1; beta_fast > beta_slow */
+  int32_t yarn_no_truncate;   /* yarn: nonzero keeps the ramp ends unrounded (truncate: false) */
+  int32_t reserved;           /* must be 0 */
+  double mscale;              /* yarn: 0 = absent */
+  double mscale_all_dim;      /* yarn: 0 = absent */
+  double attention_factor;    /* yarn, longrope: > 0 given; 0 = derived as above */
+  const double* short_factor; /* longrope: host [R/2] */
+  const double* long_factor;  /* longrope: host [R/2] */
+  int64_t seq_len;            /* longrope: sequence length that selects the table */
 } gqa_rope_params;
 
 /* Attention configuration shared by prefill and decode. */
@@ -85,9 +114,10 @@ typedef struct gqa_attn_cfg {
 } gqa_attn_cfg;
 
 /* Build cos/sin tables for positions 0 .. table_len-1 ([Models] "Scaled RoPE", rope_tables):
- * cos_out[p*(R/2) + i] = cos(p * inv_freq[i]), sin_out likewise, attention factor 1.  inv_freq is
- * computed on the host in double precision and the angles and their sine/cosine on the device in
- * double precision, then stored as fp32.  cos_out, sin_out: device, table_len * R/2 floats each,
+ * cos_out[p*(R/2) + i] = a * cos(p * inv_freq[i]), sin_out likewise, with a the attention factor
+ * (1 except for yarn and longrope).  inv_freq is computed on the host in double precision and the
+ * angles, their sine/cosine and the product with a on the device in double precision, then
+ * stored as fp32.  cos_out, sin_out: device, table_len * R/2 floats each,
  * caller-owned.  table_len >= 1.  R == 0 is a valid no-op. */
 gqa_status gqa_rope_tables(const gqa_rope_params* rope, int32_t table_len, float* cos_out,
                            float* sin_out, hipStream_t stream);
@@ -95,6 +125,15 @@ gqa_status gqa_rope_tables(const gqa_rope_params* rope, int32_t table_len, float
 /* Host-side copy of the frequencies the tables use (R/2 doubles into inv_freq_out, host memory).
  * Lets a caller inspect the schedule without a GPU. */
 gqa_status gqa_rope_inv_freq(const gqa_rope_params* rope, double* inv_freq_out);
+
+/* The attention factor the tables are multiplied by ([Models] "Scaled RoPE"), into *out (host). */
+gqa_status gqa_rope_attention_factor(const gqa_rope_params* rope, double* out);
+
+/* Softmax scale for a query/key width qk_dim > 0 ([Models] "Multi-head latent attention": YaRN's
+ * temperature applied to the scale): qk_dim^-0.5, times m^2 with m = 0.1 * mscale_all_dim *
+ * ln(factor) + 1 when the schedule is yarn with mscale_all_dim > 0 and factor > 1.  Into *out
+ * (host); pass it as gqa_attn_cfg.scale. */
+gqa_status gqa_rope_softmax_scale(const gqa_rope_params* rope, int32_t qk_dim, double* out);
 
 /* Prepare new keys for a cache: for every row j in [n_cached, S) of k [B, S, Hkv, D] and every KV
  * head, RMS-norm the row (when cfg->qk_norm, gain k_norm_w) and rotate its first rotary_dim

@@ -137,13 +137,26 @@ def test_rope_param_validation():
     assert st(theta=0.0) == 7
     assert st(kind="linear", factor=0.0) == 7
     assert st(kind="llama3", factor=8.0, low_freq_factor=4.0, high_freq_factor=1.0) == 7
-    p = g._RopeParams(64, 9, 1e4, 1.0, 1.0, 4.0, 8192.0)
+    p = g.RopeSpec(64).c_struct()
+    p.kind = 9
     assert lib.gqa_rope_tables(ctypes.byref(p), 16, FAKE, FAKE, None) == 4
     assert "not implemented" in g.last_error()
     p = g.RopeSpec(64).c_struct()
     assert lib.gqa_rope_tables(ctypes.byref(p), 0, FAKE, FAKE, None) == 2
     with pytest.raises(g.GQAError):
-        g.RopeSpec(64, kind="yarn").c_struct()
+        g.RopeSpec(64, kind="dynamic").c_struct()
+    assert st(kind="yarn", factor=0.0) == 7
+    assert st(kind="yarn", factor=4.0, beta_fast=1.0, beta_slow=2.0) == 7
+    assert st(kind="yarn", factor=4.0, original_max_pos=0.0) == 7
+    assert st(kind="longrope") == 1                       # no short table
+    assert "short_factor" in g.last_error()
+    assert st(kind="longrope", short_factor=[1.0] * 32, seq_len=9000) == 1   # needs the long one
+    assert st(kind="longrope", short_factor=[1.0] * 31 + [0.0]) == 7
+    with pytest.raises(g.GQAError):
+        g.RopeSpec(64, kind="longrope", short_factor=[1.0] * 31).c_struct()
+    p = g.RopeSpec(64).c_struct()
+    p.reserved = 1
+    assert lib.gqa_rope_tables(ctypes.byref(p), 16, FAKE, FAKE, None) == 7
 
 
 @pytest.mark.parametrize("R,kind,theta,factor", [
@@ -154,6 +167,58 @@ def test_host_inv_freq_matches_oracle(R, kind, theta, factor):
     got = np.array(g.rope_inv_freq(g.RopeSpec(R, kind, theta, factor, 1.0, 4.0, 8192.0)))
     ref = oracle.rope_inv_freq(R, theta, kind, factor, 1.0, 4.0, 8192.0)
     np.testing.assert_allclose(got, ref, rtol=1e-15, atol=0)
+
+
+_LONG = [1.0 + 0.05 * i for i in range(32)]
+_SHORT = [1.0 + 0.01 * i for i in range(32)]
+
+
+@pytest.mark.parametrize("kw,okw", [
+    (dict(rotary_dim=128, theta=1e4, factor=4.0, original_max_pos=4096.0), {}),
+    (dict(rotary_dim=64, theta=1e4, factor=40.0, original_max_pos=4096.0, beta_fast=32.0,
+          beta_slow=1.0), dict(beta_fast=32.0, beta_slow=1.0)),
+    (dict(rotary_dim=128, theta=5e5, factor=8.0, original_max_pos=8192.0, truncate=False),
+     dict(truncate=False)),
+    (dict(rotary_dim=32, theta=1e6, factor=16.0, original_max_pos=2048.0, beta_fast=16.0,
+          beta_slow=2.0, truncate=False), dict(beta_fast=16.0, beta_slow=2.0, truncate=False)),
+])
+def test_host_yarn_matches_oracle(kw, okw):
+    spec = g.RopeSpec(kind="yarn", **kw)
+    got = np.array(g.rope_inv_freq(spec))
+    ref = oracle.rope_inv_freq(kw["rotary_dim"], kw["theta"], "yarn", kw["factor"],
+                               original_max_position_embeddings=kw["original_max_pos"], **okw)
+    np.testing.assert_allclose(got, ref, rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("seq_len", [0, 4096, 4097, 131072])
+def test_host_longrope_matches_oracle(seq_len):
+    spec = g.RopeSpec(64, "longrope", 1e4, original_max_pos=4096.0, short_factor=_SHORT,
+                      long_factor=_LONG, seq_len=seq_len)
+    got = np.array(g.rope_inv_freq(spec))
+    ref = oracle.rope_inv_freq(64, 1e4, "longrope", original_max_position_embeddings=4096.0,
+                               short_factor=_SHORT, long_factor=_LONG, seq_len=seq_len)
+    np.testing.assert_allclose(got, ref, rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("kind,factor,extra", [
+    ("default", 1.0, {}), ("llama3", 8.0, {}), ("yarn", 4.0, {}), ("yarn", 0.5, {}),
+    ("yarn", 40.0, dict(mscale=1.0, mscale_all_dim=0.707)),
+    ("yarn", 40.0, dict(mscale=0.707, mscale_all_dim=0.707)),
+    ("yarn", 40.0, dict(mscale_all_dim=1.0)),
+    ("yarn", 16.0, dict(attention_factor=1.25)), ("longrope", 1.0, {}),
+    ("longrope", 1.0, dict(attention_factor=1.19)),
+])
+def test_host_attention_factor_and_softmax_scale_match_oracle(kind, factor, extra):
+    spec = g.RopeSpec(64, kind, 1e4, factor, original_max_pos=4096.0, short_factor=_SHORT,
+                      **extra)
+    ref = oracle.rope_attention_factor(kind, factor, **extra)
+    assert g.rope_attention_factor(spec) == pytest.approx(ref, rel=1e-15)
+    for qk_dim in (64, 128, 192):
+        ref_sc = (oracle.yarn_softmax_scale(qk_dim, factor, extra.get("mscale_all_dim"))
+                  if kind == "yarn" else qk_dim ** -0.5)
+        assert g.rope_softmax_scale(spec, qk_dim) == pytest.approx(ref_sc, rel=1e-15)
+    with pytest.raises(g.GQAError):
+        g.rope_softmax_scale(spec, 0)
 
 
 def test_policy_switch_validates():

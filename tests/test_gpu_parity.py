@@ -398,3 +398,124 @@ def test_all_scores_far_below_zero(policy):
     ref = ref_prefill(wl, x)
     assert np.abs(ref).max() > 0.05      # a real (non-degenerate) softmax
     check(gpu_prefill(wl, x), ref)
+
+
+# ----------------------------------------------------------------------------------------------
+# YaRN and LongRoPE: the tables carry the attention factor, YaRN's temperature enters through the
+# softmax scale.  Original contexts are short so that the test positions go well past them and the
+# kept, ramped and divided pairs all occur.
+_LR_SHORT = [1.0 + 0.02 * i for i in range(64)]
+_LR_LONG = [1.0 + 0.25 * i for i in range(64)]
+SCHED = {
+    "yarn_mscale": dict(kind="yarn", theta=1e4, factor=8.0, original_max_pos=128.0, mscale=1.0,
+                        mscale_all_dim=0.707),
+    "yarn_default": dict(kind="yarn", theta=1e6, factor=16.0, original_max_pos=64.0),
+    "yarn_betas_untruncated": dict(kind="yarn", theta=1e4, factor=4.0, original_max_pos=200.0,
+                                   beta_fast=8.0, beta_slow=2.0, truncate=False),
+    "longrope_long": dict(kind="longrope", theta=1e4, original_max_pos=128.0,
+                          attention_factor=1.19),
+    "longrope_short": dict(kind="longrope", theta=1e4, original_max_pos=4096.0),
+}
+
+
+def sched_spec(name, R, seq_len):
+    kw = dict(SCHED[name])
+    if kw["kind"] == "longrope":
+        kw.update(short_factor=_LR_SHORT[: R // 2], long_factor=_LR_LONG[: R // 2],
+                  seq_len=seq_len)
+    return g.RopeSpec(R, **kw)
+
+
+def sched_oracle(name, R, seq_len, qk_dim):
+    """(inv_freq, attention_factor, softmax scale) from the oracle."""
+    kw = dict(SCHED[name])
+    kind, theta = kw.pop("kind"), kw.pop("theta")
+    old = kw.pop("original_max_pos")
+    factor = kw.pop("factor", 1.0)
+    af_kw = {k: kw.pop(k) for k in ("mscale", "mscale_all_dim", "attention_factor") if k in kw}
+    if kind == "longrope":
+        kw.update(short_factor=_LR_SHORT[: R // 2], long_factor=_LR_LONG[: R // 2],
+                  seq_len=seq_len)
+    inv = oracle.rope_inv_freq(R, theta, kind, factor, original_max_position_embeddings=old, **kw)
+    af = oracle.rope_attention_factor(kind, factor, **af_kw)
+    sc = (oracle.yarn_softmax_scale(qk_dim, factor, af_kw.get("mscale_all_dim"))
+          if kind == "yarn" else qk_dim ** -0.5)
+    return inv, af, sc
+
+
+@pytest.mark.parametrize("name", list(SCHED))
+def test_schedule_tables_match_oracle(name):
+    say("tables", name)
+    R, n = 128, 3000
+    cos, sin = g.rope_tables(sched_spec(name, R, n), n)
+    torch.cuda.synchronize()
+    inv, af, _ = sched_oracle(name, R, n, 128)
+    assert (af != 1.0) == (name in ("yarn_mscale", "yarn_default", "yarn_betas_untruncated",
+                                    "longrope_long"))
+    ang = oracle.rope_angles(np.arange(n), inv)
+    np.testing.assert_allclose(cos.cpu().numpy(), af * np.cos(ang), rtol=0, atol=3e-7)
+    np.testing.assert_allclose(sin.cpu().numpy(), af * np.sin(ang), rtol=0, atol=3e-7)
+
+
+@pytest.mark.parametrize("name,wkw", [
+    ("yarn_mscale", dict(qk_norm=True)),
+    ("yarn_default", dict(rotary_dim=64, style="interleaved", softcap=30.0, n_cached=150)),
+    ("yarn_betas_untruncated", dict(window=90)),
+    ("longrope_long", dict(rotary_dim=64)),
+    ("longrope_short", dict(qk_norm=True)),
+])
+def test_prefill_rope_schedules(name, wkw, policy):
+    wl = BASE.with_(**{**dict(qk_norm=False), **wkw})
+    say("prefill schedule", name, wkw, "policy", policy)
+    x = prefill_inputs(wl, seed=zlib.crc32(name.encode()) % 1000)
+    spec_ = sched_spec(name, wl.rotary_dim, wl.S)
+    cos, sin = g.rope_tables(spec_, wl.S)
+    scale = g.rope_softmax_scale(spec_, wl.D)
+    cfg = g.AttnConfig("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin, wl.qk_norm,
+                       wl.eps, dev(x["q_norm_w"]) if wl.qk_norm else None,
+                       dev(x["k_norm_w"]) if wl.qk_norm else None, scale, wl.softcap)
+    out = g.attn_prefill(cfg, dev(x["q"]), dev(x["k"]), dev(x["v"]),
+                         dev(x["positions"], torch.int32), dev(x["key_positions"], torch.int32),
+                         wl.n_cached, wl.window,
+                         workspace=None if policy == "fused" else "auto")
+    torch.cuda.synchronize()
+    inv, af, sc = sched_oracle(name, wl.rotary_dim, wl.S, wl.D)
+    assert scale == pytest.approx(sc, rel=1e-12)
+    ref = oracle.attn_prefill(x["q"], x["k"], x["v"], x["positions"], x["key_positions"],
+                              inv_freq=inv, style=wl.style, n_cached=wl.n_cached,
+                              window=wl.window, q_norm_w=x.get("q_norm_w"),
+                              k_norm_w=x.get("k_norm_w"), eps=wl.eps, softcap=wl.softcap,
+                              attention_factor=af, scale=sc)
+    if name == "yarn_mscale":
+        # the schedule changes the result: plain RoPE at the default scale is far off
+        plain = ref_prefill(wl, x)
+        assert np.abs(plain - ref).max() > 0.1
+    check(out.float().cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("name", ["yarn_mscale", "longrope_long"])
+def test_decode_rope_schedules(name, policy):
+    if policy == "fused":
+        pytest.skip("decode has no fused/stream distinction")
+    wl = DEC.with_(rope_kind="default", theta=1e4, qk_norm=True)
+    say("decode schedule", name, "policy", policy)
+    lens, q, qw = decode_lens_q(wl, seed=23)
+    lens[0], lens[1] = 1, wl.S
+    kc = np.zeros((wl.B, wl.Hkv, wl.S, wl.D), np.float32)
+    vc = np.zeros_like(kc)
+    for b in range(wl.B):
+        kk, vv = decode_cache_seq(wl, b, int(lens[b]), seed=23)
+        kc[b, :, :lens[b]] = kk
+        vc[b, :, :lens[b]] = vv
+    spec_ = sched_spec(name, wl.rotary_dim, wl.S)
+    cos, sin = g.rope_tables(spec_, wl.S)
+    scale = g.rope_softmax_scale(spec_, wl.D)
+    cfg = g.AttnConfig("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin, True,
+                       wl.eps, dev(qw), dev(qw), scale, wl.softcap)
+    out = g.attn_decode(cfg, dev(q), dev(kc), dev(vc), dev(lens, torch.int32), wl.window)
+    torch.cuda.synchronize()
+    inv, af, sc = sched_oracle(name, wl.rotary_dim, wl.S, wl.D)
+    ref = oracle.attn_decode(q, kc, vc, lens, inv_freq=inv, style=wl.style, window=wl.window,
+                             q_norm_w=qw, eps=wl.eps, softcap=wl.softcap, attention_factor=af,
+                             scale=sc)
+    check(out.float().cpu().numpy(), ref, head_axis=1)
