@@ -21,8 +21,10 @@ of linear scaling; llama3 per-band behaviour; YaRN's rotation-count split, ramp 
 reduction to plain RoPE at factor 1 and its sharpening values; LongRoPE's reduction to plain and
 linear RoPE and its short/long switch; the attention factor on the table norm; complex-multiplication form of the rotation; the
 half-split pairing of the study guide; deinterleave equivalence; norm preservation; relative
-position; RMS of the normed vector; soft-cap limits; integer mask probe; window and GQA
-equivalences; decode == last prefill row; chunked prefill == tail of full prefill; brute-force
+position; RMS of the normed vector; soft-cap limits; integer mask probes (windows, chunks with
+and without lookback, floor chunks of negative positions); the sink's closed forms (one key: a
+logistic weight; constant values: the share the keys keep) and torch's SDPA with the sink as one
+more key; chunks without lookback restarting the sequence; window and GQA equivalences; decode == last prefill row; chunked prefill == tail of full prefill; brute-force
 scalar loops; and torch's CPU scaled_dot_product_attention in float64.  No function here is
 "parity unpinned".
 """
@@ -209,29 +211,39 @@ def rotate(x, positions, inv_freq, style="half", attention_factor=1.0):
 # ----------------------------------------------------------------------------------------------
 # Mask and softmax core
 # ----------------------------------------------------------------------------------------------
-def allowed_mask(query_positions, key_positions, window):
+def allowed_mask(query_positions, key_positions, window, chunk=0, chunk_lookback=0):
     """May query at position qp attend key at position kp?
 
     Causal by positions, not indices ([Models] "What differs": causal_attention takes positions
     and key_positions).  Sliding window ([Models] "Sliding windows"): keys more than w - 1
     positions back are masked, so a query sees at most w keys including itself; w = 0 means
-    no window.  Returns a [len(qp), len(kp)] bool array."""
+    no window.  Chunked attention ([Ster] llama4_text and Rnj-1.5 paragraphs): positions fall in
+    chunks of `chunk` (chunk c holds c*chunk .. (c+1)*chunk - 1); a query sees the keys of its own
+    chunk (llama4) and of the chunk_lookback chunks before it (Rnj-1.5: one); chunk = 0 means no
+    chunking.  Reading: when both are set the key must pass both tests.
+    Returns a [len(qp), len(kp)] bool array."""
     qp = np.asarray(query_positions, dtype=np.int64)[:, None]
     kp = np.asarray(key_positions, dtype=np.int64)[None, :]
     ok = kp <= qp
     if window > 0:
         ok &= (qp - kp) <= (window - 1)
+    if chunk > 0:
+        ok &= (kp // chunk) >= (qp // chunk) - chunk_lookback     # floor division
     return ok
 
 
-def softmax_attention(q, k, v, allowed, scale, softcap=0.0):
+def softmax_attention(q, k, v, allowed, scale, softcap=0.0, sink=None):
     """Masked softmax attention of one head: out_i = sum_j p_ij v_j with
     p_i = softmax over allowed j of s_ij, s_ij = scale * <q_i, k_j> ([Guide] §3.4 Attention).
 
     Soft-cap (reading; the pages name it without a formula, [Ster] "Overview"): s <- cap *
     tanh(s / cap) after scaling and before masking; cap = 0 means off.
+    Learned sink ([Ster] gpt_oss paragraph): one more logit `sink` joins every row's softmax and
+    its share is dropped: p_ij = exp(s_ij) / (sum_allowed exp(s_ij') + exp(sink)).  Reading: the
+    sink is a logit in the units of the scaled scores, not scaled and not soft-capped.
     Max subtraction as in [Guide] §2.3.  A row with no allowed key has output 0 (reading:
-    [Guide] §3.7 notes that such a row would otherwise be NaN)."""
+    [Guide] §3.7 notes that such a row would otherwise be NaN; with a sink the sink takes the
+    whole share, which gives the same 0)."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -244,8 +256,13 @@ def softmax_attention(q, k, v, allowed, scale, softcap=0.0):
         return out
     s_masked = np.where(allowed, s, -np.inf)
     m = np.max(s_masked[any_allowed], axis=1, keepdims=True)
+    if sink is not None:
+        m = np.maximum(m, float(sink))
     p = np.where(allowed[any_allowed], np.exp(s[any_allowed] - m), 0.0)
-    out[any_allowed] = (p @ v) / p.sum(axis=1, keepdims=True)
+    den = p.sum(axis=1, keepdims=True)
+    if sink is not None:
+        den = den + np.exp(float(sink) - m)
+    out[any_allowed] = (p @ v) / den
     return out
 
 
@@ -259,7 +276,8 @@ def _scale(head_dim, scale):
 
 def attn_prefill(q, k, v, positions, key_positions, *, inv_freq, style="half", n_cached=0,
                  window=0, q_norm_w=None, k_norm_w=None, eps=1e-6, scale=0.0, softcap=0.0,
-                 query_rows=None, heads=None, batches=None, attention_factor=1.0):
+                 query_rows=None, heads=None, batches=None, attention_factor=1.0, sinks=None,
+                 chunk=0, chunk_lookback=0):
     """Causal prefill of one layer: [Models] "What differs" (DecoderAttention.forward).
 
     q [B, L, Hq, D], k and v [B, S, Hkv, D], positions [B, L], key_positions [B, S].
@@ -269,6 +287,7 @@ def attn_prefill(q, k, v, positions, key_positions, *, inv_freq, style="half", n
     rotated.  Query head h reads KV head h // (Hq/Hkv) (reading: consecutive query heads share a
     KV head, i.e. K/V repeated with repeat_interleave, [Guide] §1.6).  Then masked softmax
     attention per head.  Returns out [B', L', Hq', D] for the selected batches, rows and heads.
+    sinks: None or one logit per query head [Hq]; chunk, chunk_lookback: see allowed_mask.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -296,15 +315,17 @@ def attn_prefill(q, k, v, positions, key_positions, *, inv_freq, style="half", n
         if k_norm_w is not None:
             kn = rms_norm(kn, k_norm_w, eps)
         kb[new] = rotate(kn, key_positions[b, new][:, None], inv_freq, style, attention_factor)
-        allowed = allowed_mask(positions[b, rows], key_positions[b], window)
+        allowed = allowed_mask(positions[b, rows], key_positions[b], window, chunk, chunk_lookback)
         for hi, h in enumerate(heads):
             g = h // G
-            out[bi, :, hi] = softmax_attention(qb[:, h], kb[:, g], v[b, :, g], allowed, sc, softcap)
+            out[bi, :, hi] = softmax_attention(qb[:, h], kb[:, g], v[b, :, g], allowed, sc, softcap,
+                                               None if sinks is None else sinks[h])
     return out
 
 
 def attn_decode_one(q, k, v, n, *, inv_freq, style="half", window=0, q_norm_w=None, eps=1e-6,
-                    scale=0.0, softcap=0.0, heads=None, attention_factor=1.0):
+                    scale=0.0, softcap=0.0, heads=None, attention_factor=1.0, sinks=None,
+                    chunk=0, chunk_lookback=0):
     """Single-token decode of one sequence against its cache ([Guide] §3.3 KVCache, §3.7).
 
     q [Hq, D]; k, v [Hkv, >= n, D] hold the sequence's cache rows, slot j at position j, already
@@ -319,14 +340,15 @@ def attn_decode_one(q, k, v, n, *, inv_freq, style="half", window=0, q_norm_w=No
     pos = n - 1
     qq = q if q_norm_w is None else rms_norm(q, q_norm_w, eps)
     qq = rotate(qq, np.full(Hq, pos), inv_freq, style, attention_factor)
-    allowed = allowed_mask([pos], np.arange(n), window)
+    allowed = allowed_mask([pos], np.arange(n), window, chunk, chunk_lookback)
     sc = _scale(D, scale)
     out = np.zeros((len(heads), D), dtype=np.float64)
     for hi, h in enumerate(heads):
         g = h // G
         kk = np.asarray(k[g, :n], np.float64)
         vv = np.asarray(v[g, :n], np.float64)
-        out[hi] = softmax_attention(qq[h:h + 1], kk, vv, allowed, sc, softcap)[0]
+        out[hi] = softmax_attention(qq[h:h + 1], kk, vv, allowed, sc, softcap,
+                                    None if sinks is None else sinks[h])[0]
     return out
 
 

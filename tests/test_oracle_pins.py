@@ -398,6 +398,94 @@ def test_fully_masked_row_is_zero():
     np.testing.assert_allclose(out[1], 1.0)
 
 
+@pytest.mark.parametrize("chunk,lookback", [(1, 0), (4, 0), (7, 0), (8, 1), (5, 1), (6, 2),
+                                            (64, 0)])
+def test_chunk_mask_probe_counts_allowed_keys(chunk, lookback):
+    # [Ster] llama4_text: a query sees only the keys of its own chunk of attention_chunk_size
+    # positions; Rnj-1.5: also the chunk before it.  Integer definition: the query's chunk starts
+    # at i - i mod chunk, and `lookback` whole chunks before that are visible too.
+    S = L = 40
+    kp = np.arange(S)
+    v = np.stack([np.ones(S), kp, kp.astype(float) ** 2], axis=1)
+    out = oracle.softmax_attention(np.zeros((L, 4)), np.ones((S, 4)), v,
+                                   oracle.allowed_mask(np.arange(L), kp, 0, chunk, lookback), 1.0)
+    for i in range(L):
+        start = i - i % chunk
+        keys = np.arange(max(0, start - lookback * chunk), i + 1)
+        assert out[i, 0] == pytest.approx(1.0)
+        assert out[i, 1] == pytest.approx(keys.mean(), abs=1e-9)
+        assert out[i, 2] == pytest.approx((keys.astype(float) ** 2).mean(), abs=1e-7)
+
+
+def test_chunk_mask_with_window_and_negative_positions():
+    # both tests apply; chunks tile negative positions too (chunk c = [c*C, (c+1)*C))
+    m = oracle.allowed_mask([9], np.arange(0, 12), 3, 4, 1)
+    np.testing.assert_array_equal(np.flatnonzero(m[0]), [7, 8, 9])
+    m = oracle.allowed_mask([-3], np.arange(-12, 0), 0, 4, 0)
+    np.testing.assert_array_equal(np.flatnonzero(m[0]) - 12, [-4, -3])
+
+
+def test_sink_closed_forms():
+    # [Ster] gpt_oss: one extra logit per head joins the softmax and its share is dropped.
+    # One allowed key with score s: weight e^s / (e^s + e^sink) = 1 / (1 + e^(sink - s)).
+    q = np.array([[0.5, -1.0, 2.0]])
+    k = np.array([[1.0, 0.25, 0.75]])
+    v = np.array([[3.0, -2.0]])
+    s0 = 0.4 * (0.5 - 0.25 + 1.5)
+    for sink in (-3.0, 0.0, 1.7, 40.0):
+        got = oracle.softmax_attention(q, k, v, np.array([[True]]), 0.4, sink=sink)
+        w = 1.0 / (1.0 + math.exp(sink - s0))
+        np.testing.assert_allclose(got[0], w * v[0], rtol=1e-13)
+    # constant values: the output is the share the keys keep, Z / (Z + e^sink)
+    qq = rng.standard_normal((3, 6))
+    kk = rng.standard_normal((9, 6))
+    allowed = np.tril(np.ones((3, 9), bool), 6)
+    got = oracle.softmax_attention(qq, kk, np.ones((9, 1)), allowed, 0.5, sink=0.3)
+    for i in range(3):
+        z = sum(math.exp(0.5 * float(qq[i] @ kk[j])) for j in range(9) if allowed[i, j])
+        assert got[i, 0] == pytest.approx(z / (z + math.exp(0.3)), rel=1e-13)
+    # a sink at -inf is no sink; a row with no allowed key stays 0
+    vv = rng.standard_normal((9, 2))
+    np.testing.assert_array_equal(oracle.softmax_attention(qq, kk, vv, allowed, 0.5, sink=-np.inf),
+                                  oracle.softmax_attention(qq, kk, vv, allowed, 0.5))
+    z = oracle.softmax_attention(qq, kk, np.ones((9, 2)), np.zeros((3, 9), bool), 0.5, sink=2.0)
+    np.testing.assert_array_equal(z, 0.0)
+
+
+@pytest.mark.parametrize("cap", [0.0, 2.0])
+def test_sink_against_torch_sdpa_virtual_key(cap):
+    # the sink as one more key: give q an extra feature 1 and that key the feature sink/scale with
+    # value 0, every real key feature 0; torch's float64 SDPA then sees exactly the sink logit.
+    # (Soft-cap changes the real scores only; with a cap the check runs on the capped scores.)
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    L, S, D, scale = 6, 11, 8, 0.37
+    q = rng.standard_normal((L, D))
+    k = rng.standard_normal((S, D))
+    v = rng.standard_normal((S, 3))
+    allowed = oracle.allowed_mask(np.arange(5, 5 + L), np.arange(S), 4)
+    sink = 0.8
+    got = oracle.softmax_attention(q, k, v, allowed, scale, cap, sink=sink)
+    if cap:
+        s = cap * np.tanh(scale * (q @ k.T) / cap)          # capped scores, then as logits
+        qx = np.concatenate([s, np.ones((L, 1))], axis=1)
+        kx = np.concatenate([np.eye(S), np.zeros((S, 1))], axis=1)
+        vk = np.concatenate([np.zeros((1, S)), [[sink]]], axis=1)
+        kx = np.concatenate([kx, vk], axis=0)
+        sc = 1.0
+    else:
+        qx = np.concatenate([q, np.ones((L, 1))], axis=1)
+        kx = np.concatenate([np.concatenate([k, np.zeros((S, 1))], axis=1),
+                             np.concatenate([np.zeros((1, D)), [[sink / scale]]], axis=1)])
+        sc = scale
+    vx = np.concatenate([v, np.zeros((1, 3))])
+    mask = np.concatenate([allowed, np.ones((L, 1), bool)], axis=1)
+    ref = F.scaled_dot_product_attention(torch.from_numpy(qx)[None], torch.from_numpy(kx)[None],
+                                         torch.from_numpy(vx)[None],
+                                         attn_mask=torch.from_numpy(mask)[None], scale=sc)
+    np.testing.assert_allclose(got, ref[0].numpy(), atol=1e-13)
+
+
 # ----------------------------------------------------------------------------------------------
 # Whole-path equivalences and library cross-checks
 # ----------------------------------------------------------------------------------------------
@@ -496,3 +584,32 @@ def test_selected_rows_and_heads_match_full():
     full = _prefill(wl, x)
     part = _prefill(wl, x, query_rows=[0, 7, 32], heads=[3, 1], batches=[1])
     np.testing.assert_array_equal(part[0], full[1][[0, 7, 32]][:, [3, 1]])
+
+
+def test_chunks_without_lookback_restart_the_sequence():
+    # [Ster] llama4_text: each query sees only its own chunk, so attending the whole sequence
+    # equals attending each chunk on its own (positions kept, rotation included)
+    wl = _small(B=1, L=30, S=30, Hq=4, Hkv=2, D=16, rotary_dim=16, qk_norm=True)
+    x = prefill_inputs(wl, seed=15)
+    C = 8
+    whole = _prefill(wl, x, chunk=C)
+    for c0 in range(0, 30, C):
+        part = {k: (v[:, c0:c0 + C] if k in ("q", "k", "v", "positions", "key_positions") else v)
+                for k, v in x.items()}
+        alone = _prefill(wl.with_(L=len(range(c0, min(30, c0 + C)))), part)
+        np.testing.assert_allclose(whole[:, c0:c0 + C], alone, atol=1e-13)
+
+
+def test_decode_equals_last_prefill_row_with_sinks_and_chunks():
+    wl = _small("llama31_decode_bf16", B=1, L=37, S=37, Hq=8, Hkv=2, D=32, rotary_dim=32)
+    x = prefill_inputs(wl.with_(kind="prefill"), seed=16)
+    inv = oracle.rope_inv_freq(32, 5e5, "llama3", 8.0, 1.0, 4.0, 8192.0)
+    sinks = rng.standard_normal(8) * 2.0
+    for chunk, lookback in ((8, 1), (16, 0), (0, 0)):
+        full = _prefill(wl, x, inv_freq=inv, sinks=sinks, chunk=chunk,
+                        chunk_lookback=lookback)[0, -1]
+        kc = oracle.rotate(x["k"][0], np.arange(37)[:, None], inv, "half").transpose(1, 0, 2)
+        vc = x["v"][0].transpose(1, 0, 2)
+        dec = oracle.attn_decode_one(x["q"][0, -1], kc, vc, 37, inv_freq=inv, sinks=sinks,
+                                     chunk=chunk, chunk_lookback=lookback)
+        np.testing.assert_allclose(dec, full, atol=1e-13)
