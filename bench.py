@@ -31,10 +31,18 @@ METRIC = "prefill attn TFLOP/s (% MFMA peak); decode KV GB/s (% HBM peak)"
 
 
 # ---- work models (pure functions; pinned by tests/test_abi_cpu.py) -----------------------------
-def allowed_pairs(L, S, window, n_cached):
+def allowed_pairs(L, S, window, n_cached, chunk=0, chunk_lookback=0):
     """Allowed (query, key) pairs of one (sequence, head): queries at positions S-L..S-1 when
-    keys before them are cached, else 0..L-1; keys at 0..S-1."""
+    keys before them are cached, else 0..L-1; keys at 0..S-1.  With chunks each query sees
+    its own chunk and chunk_lookback chunks before it (and at most `window` keys)."""
     start = S - L if n_cached else 0
+    if chunk > 0:
+        import numpy as np
+        p = np.arange(start, start + L, dtype=np.int64)
+        lo = np.maximum(0, (p // chunk - chunk_lookback) * chunk)
+        if window > 0:
+            lo = np.maximum(lo, p - window + 1)
+        return int(np.maximum(np.minimum(p, S - 1) - lo + 1, 0).sum())
 
     def upto(n):  # sum over positions p < n of min(p + 1, w), w = infinity when 0
         if n <= 0:
@@ -46,16 +54,27 @@ def allowed_pairs(L, S, window, n_cached):
 
 
 def prefill_flops(wl):
-    return 4 * wl.B * wl.Hq * wl.D * allowed_pairs(wl.L, wl.S, wl.window, wl.n_cached)
+    return 4 * wl.B * wl.Hq * wl.D * allowed_pairs(wl.L, wl.S, wl.window, wl.n_cached, wl.chunk,
+                                                   wl.chunk_lookback)
 
 
 def kv_bytes_per_token_per_layer(kv_heads, head_dim, bytes_per_elem):
     return 2 * kv_heads * head_dim * bytes_per_elem
 
 
+def decode_keys(wl, n):
+    """Cache rows a decode query at position n - 1 reads: its window and chunks."""
+    first = 0
+    if wl.window:
+        first = max(first, n - wl.window)
+    if wl.chunk:
+        first = max(first, ((n - 1) // wl.chunk - wl.chunk_lookback) * wl.chunk)
+    return n - first
+
+
 def decode_bytes(wl, lens):
     eb = 2 if wl.dtype == "bf16" else 4
-    keys = sum(min(int(n), wl.window) if wl.window else int(n) for n in lens)
+    keys = sum(decode_keys(wl, int(n)) for n in lens)
     return (keys * kv_bytes_per_token_per_layer(wl.Hkv, wl.D, eb)
             + 2 * wl.B * wl.Hq * wl.D * eb + 4 * wl.B)
 
@@ -87,6 +106,14 @@ def _rope_spec(g, wl):
                       wl.high_freq_factor, wl.original_max_pos)
 
 
+def _mask_cfg(wl, torch):
+    """Learned sinks (seeded draw) and chunking of a workload, as AttnConfig fields."""
+    from synth import draw_sinks
+    sk = draw_sinks(wl)
+    return dict(sinks=None if sk is None else torch.from_numpy(sk).to("cuda"),
+                chunk_size=wl.chunk, chunk_lookback=wl.chunk_lookback)
+
+
 def _prefill_setup(wl, torch, g):
     from synth import device_normal
     dev = "cuda"
@@ -105,7 +132,7 @@ def _prefill_setup(wl, torch, g):
     cos = torch.empty((table_len, wl.rotary_dim // 2), dtype=torch.float32, device=dev)
     sin = torch.empty_like(cos)
     cfg = g.AttnConfig(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
-                       wl.qk_norm, wl.eps, qw, kw, 0.0, wl.softcap)
+                       wl.qk_norm, wl.eps, qw, kw, 0.0, wl.softcap, **_mask_cfg(wl, torch))
     out = torch.empty_like(q)
     kcache = k.clone()   # rows < n_cached: the cache as stored; the rest is rewritten each step
     return dict(q=q, k=k, v=v, qw=qw, kw=kw, pos=pos, kpos=kpos, cos=cos, sin=sin, cfg=cfg,
@@ -155,7 +182,8 @@ def run_decode(wl, steps, warmup, torch, g):
     spec = _rope_spec(g, wl)
     cos, sin = g.rope_tables(spec, wl.S)
     cfg = g.AttnConfig(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
-                       wl.qk_norm, wl.eps, x.get("qw"), x.get("kw"), 0.0, wl.softcap)
+                       wl.qk_norm, wl.eps, x.get("qw"), x.get("kw"), 0.0, wl.softcap,
+                       **_mask_cfg(wl, torch))
     ws = torch.empty(g.decode_workspace_bytes(cfg, wl.B, wl.S), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(x["q"])
     stream = torch.cuda.current_stream()
@@ -185,6 +213,8 @@ def cpu_baseline_prefill(wl, x, torch, budget_s=15.0):
     kw = x["kw"].float().cpu().numpy() if x["kw"] is not None else None
     pos = x["pos"].cpu().numpy()[None]
     kpos = x["kpos"].cpu().numpy()[None]
+    from synth import draw_sinks
+    sinks = draw_sinks(wl)
     t_total, nseq, ok, maxerr = 0.0, 0, True, 0.0
     for b in range(wl.B):
         q = x["q"][b:b + 1].float().cpu().numpy()
@@ -193,7 +223,8 @@ def cpu_baseline_prefill(wl, x, torch, budget_s=15.0):
         t = time.perf_counter()
         ref = oracle.attn_prefill(q, k, v, pos, kpos, inv_freq=inv, style=wl.style,
                                   n_cached=wl.n_cached, window=wl.window, q_norm_w=qw,
-                                  k_norm_w=kw, eps=wl.eps, softcap=wl.softcap)
+                                  k_norm_w=kw, eps=wl.eps, softcap=wl.softcap, sinks=sinks,
+                                  chunk=wl.chunk, chunk_lookback=wl.chunk_lookback)
         t_total += time.perf_counter() - t
         got = x["out"][b:b + 1].float().cpu().numpy()
         err = np.abs(got - ref)
@@ -202,7 +233,8 @@ def cpu_baseline_prefill(wl, x, torch, budget_s=15.0):
         nseq += 1
         if t_total >= budget_s:
             break
-    flops = 4 * nseq * wl.Hq * wl.D * allowed_pairs(wl.L, wl.S, wl.window, wl.n_cached)
+    flops = 4 * nseq * wl.Hq * wl.D * allowed_pairs(wl.L, wl.S, wl.window, wl.n_cached,
+                                                    wl.chunk, wl.chunk_lookback)
     return dict(value=flops / t_total / 1e12, unit="TFLOP/s", cores=_blas_threads(),
                 kind="oracle",
                 sample=f"{nseq} of {wl.B} sequences of {wl.name}, all rows and heads "
@@ -217,6 +249,8 @@ def cpu_baseline_decode(wl, x, torch, budget_s=15.0):
     inv = oracle.rope_inv_freq(wl.rotary_dim, wl.theta, wl.rope_kind, wl.factor,
                                wl.low_freq_factor, wl.high_freq_factor, wl.original_max_pos)
     eb = 2
+    from synth import draw_sinks
+    sinks = draw_sinks(wl)
     t_total, nbytes, ok, maxerr, nseq = 0.0, 0, True, 0.0, 0
     for b in range(wl.B):
         n = int(lens[b])
@@ -225,13 +259,14 @@ def cpu_baseline_decode(wl, x, torch, budget_s=15.0):
         qq = x["q"][b].float().cpu().numpy()
         t = time.perf_counter()
         ref = oracle.attn_decode_one(qq, kk, vv, n, inv_freq=inv, style=wl.style,
-                                     window=wl.window, softcap=wl.softcap)
+                                     window=wl.window, softcap=wl.softcap, sinks=sinks,
+                                     chunk=wl.chunk, chunk_lookback=wl.chunk_lookback)
         t_total += time.perf_counter() - t
         got = x["out"][b].float().cpu().numpy()
         err = np.abs(got - ref)
         maxerr = max(maxerr, float(err.max()))
         ok &= bool(np.all(err <= 2e-2 + 2e-2 * np.abs(ref)))
-        keys = min(n, wl.window) if wl.window else n
+        keys = decode_keys(wl, n)
         nbytes += keys * kv_bytes_per_token_per_layer(wl.Hkv, wl.D, eb)
         nseq += 1
         if t_total >= budget_s:
@@ -305,6 +340,7 @@ def main(argv=None):
                    "Hkv": wl.Hkv, "head_dim": wl.D, "rotary_dim": wl.rotary_dim,
                    "rope": wl.rope_kind, "theta": wl.theta, "qk_norm": wl.qk_norm,
                    "window": wl.window, "softcap": wl.softcap, "n_cached": wl.n_cached,
+                   "chunk": wl.chunk, "chunk_lookback": wl.chunk_lookback, "sinks": wl.sinks,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "prefill_stream_kernel",
                      "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,

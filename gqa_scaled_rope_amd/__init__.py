@@ -59,7 +59,8 @@ class _AttnCfg(ctypes.Structure):
                 ("table_len", ctypes.c_int32), ("qk_norm", ctypes.c_int32),
                 ("eps", ctypes.c_double), ("q_norm_w", ctypes.c_void_p),
                 ("k_norm_w", ctypes.c_void_p), ("scale", ctypes.c_double),
-                ("softcap", ctypes.c_double)]
+                ("softcap", ctypes.c_double), ("sinks", ctypes.c_void_p),
+                ("chunk_size", ctypes.c_int32), ("chunk_lookback", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -250,6 +251,9 @@ class AttnConfig:
     k_norm_w: Optional[object] = None
     scale: float = 0.0
     softcap: float = 0.0
+    sinks: Optional[object] = None      # device tensor [num_q_heads] fp32: learned sink logits
+    chunk_size: int = 0                 # chunked attention: chunk length in positions (0 = off)
+    chunk_lookback: int = 0             # chunks before the query's own that stay visible
 
     @property
     def torch_dtype(self):
@@ -277,10 +281,14 @@ class AttnConfig:
                 raise GQAError(1, "q_norm_w and k_norm_w are required when qk_norm is set")
             qw = _need(self.q_norm_w, "q_norm_w", (self.head_dim,), self.torch_dtype).value
             kw = _need(self.k_norm_w, "k_norm_w", (self.head_dim,), self.torch_dtype).value
+        sk = None
+        if self.sinks is not None:
+            sk = _need(self.sinks, "sinks", (self.num_q_heads,), torch.float32).value
         return _AttnCfg(GQA_BF16 if self.dtype == "bf16" else GQA_F32, self.head_dim,
                         self.num_q_heads, self.num_kv_heads, self.rotary_dim,
                         ROT_STYLES[self.rot_style], pc, ps, tl, int(bool(self.qk_norm)), self.eps,
-                        qw, kw, self.scale, self.softcap)
+                        qw, kw, self.scale, self.softcap, sk, int(self.chunk_size),
+                        int(self.chunk_lookback))
 
 
 def prep_keys(cfg: AttnConfig, k, key_positions, n_cached=0, k_out=None, stream=None):

@@ -1,7 +1,8 @@
 // bf16 split-KV single-token decode, head_dim 128, for gfx950.
 //
 // [Guide] section 3.3 (KVCache, layout [B, Hkv, Smax, D]) and section 3.7 (the decode step:
-// the new query sits after every cached key, so only the window can mask), with the query
+// the new query sits after every cached key, so only the window or chunks can mask: they set
+// the first slot read, and a learned sink enters the final log-sum-exp merge), with the query
 // normed and rotated at position lens-1 ([Models] "What differs": keys are cached already
 // rotated, so they are read as stored).
 //
@@ -166,6 +167,13 @@ struct Item {
   bool valid;
 };
 
+// First cache slot the query at position n - 1 may see: the window's and the chunk's bound
+// ([Models] "Sliding windows"; chunks as in [Ster]'s llama4_text and Rnj-1.5 paragraphs); slot j
+// holds position j.
+__device__ __forceinline__ int first_key(const AttnArgs& a, int n) {
+  return a.has_floor() ? (int)max<int64_t>(0, key_floor(a, (int64_t)n - 1)) : 0;
+}
+
 template <bool CAP>
 __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs da) {
   __shared__ SplitSmem sm;
@@ -177,7 +185,7 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
   // ---- plan: items of sequence i = Hkv * (splits of its window); exclusive prefix in LDS -------
   for (int i = tid; i < B; i += DT) {
     const int n = min(max(a.lens[i], 0), a.S);
-    const int start = a.window > 0 ? max(0, n - a.window) : 0;
+    const int start = first_key(a, n);
     sm.len[i] = n;
     sm.plan[i] = ((n - start + SPLIT - 1) / SPLIT) * Hkv;
   }
@@ -231,7 +239,7 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
     it.b = lo;
     it.g = r / nsp;
     it.sp = r - it.g * nsp;
-    const int start = a.window > 0 ? max(0, n - a.window) : 0;
+    const int start = first_key(a, n);
     const int ks = start + it.sp * SPLIT;
     const int ke = min(ks + SPLIT, n);
     it.ws = ks + w * SUB;
@@ -446,7 +454,7 @@ __global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs da) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int G = a.G, g = h / G, hs = h % G;
   const int n = min(max(a.lens[b], 0), a.S);
-  const int start = a.window > 0 ? max(0, n - a.window) : 0;
+  const int start = first_key(a, n);
   const int nsp = (n - start + SPLIT - 1) / SPLIT;
   const int64_t item0 = (((int64_t)b * a.Hkv + g) * da.nsplit) * G + hs;
   const float* ml = da.part_ml;
@@ -486,7 +494,9 @@ __global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs da) {
     acc0 += sc * po[(int64_t)s * step];
   }
   const float acc = (acc0 + acc1) + (acc2 + acc3);
-  const float r = lt > 0.f ? acc / lt : 0.f;
+  // a learned sink joins the denominator only (log2 units, relative to M)
+  const float lden = (a.sinks != nullptr && lt > 0.f) ? lt + fast_exp2(a.sinks[h] * kLog2e - M) : lt;
+  const float r = lt > 0.f ? acc / lden : 0.f;
   uint16_t* orow = (uint16_t*)a.out + (int64_t)b * a.o_b + (int64_t)h * a.o_h;
   orow[d] = f32_to_bf16(r);
 }

@@ -6,10 +6,11 @@
 //
 // Per row: the query is RMS-normed ([Guide] section 3.2) and rotated at its position ([Guide]
 // section 4; [Models] "Serving it" for adjacent pairs), then scaled.  Keys in the band allowed
-// by the causal/window mask ([Models] "Sliding windows") are visited 64 at a time, one key per
-// lane: new keys (index >= n_cached) are normed and rotated on the fly, cached keys are used as
-// stored.  An online softmax (running max and sum, rescaled when the max grows) accumulates the
-// values, one feature per lane.
+// by the causal/window/chunk mask ([Models] "Sliding windows"; chunks as in [Ster]'s llama4_text
+// paragraph) are visited 64 at a time, one key per lane: new keys (index >= n_cached) are normed
+// and rotated on the fly, cached keys are used as stored.  An online softmax (running max and
+// sum, rescaled when the max grows) accumulates the values, one feature per lane; a learned sink
+// adds its term to the final sum.
 #include "launch.hpp"
 
 namespace gqa {
@@ -94,7 +95,9 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
 
   // ---- band of allowed keys ----
   const int hi = lower_bound_pos(kp, S, qp + 1);
-  const int lo = a.window > 0 ? lower_bound_pos(kp, S, qp - a.window + 1) : 0;
+  const bool floor_on = a.has_floor();
+  const int64_t kfl = key_floor(a, qp);
+  const int lo = floor_on ? lower_bound_pos(kp, S, kfl) : 0;
 
   float m = kNegBig, l = 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
     int64_t kpj = 0;
     if (valid) {
       kpj = kp ? (int64_t)kp[j] : (int64_t)j;
-      valid = kpj <= qp && (a.window == 0 || qp - kpj <= a.window - 1);
+      valid = kpj <= qp && (!floor_on || kpj >= kfl);
     }
     float s = -INFINITY;
     if (valid) {
@@ -162,7 +165,9 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
     __syncthreads();
     m = m_new;
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  // a learned sink joins the denominator only ([Ster] gpt_oss paragraph)
+  const float lt = (a.sinks != nullptr && l > 0.f) ? l + expf(a.sinks[h] - m) : l;
+  const float inv = l > 0.f ? 1.f / lt : 0.f;
   T* orow = (T*)a.out + b * a.o_b + i * a.o_i + h * a.o_h;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {

@@ -22,9 +22,10 @@
 //    for both the row reads of K and the transposing reads of V); the next tile's global loads
 //    are in flight while the current tile is computed.  New keys (index >= n_cached) are RMS-normed
 //    and rotated in registers between the global load and the LDS store.
-//  * Only key tiles that intersect the causal/window band of the workgroup's queries are visited
-//    ([Models] "Sliding windows": the loop starts at the first block inside the oldest query's
-//    window); only tiles that straddle the band's edge evaluate the mask per element.
+//  * Only key tiles that intersect the causal/window/chunk band of the workgroup's queries are
+//    visited ([Models] "Sliding windows": the loop starts at the first block the oldest query may
+//    see, by window or by chunk); only tiles that straddle the band's edge evaluate the mask per
+//    element.  A learned sink ([Ster] gpt_oss paragraph) enters the final denominator only.
 #include "launch.hpp"
 
 namespace gqa {
@@ -320,7 +321,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(AttnArgs a, int nqb
   }
   const int32_t* kpos_b = a.kpos + (int64_t)cx.b * a.kpos_b;
   const int j_hi = lower_bound_pos(kpos_b, a.S, qmax + 1);
-  const int j_lo = a.window > 0 ? min(lower_bound_pos(kpos_b, a.S, qmin - a.window + 1), j_hi) : 0;
+  const int j_lo = a.has_floor() ? min(lower_bound_pos(kpos_b, a.S, key_floor(a, qmin)), j_hi) : 0;
+  // smallest key position this lane's query may see (window, chunks)
+  const int64_t qfl = key_floor(a, qp);
   const int n_tiles = (j_hi - j_lo + BN - 1) / BN;
 
 
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(AttnArgs a, int nqb
     const int32_t kfirst = sm.kpos[buf][0];
     const int32_t klast = sm.kpos[buf][BN - 1];
     const bool full = (jt + BN <= j_hi) && ((int64_t)klast <= qmin) &&
-                      (a.window == 0 || qmax - (int64_t)kfirst <= a.window - 1);
+                      (!a.has_floor() || (int64_t)kfirst >= key_floor(a, qmax));
     const uint16_t* ks = sm.k[buf];
     const uint16_t* vs = sm.v[buf];
     const int gi = lane >> 4, s16 = lane & 15;
@@ -385,7 +388,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(AttnArgs a, int nqb
         for (int r = 0; r < 16; ++r) {
           const int kk = kb * 32 + 8 * (r >> 2) + 4 * hg + (r & 3);
           const int64_t kp = sm.kpos[buf][kk];
-          const bool ok = qvalid && kp <= qp && (a.window == 0 || qp - kp <= a.window - 1);
+          const bool ok = qvalid && kp <= qp && kp >= qfl;
           if (!ok) sacc[r] = -INFINITY;
         }
       }
@@ -445,7 +448,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(AttnArgs a, int nqb
 
   // ---- epilogue: O / l, round to bf16, store row (b, qi, qh) ----
   const float ltot = lsum + swap_halves(lsum);
-  const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+  // a learned sink joins the denominator only (log2 units, relative to the running max)
+  const float lden =
+      (a.sinks != nullptr && ltot > 0.f) ? ltot + fast_exp2(a.sinks[qh] * kLog2e - m) : ltot;
+  const float inv = ltot > 0.f ? 1.0f / lden : 0.f;
   if (qvalid) {
     uint16_t* orow = (uint16_t*)a.out + (int64_t)cx.b * a.o_b + (int64_t)qi * a.o_i +
                      (int64_t)qh * a.o_h;

@@ -334,8 +334,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     if (w == 0) pbuf<buf>()[lane] = kp_pend_ok ? (int32_t)kp_pend : INT32_MAX;
   };
 
-  // Without a window the first tile starts at key 0: start its loads before the query prep.
-  if (a.window == 0) issue_tile(0, std::integral_constant<int, 0>());
+  // Without a window or chunks the first tile starts at key 0: start its loads before the query
+  // prep.
+  if (!a.has_floor()) issue_tile(0, std::integral_constant<int, 0>());
 
   // ---- band guesses: with consecutive key positions the band edges are known from the query
   // positions; the two keys around each guess are loaded now (clamped indices) and checked below
@@ -347,11 +348,17 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   }
   // wave-uniform from here on: scalar registers
   const int64_t qmin = __builtin_amdgcn_readfirstlane(qmn), qmax = __builtin_amdgcn_readfirstlane(qmx);
-  const int64_t x_hi = qmax + 1, x_lo = qmin - a.window + 1;
+  const int64_t x_hi = qmax + 1, x_lo = key_floor(a, qmin);
+  // a tile needs no mask when every query may see its first key (and its last is causal for all)
+  const int32_t floor_max = (int32_t)max<int64_t>(key_floor(a, qmax), INT32_MIN);
   const int g_hi = (int)min<int64_t>(max<int64_t>(x_hi - kp0, 0), a.S);
   const int g_lo = (int)min<int64_t>(max<int64_t>(x_lo - kp0, 0), a.S);
   const int32_t hi_l = kpos_b[max(g_hi - 1, 0)], hi_r = kpos_b[min(g_hi, a.S - 1)];
   const int32_t lo_l = kpos_b[max(g_lo - 1, 0)], lo_r = kpos_b[min(g_lo, a.S - 1)];
+  // smallest key position the row may see (window, chunks); INT32_MAX for rows past the end
+  const int32_t qlo32 = !qvalid ? INT32_MAX
+                        : a.has_floor() ? (int32_t)max<int64_t>(key_floor(a, qp), INT32_MIN)
+                                        : INT32_MIN;
 
   // ---- query prep, shared by the workgroup: 16 lanes per query row, 8 features per lane (32 rows
   // per pass, 8 passes, in two batches whose loads all go out before their arithmetic).  Each
@@ -444,13 +451,13 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   __syncthreads();  // staging complete
   bf16x8 qop[8];  // read from the staging area just before the loop
 
-  // ---- band: first key past the newest query, first key inside the oldest query's window ----
+  // ---- band: first key past the newest query, first key the oldest query may see ----
   // (a guess is right when the key before it is below the target and the key at it is not; if
   // positions are not consecutive the wavefront searches)
   const bool ok_hi = (g_hi == 0 || (int64_t)hi_l < x_hi) && (g_hi == a.S || (int64_t)hi_r >= x_hi);
   const bool ok_lo = (g_lo == 0 || (int64_t)lo_l < x_lo) && (g_lo == a.S || (int64_t)lo_r >= x_lo);
   int j_hi = ok_hi ? g_hi : wave_lower_bound(kpos_b, a.S, x_hi);
-  int j_lo = a.window == 0 ? 0 : ok_lo ? g_lo : wave_lower_bound(kpos_b, a.S, x_lo);
+  int j_lo = !a.has_floor() ? 0 : ok_lo ? g_lo : wave_lower_bound(kpos_b, a.S, x_lo);
   j_lo = min(j_lo, j_hi);
   const int n_tiles = (j_hi - j_lo + BN - 1) / BN;
 
@@ -488,10 +495,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   }
   // mask bounds in int32: allowed <=> qlo32 <= key position <= qp32 (key positions past the last
   // key read INT32_MAX, so the ragged tail fails the first test)
+  // (qlo32, the window/chunk bound, is computed once the band loads are out: earlier it would
+  // wait for this row's position before any other load is issued, later it costs registers)
   const int32_t qp32 = qvalid ? (int32_t)qp : INT32_MIN;
-  const int32_t qlo32 = !qvalid ? INT32_MAX
-                        : a.window > 0 ? (int32_t)max<int64_t>(qp - a.window + 1, INT32_MIN)
-                                       : INT32_MIN;
 
   // S^T - m_eff for the 32 keys of half kb of a buffered tile
   auto qk = [&](auto bufc, auto kbc) {
@@ -535,7 +541,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     const int32_t kfirst = kpt[0];
     const int32_t klast = kpt[BN - 1];
     const bool full = (jt + BN <= j_hi) && ((int64_t)klast <= qmin) &&
-                      (a.window == 0 || qmax - (int64_t)kfirst <= a.window - 1);
+                      (kfirst >= floor_max);
     f32x16 sc = s_cur;
 
     // ---- soft-cap, mask, running max ----
@@ -625,7 +631,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
       }
   };
 
-  if (a.window > 0 && n_tiles > 0) issue_tile(j_lo, std::integral_constant<int, 0>());
+  if (a.has_floor() && n_tiles > 0) issue_tile(j_lo, std::integral_constant<int, 0>());
   // this lane's query operands from the staging rows (chunk 2s + hg of row 32w + ql)
   {
     const int rr = ((w & 1) << 5) + ql;
@@ -654,7 +660,11 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   }
 
   const float ltot = lsum + swap_halves(lsum);
-  const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+  // a learned sink joins the denominator only (log2 units, relative to the running max m, which
+  // is set whenever ltot > 0)
+  const float lden =
+      (a.sinks != nullptr && ltot > 0.f) ? ltot + fast_exp2(a.sinks[qh] * kLog2e - m) : ltot;
+  const float inv = ltot > 0.f ? 1.0f / lden : 0.f;
   if (qvalid) {
     uint16_t* orow = (uint16_t*)a.out + (int64_t)b * a.o_b + (int64_t)qi * a.o_i +
                      (int64_t)qh * a.o_h;

@@ -82,7 +82,52 @@ struct AttnArgs {
   int32_t table_len;
   float scale;               // score scale (natural units)
   float softcap;             // 0 = off
+  const float* sinks;        // [Hq] logits in scaled-score units; null = none
+  int32_t chunk;             // chunk length in positions; 0 = no chunking
+  int32_t chunk_lb;          // visible chunks before the query's own
+  uint32_t chunk_m_lo, chunk_m_hi;  // ceil(2^64 / chunk) for chunk >= 2 (set by set_chunk)
+
+  // true when some key position below the query's can be masked (window or chunks)
+  __host__ __device__ bool has_floor() const { return window > 0 || chunk > 0; }
 };
+
+// floor(u / chunk) for any 32-bit u, by multiplication: with M = ceil(2^64 / chunk) = 2^64/chunk + e
+// (0 <= e < 1), u*M / 2^64 exceeds u/chunk by less than 2^-32, and the fraction of u/chunk is at
+// most 1 - 1/chunk, so the floor is exact for chunk < 2^32.  The 96-bit product is formed from the
+// two 32-bit halves of M.
+__host__ __device__ inline uint32_t chunk_div(const AttnArgs& a, uint32_t u) {
+  if (a.chunk == 1) return u;
+  const uint64_t t = (uint64_t)u * a.chunk_m_hi + (((uint64_t)u * a.chunk_m_lo) >> 32);
+  return (uint32_t)(t >> 32);
+}
+
+// Sets the chunk fields (chunk 0: off).
+inline void set_chunk(AttnArgs& a, int32_t chunk, int32_t lookback) {
+  a.chunk = chunk > 0 ? chunk : 0;
+  a.chunk_lb = chunk > 0 ? lookback : 0;
+  const uint64_t m = chunk >= 2 ? UINT64_MAX / (uint64_t)chunk + 1 : 0;
+  a.chunk_m_lo = (uint32_t)m;
+  a.chunk_m_hi = (uint32_t)(m >> 32);
+}
+
+// Smallest key position a query at position p (an int32 value) may see ([Models] "Sliding windows": p - w + 1;
+// chunked attention: the first position of the chunk chunk_lb chunks before p's own, chunks
+// counted by floor division).  Nondecreasing in p, so over a block of queries the smallest
+// floor is the first query's and the largest the last one's.  Without window and chunks the
+// result is far below every int32 position.
+__host__ __device__ inline int64_t key_floor(const AttnArgs& a, int64_t p) {
+  int64_t lo = -((int64_t)1 << 40);
+  if (a.window > 0) lo = p - a.window + 1;
+  if (a.chunk > 0) {
+    // floor(p / chunk) for an int32 p: |p| (+ chunk - 1 when negative) stays below 2^32
+    const int32_t p32 = (int32_t)p;
+    const int64_t idx = p32 >= 0 ? (int64_t)chunk_div(a, (uint32_t)p32)
+                                 : -(int64_t)chunk_div(a, 0u - (uint32_t)p32 + (uint32_t)(a.chunk - 1));
+    const int64_t first = (idx - a.chunk_lb) * (int64_t)a.chunk;
+    lo = lo > first ? lo : first;
+  }
+  return lo;
+}
 
 
 }  // namespace gqa

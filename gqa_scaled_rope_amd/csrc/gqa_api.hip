@@ -216,6 +216,10 @@ gqa_status check_cfg(const gqa_attn_cfg* c) {
   if (!finite_nonneg(c->scale)) return fail(GQA_E_VALUE, "scale must be finite and >= 0, got %g", c->scale);
   if (!finite_nonneg(c->softcap))
     return fail(GQA_E_VALUE, "softcap must be finite and >= 0, got %g", c->softcap);
+  if (((uintptr_t)c->sinks & 3u) != 0) return fail(GQA_E_VALUE, "sinks must be 4-byte aligned");
+  if (c->chunk_size < 0 || c->chunk_lookback < 0)
+    return fail(GQA_E_SHAPE, "chunk_size and chunk_lookback must be >= 0, got %d, %d",
+                c->chunk_size, c->chunk_lookback);
   return ok();
 }
 
@@ -236,6 +240,8 @@ gqa::AttnArgs base_args(const gqa_attn_cfg* c) {
   a.table_len = c->table_len;
   a.scale = (float)(c->scale > 0.0 ? c->scale : 1.0 / std::sqrt((double)c->head_dim));
   a.softcap = (float)c->softcap;
+  a.sinks = c->sinks;
+  gqa::set_chunk(a, c->chunk_size, c->chunk_lookback);
   return a;
 }
 

@@ -111,6 +111,18 @@ typedef struct gqa_attn_cfg {
   const void* k_norm_w;       /* device [D] gain in dtype (required when qk_norm) */
   double scale;               /* score scale; 0 selects 1/sqrt(head_dim) ([Guide] section 3.4) */
   double softcap;             /* > 0: scores become softcap * tanh(score / softcap); 0: off */
+  /* Learned attention sinks ([Ster] gpt_oss paragraph): device [num_q_heads] fp32, one logit per
+   * query head that joins every softmax of that head with no value, so its share of the weight is
+   * dropped.  The logit is in the units of the scaled scores and is not soft-capped.  Null: no
+   * sinks.  Read-only during the call; 4-byte aligned. */
+  const float* sinks;
+  /* Chunked attention ([Ster] llama4_text and Rnj-1.5 paragraphs): positions fall in chunks of
+   * chunk_size (chunk c = positions c*chunk_size .. (c+1)*chunk_size - 1, negative positions
+   * included); a query sees the keys of its own chunk and of the chunk_lookback chunks before it
+   * (Llama 4: 0, Rnj-1.5: 1), still causally and still inside the window when one is given.
+   * chunk_size 0: no chunking.  Both >= 0. */
+  int32_t chunk_size;
+  int32_t chunk_lookback;
 } gqa_attn_cfg;
 
 /* Build cos/sin tables for positions 0 .. table_len-1 ([Models] "Scaled RoPE", rope_tables):

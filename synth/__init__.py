@@ -44,6 +44,9 @@ class Workload:
     lens_lo: int = 0          # decode: cache lengths uniform on [lens_lo, lens_hi]
     lens_hi: int = 0
     seed: int = 0
+    chunk: int = 0            # chunked attention: chunk length in positions (0 = off)
+    chunk_lookback: int = 0   # chunks before the query's own that stay visible
+    sinks: bool = False       # one learned sink logit per query head (drawn by draw_sinks)
 
     @property
     def G(self):
@@ -81,6 +84,19 @@ WORKLOADS = {
                                           L=512, S=4096, Hq=24, Hkv=8, D=128, rotary_dim=64,
                                           style="interleaved", theta=1e4, window=0, softcap=50.0,
                                           n_cached=3584, seed=5),
+    # Widened rows, measured beside the five above.  Learned sinks with a 128-key sliding window
+    # (the gpt-oss layer kind; its head_dim of 64 is replaced by 128, the width the MFMA kernels
+    # take), and Llama 4's chunked attention (chunks of 8192 positions, each query in its own).
+    "sinks_swa128_prefill_bf16": Workload("sinks_swa128_prefill_bf16", "prefill", "bf16", B=4,
+                                          L=4096, S=4096, Hq=64, Hkv=8, D=128, rotary_dim=128,
+                                          theta=1.5e5, window=128, sinks=True, seed=6),
+    "llama4_chunked_prefill_bf16": Workload("llama4_chunked_prefill_bf16", "prefill", "bf16",
+                                            B=1, L=16384, S=16384, Hq=40, Hkv=8, D=128,
+                                            rotary_dim=128, theta=5e5, chunk=8192, seed=7),
+    "sinks_chunk_decode_bf16": Workload("sinks_chunk_decode_bf16", "decode", "bf16", B=64, L=1,
+                                        S=32768, Hq=32, Hkv=8, D=128, rotary_dim=128, theta=5e5,
+                                        chunk=8192, sinks=True, lens_lo=1024, lens_hi=32768,
+                                        seed=8),
 }
 
 
@@ -162,6 +178,20 @@ def decode_cache_seq(wl: Workload, b, n, seed=None):
     k = rng.standard_normal((wl.Hkv, n, wl.D), dtype=np.float32)
     v = rng.standard_normal((wl.Hkv, n, wl.D), dtype=np.float32)
     return round_to(k, wl.dtype), round_to(v, wl.dtype)
+
+
+def draw_sinks(wl: Workload, seed=None):
+    """Sink logits [Hq] float32 (None unless wl.sinks): N(0, 3^2) from their own seeded stream,
+    with head 0 at +8 (the sink takes most of the weight) and the last head at -30 (none)."""
+    if not wl.sinks:
+        return None
+    seed = wl.seed if seed is None else seed
+    rng = np.random.default_rng([seed, 77])
+    s = (3.0 * rng.standard_normal(wl.Hq)).astype(np.float32)
+    s[0] = 8.0
+    if wl.Hq > 1:
+        s[-1] = -30.0
+    return s
 
 
 def rope_params(wl: Workload):

@@ -37,7 +37,7 @@ def test_version():
 def _cfg(**kw):
     base = dict(dtype=1, head_dim=128, num_q_heads=32, num_kv_heads=8, rotary_dim=0, rot_style=0,
                 cos_table=None, sin_table=None, table_len=0, qk_norm=0, eps=1e-6, q_norm_w=None,
-                k_norm_w=None, scale=0.0, softcap=0.0)
+                k_norm_w=None, scale=0.0, softcap=0.0, sinks=None, chunk_size=0, chunk_lookback=0)
     base.update(kw)
     c = g._AttnCfg()
     for k, v in base.items():
@@ -70,6 +70,9 @@ def _prefill(c, B=1, L=4, S=4, n_cached=0, window=0, q=FAKE, k=FAKE, v=FAKE, pos
     (dict(qk_norm=1, q_norm_w=FAKE, k_norm_w=FAKE, eps=-1.0), 7, "eps"),
     (dict(scale=-1.0), 7, "scale"),
     (dict(softcap=float("nan")), 7, "softcap"),
+    (dict(sinks=FAKE + 2), 7, "sinks"),
+    (dict(chunk_size=-1), 2, "chunk_size"),
+    (dict(chunk_size=64, chunk_lookback=-1), 2, "chunk_lookback"),
 ])
 def test_prefill_rejects_bad_cfg(kw, status, msg):
     st = _prefill(_cfg(**kw))
@@ -247,8 +250,57 @@ def test_prefill_flop_model():
         qp = np.arange(S - L, S) if nc else np.arange(L)
         brute = int(oracle.allowed_mask(qp, np.arange(S), w).sum())
         assert bench.allowed_pairs(L, S, w, nc) == brute
+    for L, S, w, nc, c, lb in ((64, 64, 0, 0, 8, 0), (64, 64, 0, 0, 7, 1), (16, 64, 5, 48, 6, 2),
+                               (64, 64, 0, 0, 1, 0), (64, 64, 0, 0, 1000, 0)):
+        qp = np.arange(S - L, S) if nc else np.arange(L)
+        brute = int(oracle.allowed_mask(qp, np.arange(S), w, c, lb).sum())
+        assert bench.allowed_pairs(L, S, w, nc, c, lb) == brute
+    assert bench.allowed_pairs(16384, 16384, 0, 0, 8192, 0) == 2 * 8192 * 8193 // 2
     assert bench.allowed_pairs(2048, 2048, 0, 0) == 2098176
     assert bench.allowed_pairs(8192, 8192, 4096, 0) == 25167872
     assert bench.allowed_pairs(512, 4096, 4096, 3584) == 1966336
     assert bench.allowed_pairs(512, 4096, 0, 3584) == 1966336
     assert math.isclose(4 * 4 * 32 * 128 * 2098176, 1.3751e11, rel_tol=1e-4)
+
+
+def test_decode_key_count_model():
+    # rows a decode query reads = allowed keys of the last row, by the oracle's mask
+    import bench
+    from synth import WORKLOADS
+    for kw in (dict(window=0), dict(window=100), dict(chunk=64), dict(chunk=64, chunk_lookback=1),
+               dict(chunk=50, window=70)):
+        wl = WORKLOADS["llama31_decode_bf16"].with_(**kw)
+        for n in (1, 63, 64, 65, 129, 1000):
+            want = int(oracle.allowed_mask([n - 1], np.arange(n), wl.window, wl.chunk,
+                                           wl.chunk_lookback).sum())
+            assert bench.decode_keys(wl, n) == want
+
+
+def test_c_struct_layout_matches_ctypes(tmp_path):
+    # the ctypes mirrors of the two public structs have the header's sizes and offsets
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    fields = {"gqa_attn_cfg": g._AttnCfg, "gqa_rope_params": g._RopeParams}
+    lines = []
+    for cname, py in fields.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    src = tmp_path / "lay.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "gqa_rope.h"\n'
+                   "int main(void) {" + "".join(lines) + "return 0;}\n")
+    exe = tmp_path / "lay"
+    r = subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(root, "include"),
+                        "-I", "/opt/rocm/include", str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("header needs the HIP runtime headers: " + r.stderr[-200:])
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    for line in filter(None, out):
+        cname, what, val = line.split()
+        py = fields[cname]
+        want = ctypes.sizeof(py) if what == "size" else getattr(py, what).offset
+        assert int(val) == want, line

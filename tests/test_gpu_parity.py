@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synth import (WORKLOADS, decode_cache_seq, decode_device_inputs, decode_lens_q,
+from synth import (WORKLOADS, decode_cache_seq, decode_device_inputs, decode_lens_q, draw_sinks,
                    prefill_inputs)
 
 pytestmark = pytest.mark.gpu
@@ -58,6 +58,18 @@ def policy(request):
     PATH["path"] = "stream"
 
 
+def mask_kw(wl):
+    """Sinks and chunking of a workload, as oracle keyword arguments."""
+    return dict(sinks=draw_sinks(wl), chunk=wl.chunk, chunk_lookback=wl.chunk_lookback)
+
+
+def cfg_extra(wl):
+    """Sinks and chunking of a workload, as AttnConfig fields."""
+    sk = draw_sinks(wl)
+    return dict(sinks=None if sk is None else dev(sk, torch.float32), chunk_size=wl.chunk,
+                chunk_lookback=wl.chunk_lookback)
+
+
 def gpu_prefill(wl, x, table_len=None, shared_pos=False):
     dt = tdt(wl)
     tl = table_len or int(max(x["positions"].max(), x["key_positions"].max())) + 1
@@ -65,7 +77,8 @@ def gpu_prefill(wl, x, table_len=None, shared_pos=False):
     cfg = g.AttnConfig(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
                        wl.qk_norm, wl.eps,
                        dev(x["q_norm_w"], dt) if wl.qk_norm else None,
-                       dev(x["k_norm_w"], dt) if wl.qk_norm else None, 0.0, wl.softcap)
+                       dev(x["k_norm_w"], dt) if wl.qk_norm else None, 0.0, wl.softcap,
+                       **cfg_extra(wl))
     pos = x["positions"][0] if shared_pos else x["positions"]
     kpos = x["key_positions"][0] if shared_pos else x["key_positions"]
     ws = None if PATH["path"] == "fused" else "auto"
@@ -80,7 +93,8 @@ def ref_prefill(wl, x, **kw):
     return oracle.attn_prefill(x["q"], x["k"], x["v"], x["positions"], x["key_positions"],
                                inv_freq=inv_freq(wl), style=wl.style, n_cached=wl.n_cached,
                                window=wl.window, q_norm_w=x.get("q_norm_w"),
-                               k_norm_w=x.get("k_norm_w"), eps=wl.eps, softcap=wl.softcap, **kw)
+                               k_norm_w=x.get("k_norm_w"), eps=wl.eps, softcap=wl.softcap,
+                               **{**mask_kw(wl), **kw})
 
 
 def check(got, ref, dtype="bf16", head_axis=2):
@@ -138,6 +152,14 @@ VARIANTS = {
     "ragged_L257": BASE.with_(L=257, S=257),
     "single_token": BASE.with_(L=1, S=1),
     "chunk_L1": BASE.with_(L=1, S=300, n_cached=299, qk_norm=False),
+    # learned sinks ([Ster] gpt_oss) and chunked attention ([Ster] llama4_text, Rnj-1.5)
+    "sinks": BASE.with_(sinks=True),
+    "sinks_interleaved_cap_cached": BASE.with_(Hq=6, Hkv=2, rotary_dim=64, style="interleaved",
+                                               softcap=50.0, qk_norm=False, n_cached=180,
+                                               theta=1e4, sinks=True),
+    "chunk64_llama4": BASE.with_(chunk=64),
+    "chunk50_lookback1_sinks": BASE.with_(qk_norm=False, chunk=50, chunk_lookback=1, sinks=True),
+    "chunk8_lookback2_window20": BASE.with_(qk_norm=False, chunk=8, chunk_lookback=2, window=20),
 }
 
 
@@ -198,19 +220,25 @@ def test_prefill_no_keys_rows_are_zero():
     assert np.all(ref == 0) and np.all(got == 0)
 
 
-@pytest.mark.parametrize("window,n_cached,shift", [(0, 0, 0), (1, 0, 0), (5, 0, 0), (64, 0, 3),
-                                                   (100, 120, 0), (0, 200, 5), (129, 0, 0)])
-def test_mask_probe_bitexact(window, n_cached, shift, policy):
+@pytest.mark.parametrize("window,n_cached,shift,chunk,lookback", [
+    (0, 0, 0, 0, 0), (1, 0, 0, 0, 0), (5, 0, 0, 0, 0), (64, 0, 3, 0, 0), (100, 120, 0, 0, 0),
+    (0, 200, 5, 0, 0), (129, 0, 0, 0, 0),
+    # chunked attention: own chunk (Llama 4), one chunk of lookback (Rnj-1.5), tile-aligned and
+    # not, with a window, chunk 1, and positions below zero (floor chunks)
+    (0, 0, 0, 64, 0), (0, 0, 0, 50, 1), (0, 120, 7, 33, 2), (40, 0, 0, 32, 1), (0, 0, 0, 1, 0),
+    (0, 0, -150, 48, 0), (0, 0, -301, 7, 1), (0, 0, 0, 1 << 30, 0),
+])
+def test_mask_probe_bitexact(window, n_cached, shift, chunk, lookback, policy):
     wl = BASE.with_(qk_norm=False, rotary_dim=0, window=window, n_cached=n_cached, L=300 - n_cached,
-                    S=300)
-    say("mask probe", window, n_cached, shift, "policy", policy)
+                    S=300, chunk=chunk, chunk_lookback=lookback)
+    say("mask probe", window, n_cached, shift, chunk, lookback, "policy", policy)
     x = prefill_inputs(wl, seed=12)
     x["q"][:] = 0.0
     for b in range(wl.B):
         x["key_positions"][b] += shift * b
         x["positions"][b] += shift * b
-    allowed = [oracle.allowed_mask(x["positions"][b], x["key_positions"][b], window)
-               for b in range(wl.B)]
+    allowed = [oracle.allowed_mask(x["positions"][b], x["key_positions"][b], window, wl.chunk,
+                                   wl.chunk_lookback) for b in range(wl.B)]
     for blk in range(0, wl.S, wl.D):
         v = np.zeros_like(x["v"])
         n = min(wl.D, wl.S - blk)
@@ -232,7 +260,7 @@ def gpu_decode(wl, q, kc, vc, lens, qw=None):
     cos, sin = g.rope_tables(spec(wl), kc.shape[2]) if wl.rotary_dim else (None, None)
     cfg = g.AttnConfig(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
                        wl.qk_norm, wl.eps, dev(qw, dt) if wl.qk_norm else None,
-                       dev(qw, dt) if wl.qk_norm else None, 0.0, wl.softcap)
+                       dev(qw, dt) if wl.qk_norm else None, 0.0, wl.softcap, **cfg_extra(wl))
     out = g.attn_decode(cfg, dev(q, dt), dev(kc, dt), dev(vc, dt), dev(lens, torch.int32),
                         wl.window)
     torch.cuda.synchronize()
@@ -249,6 +277,10 @@ DEC_VARIANTS = {
     "G3": DEC.with_(Hq=24, Hkv=8),
     "G16": DEC.with_(Hq=32, Hkv=2),
     "half32": DEC.with_(rotary_dim=32),
+    "sinks": DEC.with_(sinks=True),
+    "chunk1000_lookback1": DEC.with_(chunk=1000, chunk_lookback=1),
+    "chunk2048_window1500_sinks": DEC.with_(chunk=2048, window=1500, sinks=True),
+    "chunk256_G16_sinks": DEC.with_(Hq=32, Hkv=2, chunk=256, sinks=True),
 }
 
 
@@ -269,7 +301,7 @@ def test_decode_variants(name, policy):
     got = gpu_decode(wl, q, kc, vc, lens, qw)
     ref = oracle.attn_decode(q, np.nan_to_num(kc), np.nan_to_num(vc), lens, inv_freq=inv_freq(wl),
                              style=wl.style, window=wl.window, q_norm_w=qw, eps=wl.eps,
-                             softcap=wl.softcap)
+                             softcap=wl.softcap, **mask_kw(wl))
     check(got, ref, head_axis=1)
 
 
@@ -305,6 +337,8 @@ def test_decode_equals_last_prefill_row():
     ("mistral_swa_prefill_bf16", [1], [0, 4094, 4095, 4096, 4097, 6000, 8191]),
     ("chunked_prefill_bf16_w4096", [0, 7], [0, 1, 255, 256, 511]),
     ("chunked_prefill_bf16_full", [5], [0, 300, 511]),
+    ("sinks_swa128_prefill_bf16", [0, 3], [0, 127, 128, 129, 2000, 4095]),
+    ("llama4_chunked_prefill_bf16", [0], [0, 8191, 8192, 8193, 16383]),
 ])
 @pytest.mark.parametrize("path", ["stream", "fused"])
 def test_full_size_prefill_sampled(name, batches, rows, path):
@@ -328,13 +362,15 @@ def test_chunked_window4096_equals_full_bitwise():
                                   gpu_prefill(b, x, shared_pos=True))
 
 
-def test_full_size_decode_sampled():
-    wl = WORKLOADS["llama31_decode_bf16"]
+@pytest.mark.parametrize("name", ["llama31_decode_bf16", "sinks_chunk_decode_bf16"])
+def test_full_size_decode_sampled(name):
+    wl = WORKLOADS[name]
     say("full size decode", wl.name)
     x = decode_device_inputs(wl)
     cos, sin = g.rope_tables(spec(wl), wl.S)
-    cfg = g.AttnConfig("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin)
-    out = g.attn_decode(cfg, x["q"], x["k"], x["v"], x["lens"], 0)
+    cfg = g.AttnConfig("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
+                       **cfg_extra(wl))
+    out = g.attn_decode(cfg, x["q"], x["k"], x["v"], x["lens"], wl.window)
     torch.cuda.synchronize()
     lens = x["lens"].cpu().numpy()
     got = out.float().cpu().numpy()
@@ -344,7 +380,8 @@ def test_full_size_decode_sampled():
         n = int(lens[b])
         ref = oracle.attn_decode_one(x["q"][b].float().cpu().numpy(),
                                      x["k"][b, :, :n].float().cpu().numpy(),
-                                     x["v"][b, :, :n].float().cpu().numpy(), n, inv_freq=inv)
+                                     x["v"][b, :, :n].float().cpu().numpy(), n, inv_freq=inv,
+                                     window=wl.window, **mask_kw(wl))
         check(got[b][None], ref[None], head_axis=1)
 
 
