@@ -4,8 +4,9 @@
 // Two launches:
 //  1. k_prep_kernel: every NEW key row (index >= n_cached) is RMS-normed and rotated once
 //     ([Models] "What differs": q/k norm then rotation; [Guide] section 3.2 and section 4) and
-//     written, rounded to bf16, to the workspace [B, S - n_cached, Hkv, D].  Cached rows are used
-//     as stored and are not copied.  This is the cache-append step of the page's flow (rotate,
+//     written, rounded to bf16, to the workspace; the workspace also holds the last 63 cached rows
+//     (copied as stored) so that every key tile reads a single source.  Other cached rows are
+//     used in place.  This is the cache-append step of the page's flow (rotate,
 //     then cache.update) and costs one read and one write of the new keys, instead of redoing the
 //     norm and rotation each time a key tile is revisited by another query block.
 //  2. prefill_stream_kernel: the attention proper.  Same tiling and math as the fused kernel
@@ -31,10 +32,41 @@ constexpr int BN = 64;
 constexpr int TILE_ELEMS = BN * HD;
 constexpr float kRescaleThreshold = 8.0f;
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit dwords, range checked
+
 constexpr int kXcds = 8;               // MI355X: 8 accelerator complex dies, one L2 each
 
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor as four words (base, stride 0, num_records, flags) for tile_dma16.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, int nrec) {
+  const uint64_t p = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(nrec);
+  r[3] = kBufFlags;
+  return r;
+}
+
+// One HBM -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds: lane l's bytes land at
+// dst + 16 l).  Written as assembly on purpose: the compiler's wait-count pass cannot tell these
+// asynchronous LDS writes apart from the reads of the other tile buffers and would make the
+// next LDS read wait for every tile load just issued, which removes the prefetch.  Correctness
+// rests on the explicit full wait before each barrier that hands a buffer to its readers; the
+// compiler's own memory waits stay correct because loads retire in issue order.
+// The five wait states before the load cover the m0 write (one needed) and a descriptor word
+// written by a VALU instruction just before (five needed before a memory instruction reads it);
+// the compiler does not look inside the statement for either hazard.
+__device__ __forceinline__ void tile_dma16(i32x4 rsrc, const lds_void* dst, int voff) {
+  uint32_t saved;  // m0 is the LDS address operand; it is restored for the compiler
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 4\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane((int)(uintptr_t)dst)), "v"(voff), "s"(rsrc));
+}
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& w) { return __builtin_bit_cast(bf16x8, w); }
@@ -118,32 +150,35 @@ __device__ __forceinline__ void rotate_chunk(float* x, const float* y, int c, in
 // ---------------------------------------------------------------------------------------------
 // 1. key preparation: 16 lanes per key row (8 features each), 16 rows per 256-thread block
 // ---------------------------------------------------------------------------------------------
-// Output row (b, j, g) lands at kout + b*ob + (j - jofs)*oj + g*D: the compact workspace
-// [B, S - n_cached, Hkv, D] (jofs = n_cached) or a full [B, S, Hkv, D] buffer such as a KV cache
-// (jofs = 0), which may be k itself (each row is read completely before it is written).
+// Rows j0 .. S-1 of k are visited; row (b, j, g) lands at kout + b*ob + (j - jofs)*oj + g*D: the
+// compact workspace [B, S - j0, Hkv, D] (jofs = j0) or a full [B, S, Hkv, D] buffer such as a KV
+// cache (jofs = 0), which may be k itself (each row is read completely before it is written).
+// Rows below n_cached are copied as stored, rows from n_cached on are normed and rotated.
 struct PrepOut {
   uint16_t* p;
   int64_t ob, oj;
   int32_t jofs;
+  int32_t j0;
 };
 
 template <int ROT, bool NORM>
 __global__ __launch_bounds__(256) void k_prep_kernel(AttnArgs a, PrepOut po, int64_t nrows) {
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int c = threadIdx.x & 15;
-  const int64_t nnew = a.S - a.n_cached;
+  const int64_t nnew = a.S - po.j0;
   const bool valid = row < nrows;
-  // row enumerates (b, jn, g) in the workspace layout [B, S - n_cached, Hkv, D]
+  // row enumerates (b, jn, g) in the layout [B, S - j0, Hkv, D]
   const int64_t r = valid ? row : 0;
   const int g = (int)(r % a.Hkv);
   const int64_t bj = r / a.Hkv;
   const int64_t jn = bj % nnew;
   const int b = (int)(bj / nnew);
-  const int64_t j = a.n_cached + jn;
+  const int64_t j = po.j0 + jn;
+  const bool fresh = j >= a.n_cached;  // uniform over the row's 16 lanes
   const uint16_t* src = (const uint16_t*)a.k + (int64_t)b * a.k_b + j * a.k_j + (int64_t)g * a.k_h;
   float x[8];
   unpack8(ld16(src + 8 * c), x);
-  if (NORM) {
+  if (NORM && fresh) {
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
@@ -157,7 +192,7 @@ __global__ __launch_bounds__(256) void k_prep_kernel(AttnArgs a, PrepOut po, int
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] *= rs * w[e];
   }
-  if (ROT != 0) {
+  if (ROT != 0 && fresh) {
     const int32_t kp = a.kpos[(int64_t)b * a.kpos_b + j];
     const int64_t tp = min<int64_t>(max<int64_t>(kp, 0), a.table_len - 1);
     const int halfp = a.R >> 1;
@@ -211,7 +246,8 @@ __device__ __forceinline__ uint16_t* qstage(int k) {
 
 struct StreamArgs {
   AttnArgs a;
-  const uint16_t* kprep;   // [B, S - n_cached, Hkv, D] prepared new keys (null if none)
+  const uint16_t* kprep;   // [B, S - w0, Hkv, D] keys from row w0 = max(n_cached - (BN-1), 0) on,
+                           // new ones prepared (null if nothing needs preparing)
 };
 
 template <int ROT, bool NORM, bool CAP>
@@ -274,18 +310,19 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   // ---- buffer descriptors of this (b, g): cached keys, prepared keys, values ----
   const int row_bytes = (int)(a.k_j * 2);  // bytes between consecutive keys of one head
   const int64_t kv_base = (int64_t)b * a.k_b + (int64_t)g * a.k_h;
-  // keys below nc come from k as stored; keys at or above nc from the prepared workspace (when
-  // there is none, nothing needs preparing and every key comes from k)
+  // Without a workspace nothing needs preparing and every key comes from k.  With one, a tile
+  // whose keys all lie below nc comes from k as stored and any other from the workspace, which
+  // starts at row w0 <= (first row of any tile reaching past nc).  The choice is uniform per
+  // tile, so each load names one descriptor.
   const int nc = sa.kprep ? a.n_cached : a.S;
-  const int nnew = a.S - nc;
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const uint16_t*)a.k + kv_base), (short)0,
-      nc > 0 ? (nc - 1) * row_bytes + HD * 2 : 0, kBufFlags);
-  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(sa.kprep ? sa.kprep + (int64_t)b * nnew * a.k_j + (int64_t)g * a.k_h : nullptr),
-      (short)0, (sa.kprep && nnew > 0) ? (nnew - 1) * row_bytes + HD * 2 : 0, kBufFlags);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const uint16_t*)a.v + kv_base), (short)0, (a.S - 1) * row_bytes + HD * 2, kBufFlags);
+  const int w0 = nc > BN - 1 ? nc - (BN - 1) : 0;
+  const int nws = a.S - w0;
+  const i32x4 rk = rsrc_words((const uint16_t*)a.k + kv_base,
+                              nc > 0 ? (nc - 1) * row_bytes + HD * 2 : 0);
+  const i32x4 rw = rsrc_words(
+      sa.kprep ? sa.kprep + (int64_t)b * nws * a.k_j + (int64_t)g * a.k_h : nullptr,
+      (sa.kprep && nws > 0) ? (nws - 1) * row_bytes + HD * 2 : 0);
+  const i32x4 rv = rsrc_words((const uint16_t*)a.v + kv_base, (a.S - 1) * row_bytes + HD * 2);
   const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.kpos + (int64_t)b * a.kpos_b), (short)0, a.S * 4, kBufFlags);
 
@@ -304,22 +341,16 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   }
   auto issue_tile = [&](int jt, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    const int tb = jt * row_bytes;         // cached keys and values: rows from 0
-    const int wb = (jt - nc) * row_bytes;  // prepared keys: rows from nc
+    const int tb = jt * row_bytes;  // values (and cached keys): rows from 0
+    const bool from_k = sa.kprep == nullptr || jt + BN <= nc;
+    const i32x4 rks = from_k ? rk : rw;
+    const int kb0 = from_k ? tb : (jt - w0) * row_bytes;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       lds_void* kdst = (lds_void*)(kbuf<buf>() + 4 * (w + 8 * i) * HD);
       lds_void* vdst = (lds_void*)(vbuf<buf>() + 4 * (w + 8 * i) * HD);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vdst, 16, lv[i] + tb, 0, 0, 0);
-      if (jt + BN <= nc) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, lk[i] + tb, 0, 0, 0);
-      } else if (jt >= nc) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, kdst, 16, lk[i] + wb, 0, 0, 0);
-      } else if (jt + 4 * (w + 8 * i) + (lane >> 4) < nc) {  // a tile straddling nc
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, lk[i] + tb, 0, 0, 0);
-      } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, kdst, 16, lk[i] + wb, 0, 0, 0);
-      }
+      tile_dma16(rv, vdst, lv[i] + tb);
+      tile_dma16(rks, kdst, lk[i] + kb0);
     }
     // key positions of the tile: loaded by wave 0 into a register and written to LDS by
     // commit_kpos once the tile's loads are complete, with INT32_MAX past the last key so that the
@@ -701,7 +732,7 @@ hipError_t launch_attn_norm(const StreamArgs& sa, hipStream_t s) {
 
 template <int ROT, bool NORM>
 hipError_t launch_prep(const AttnArgs& a, const PrepOut& po, hipStream_t stream) {
-  const int64_t nrows = (int64_t)a.B * (a.S - a.n_cached) * a.Hkv;
+  const int64_t nrows = (int64_t)a.B * (a.S - po.j0) * a.Hkv;
   if (nrows == 0) return hipSuccess;
   hipLaunchKernelGGL((k_prep_kernel<ROT, NORM>), dim3((unsigned)((nrows + 15) / 16)), dim3(256),
                      0, stream, a, po, nrows);
@@ -735,14 +766,20 @@ hipError_t launch_prep_keys(const AttnArgs& a, void* k_out, hipStream_t stream) 
   po.oj = a.k_j;
   po.ob = a.k_b;
   po.jofs = 0;
+  po.j0 = a.n_cached;
   return dispatch_prep(a, po, stream);
 }
 
 bool prefill_needs_kprep(const AttnArgs& a) { return (a.qk_norm || a.R > 0) && a.n_cached < a.S; }
 
+// First key row of the prepared-key workspace: it also holds the last BN - 1 cached rows (as
+// stored), so that a tile starting below n_cached but reaching past it comes whole from the
+// workspace and every tile reads one source.
+static int kprep_first_row(const AttnArgs& a) { return a.n_cached > BN - 1 ? a.n_cached - (BN - 1) : 0; }
+
 size_t prefill_stream_workspace_bytes(const AttnArgs& a) {
   if (!prefill_needs_kprep(a)) return 0;
-  return (size_t)a.B * (a.S - a.n_cached) * a.Hkv * HD * sizeof(uint16_t);
+  return (size_t)a.B * (a.S - kprep_first_row(a)) * a.Hkv * HD * sizeof(uint16_t);
 }
 
 bool prefill_stream_supported(const AttnArgs& a) {
@@ -759,8 +796,9 @@ hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t
     PrepOut po;
     po.p = (uint16_t*)workspace;
     po.oj = a.k_j;
-    po.ob = (int64_t)(a.S - a.n_cached) * a.k_j;
-    po.jofs = a.n_cached;
+    po.j0 = kprep_first_row(a);
+    po.ob = (int64_t)(a.S - po.j0) * a.k_j;
+    po.jofs = po.j0;
     hipError_t e = dispatch_prep(a, po, stream);
     if (e != hipSuccess) return e;
     sa.kprep = po.p;
