@@ -2,7 +2,7 @@
 // workspace for the prepared keys.
 //
 // Two launches:
-//  1. k_prep_kernel: every NEW key row (index >= n_cached) is RMS-normed and rotated once
+//  1. rows_prep_kernel: every NEW key row (index >= n_cached) is RMS-normed and rotated once
 //     ([Models] "What differs": q/k norm then rotation; [Guide] section 3.2 and section 4) and
 //     written, rounded to bf16, to the workspace; the workspace also holds the last 63 cached rows
 //     (copied as stored) so that every key tile reads a single source.  Other cached rows are
@@ -116,37 +116,6 @@ __device__ __forceinline__ int wave_lower_bound(const int32_t* kp, int n, int64_
   return lo;
 }
 
-// Rotate 8 consecutive features starting at 8*c, given the partner chunk y (half-split) or in
-// place (interleaved).  Feature pairs: half-split (d, d + R/2); interleaved (2i, 2i + 1).
-template <int ROT>
-__device__ __forceinline__ void rotate_chunk(float* x, const float* y, int c, int R,
-                                             const float* cr, const float* sr) {
-  const int d0 = 8 * c;
-  if (d0 >= R) return;
-  if (ROT == 1) {
-    const int half = R >> 1;
-    const bool first = d0 < half;
-    const int p0 = first ? d0 : d0 - half;
-    const f32x4 c0 = *(const f32x4*)(cr + p0), c1 = *(const f32x4*)(cr + p0 + 4);
-    const f32x4 s0 = *(const f32x4*)(sr + p0), s1 = *(const f32x4*)(sr + p0 + 4);
-    const float cs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-    const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      x[e] = first ? (x[e] * cs[e] - y[e] * sn[e]) : (y[e] * sn[e] + x[e] * cs[e]);
-  } else if (ROT == 2) {
-    const int p0 = d0 >> 1;
-    const f32x4 cs = *(const f32x4*)(cr + p0);
-    const f32x4 sn = *(const f32x4*)(sr + p0);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = x[2 * e], b = x[2 * e + 1];
-      x[2 * e] = a * cs[e] - b * sn[e];
-      x[2 * e + 1] = a * sn[e] + b * cs[e];
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------------------------
 // 1. key preparation: 16 lanes per key row (8 features each), 16 rows per 256-thread block
 // ---------------------------------------------------------------------------------------------
@@ -161,56 +130,150 @@ struct PrepOut {
   int32_t j0;
 };
 
+// Lane exchanges within a row of 16 lanes by data-parallel-primitive moves (no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppShl4 = 0x104;       // lane i reads lane i + 4
+constexpr int kDppShr4 = 0x114;       // lane i reads lane i - 4
+constexpr int kDppRor8 = 0x128;       // lane i reads lane i ^ 8 (rotate by half a row)
+constexpr int kDppHalfMirror = 0x141; // lane i reads lane 7 - i within its 8
+constexpr int kDppMirror = 0x140;     // lane i reads lane 15 - i
+
+// Sum over the 16 lanes of a row, in every lane.
+__device__ __forceinline__ float row16_sum(float s) {
+  s += dpp_mov<kDppXor1>(s);
+  s += dpp_mov<kDppXor2>(s);
+  s += dpp_mov<kDppHalfMirror>(s);
+  s += dpp_mov<kDppMirror>(s);
+  return s;
+}
+
+// Rows (b, p, h) for position indices p in [p0, pend) of a [B, *, H, 128] bf16 source are normed
+// (gain w), rotated at pos[b * pos_b + p] and multiplied by mul, then stored as bf16 at
+// dst + b*db + (p - pofs)*dp + h*128.  Rows with p < fresh_from are copied as stored.
+struct RowJob {
+  const uint16_t* src;
+  int64_t sb, sp, sh;
+  uint16_t* dst;
+  int64_t db, dp;
+  const int32_t* pos;
+  int64_t pos_b;
+  const uint16_t* w;
+  int32_t H, p0, pend, pofs, fresh_from;
+  float mul;
+};
+
+// 16 lanes per row, 8 features per lane (lane c: features 8c .. 8c + 7).  Each 16-lane group takes
+// up to kHeadsPerGroup heads of one position, so the position's table entries are loaded once
+// for all of them; 16 groups per block, blockIdx.y is the sequence.  (pend - p0) * H < 2^31 (the
+// host checks the sizes).
+constexpr int kHeadsPerGroup = 8;
+
 template <int ROT, bool NORM>
-__global__ __launch_bounds__(256) void k_prep_kernel(AttnArgs a, PrepOut po, int64_t nrows) {
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+__global__ __launch_bounds__(256) void rows_prep_kernel(AttnArgs a, RowJob jb) {
+  constexpr int HG = kHeadsPerGroup;
+  const int b = blockIdx.y;
   const int c = threadIdx.x & 15;
-  const int64_t nnew = a.S - po.j0;
-  const bool valid = row < nrows;
-  // row enumerates (b, jn, g) in the layout [B, S - j0, Hkv, D]
-  const int64_t r = valid ? row : 0;
-  const int g = (int)(r % a.Hkv);
-  const int64_t bj = r / a.Hkv;
-  const int64_t jn = bj % nnew;
-  const int b = (int)(bj / nnew);
-  const int64_t j = po.j0 + jn;
-  const bool fresh = j >= a.n_cached;  // uniform over the row's 16 lanes
-  const uint16_t* src = (const uint16_t*)a.k + (int64_t)b * a.k_b + j * a.k_j + (int64_t)g * a.k_h;
-  float x[8];
-  unpack8(ld16(src + 8 * c), x);
-  if (NORM && fresh) {
-    float ss = 0.f;
+  const uint32_t nch = (uint32_t)(jb.H + HG - 1) / HG;  // head chunks per position
+  const uint32_t gi = blockIdx.x * 16u + (threadIdx.x >> 4);
+  const bool valid = gi < (uint32_t)(jb.pend - jb.p0) * nch;
+  const uint32_t gg = valid ? gi : 0u;
+  const uint32_t pi = gg / nch;
+  const int h0 = (int)(gg - pi * nch) * HG;
+  const int p = jb.p0 + (int)pi;
+  const bool fresh = p >= jb.fresh_from;  // uniform over the group's 16 lanes
+  const uint16_t* src = jb.src + (int64_t)b * jb.sb + (int64_t)p * jb.sp + 8 * c;
+  u32x4 raw[HG];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
-    ss += __shfl_xor(ss, 4, 64);
-    ss += __shfl_xor(ss, 8, 64);
-    const float rs = rsqrtf(ss * (1.0f / HD) + a.eps);
-    float w[8];
-    unpack8(ld16((const uint16_t*)a.kw + 8 * c), w);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] *= rs * w[e];
-  }
-  if (ROT != 0 && fresh) {
-    const int32_t kp = a.kpos[(int64_t)b * a.kpos_b + j];
-    const int64_t tp = min<int64_t>(max<int64_t>(kp, 0), a.table_len - 1);
+  for (int k = 0; k < HG; ++k) raw[k] = ld16(src + (int64_t)min(h0 + k, jb.H - 1) * jb.sh);
+  // this lane's table entries at the row position: 8 (half-split) or 4 (adjacent pairs) pairs
+  float cs[8], sn[8];
+  const bool rot = ROT != 0 && fresh && 8 * c < a.R;
+  if (ROT != 0) {
+    const int32_t pp = jb.pos[(int64_t)b * jb.pos_b + p];
+    const int64_t tp = min<int64_t>(max<int64_t>(pp, 0), a.table_len - 1);
     const int halfp = a.R >> 1;
-    const float* cr = a.cos_t + tp * halfp;
-    const float* sr = a.sin_t + tp * halfp;
+    const int d0 = rot ? 8 * c : 0;
+    const int q0 = ROT == 1 ? (d0 < halfp ? d0 : d0 - halfp) : d0 >> 1;
+    const float* cr = a.cos_t + tp * halfp + q0;
+    const float* sr = a.sin_t + tp * halfp + q0;
+    const f32x4 c0 = *(const f32x4*)cr, s0 = *(const f32x4*)sr;
+    f32x4 c1 = c0, s1 = s0;
     if (ROT == 1) {
-      float y[8];
-      const int P = a.R >> 4;  // partner distance in chunks: 1, 2, 4 or 8
+      c1 = *(const f32x4*)(cr + 4);
+      s1 = *(const f32x4*)(sr + 4);
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = __shfl_xor(x[e], P, 64);
-      rotate_chunk<1>(x, y, c, a.R, cr, sr);
-    } else {
-      rotate_chunk<2>(x, x, c, a.R, cr, sr);
+    for (int e = 0; e < 4; ++e) {
+      cs[e] = c0[e];
+      sn[e] = s0[e];
+      cs[e + 4] = c1[e];
+      sn[e + 4] = s1[e];
     }
   }
-  if (valid) {
-    uint16_t* dst = po.p + (int64_t)b * po.ob + (j - po.jofs) * po.oj + (int64_t)g * HD;
-    *(u32x4*)(dst + 8 * c) = pack8(x);
+  float wv[8];
+  if (NORM) unpack8(ld16(jb.w + 8 * c), wv);
+  const bool first = 8 * c < (a.R >> 1);
+  const int P = a.R >> 4;  // half-split: the partner chunk is P = R/16 chunks away (lane c ^ P)
+#pragma unroll
+  for (int k = 0; k < HG; ++k) {
+    float x[8];
+    unpack8(raw[k], x);
+    if (NORM && fresh) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+      ss = row16_sum(ss);
+      const float rs = rsqrtf(ss * (1.0f / HD) + a.eps);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= rs * wv[e];
+    }
+    if (ROT == 1 && fresh) {
+      float y[8];
+      if (P == 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = dpp_mov<kDppXor1>(x[e]);
+      } else if (P == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = dpp_mov<kDppXor2>(x[e]);
+      } else if (P == 4) {
+        const bool up = (c & 4) != 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float l = dpp_mov<kDppShl4>(x[e]), rgt = dpp_mov<kDppShr4>(x[e]);
+          y[e] = up ? rgt : l;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = dpp_mov<kDppRor8>(x[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float r = first ? (x[e] * cs[e] - y[e] * sn[e]) : (y[e] * sn[e] + x[e] * cs[e]);
+        x[e] = rot ? r : x[e];
+      }
+    } else if (ROT == 2 && fresh) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float u = x[2 * e], v = x[2 * e + 1];
+        x[2 * e] = rot ? u * cs[e] - v * sn[e] : u;
+        x[2 * e + 1] = rot ? u * sn[e] + v * cs[e] : v;
+      }
+    }
+    if (jb.mul != 1.0f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= jb.mul;
+    }
+    if (valid && h0 + k < jb.H) {
+      uint16_t* dst =
+          jb.dst + (int64_t)b * jb.db + (int64_t)(p - jb.pofs) * jb.dp + (int64_t)(h0 + k) * HD;
+      *(u32x4*)(dst + 8 * c) = pack8(x);
+    }
   }
 }
 
@@ -392,9 +455,11 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
                                         : INT32_MIN;
 
   // ---- query prep, shared by the workgroup: 16 lanes per query row, 8 features per lane (32 rows
-  // per pass, 8 passes, in two batches whose loads all go out before their arithmetic).  Each
-  // row is RMS-normed, rotated at its position and scaled into log2 units, then stored as bf16 in
-  // the staging area; rows past the end are stored as zeros ----
+  // per pass, 8 passes in two batches whose loads all go out before their arithmetic: rows and
+  // positions, then the table entries at those positions).  Each row is RMS-normed, rotated at
+  // its position and scaled into log2 units, then stored as bf16 in the staging area; rows past
+  // the end are stored as zeros.  The row-local exchanges (norm sum, rotation partner) are DPP
+  // moves ----
   {
     const int grp = tid >> 4, c = tid & 15;
     const uint16_t* qw = (const uint16_t*)a.qw;
@@ -404,79 +469,94 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     const bool first = 8 * c < halfp;
     const int p0 = ROT == 1 ? (!rot ? 0 : (first ? 8 * c : 8 * c - halfp)) : (rot ? 4 * c : 0);
     const float qscale = a.scale * kLog2e;
+    constexpr int NP = ROWS / 64;  // passes per batch
     float wv[8];
     if (NORM) unpack8(ld16(qw + 8 * c), wv);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      u32x4 xw[4];
-      int32_t pw[4];
-      bool vw[4];
+    u32x4 xw[NP];
+    int32_t pw[NP];
+    bool vw[NP];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t f = f0 + 32 * (4 * hb + j) + grp;
-        vw[j] = f < nrows;
-        const int ri = vw[j] ? (int)(f / G) : 0;
-        const int rh = g * G + (vw[j] ? (int)(f % G) : 0);
-        xw[j] = ld16((const uint16_t*)a.q + (int64_t)b * a.q_b + (int64_t)ri * a.q_i +
-                     (int64_t)rh * a.q_h + 8 * c);
-        pw[j] = qpos_b[ri];
-      }
-      f32x4 tc[4][2], ts[4][2];
-      if (ROT) {
+    for (int j = 0; j < NP; ++j) {
+      // a valid flattened row index is below L*G < 2^31 (checked on the host): 32-bit division
+      const int64_t f = f0 + 32 * (NP * hb + j) + grp;
+      vw[j] = f < nrows;
+      const uint32_t fv = vw[j] ? (uint32_t)f : 0u;
+      const int ri = (int)(fv / (uint32_t)G);
+      const int rh = g * G + (int)(fv - (uint32_t)ri * (uint32_t)G);
+      xw[j] = ld16((const uint16_t*)a.q + (int64_t)b * a.q_b + (int64_t)ri * a.q_i +
+                   (int64_t)rh * a.q_h + 8 * c);
+      pw[j] = qpos_b[ri];
+    }
+    f32x4 tc[NP][2], ts[NP][2];
+    if (ROT) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t tp = min<int64_t>(max<int64_t>(pw[j], 0), a.table_len - 1);
-          const float* cr = a.cos_t + tp * halfp + p0;
-          const float* sr = a.sin_t + tp * halfp + p0;
-          tc[j][0] = *(const f32x4*)cr;
-          ts[j][0] = *(const f32x4*)sr;
-          if (ROT == 1) {
-            tc[j][1] = *(const f32x4*)(cr + 4);
-            ts[j][1] = *(const f32x4*)(sr + 4);
-          }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float x[8];
-        unpack8(xw[j], x);
-        if (NORM) {
-          float ss = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-          ss += __shfl_xor(ss, 1, 64);
-          ss += __shfl_xor(ss, 2, 64);
-          ss += __shfl_xor(ss, 4, 64);
-          ss += __shfl_xor(ss, 8, 64);
-          const float rs = rsqrtf(ss * (1.0f / HD) + a.eps);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] *= rs * wv[e];
-        }
+      for (int j = 0; j < NP; ++j) {
+        const int64_t tp = min<int64_t>(max<int64_t>(pw[j], 0), a.table_len - 1);
+        const float* cr = a.cos_t + tp * halfp + p0;
+        const float* sr = a.sin_t + tp * halfp + p0;
+        tc[j][0] = *(const f32x4*)cr;
+        ts[j][0] = *(const f32x4*)sr;
         if (ROT == 1) {
-          float y[8];
+          tc[j][1] = *(const f32x4*)(cr + 4);
+          ts[j][1] = *(const f32x4*)(sr + 4);
+        }
+      }
+    }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = __shfl_xor(x[e], P, 64);
+    for (int j = 0; j < NP; ++j) {
+      float x[8];
+      unpack8(xw[j], x);
+      if (NORM) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+        ss = row16_sum(ss);
+        const float rs = rsqrtf(ss * (1.0f / HD) + a.eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= rs * wv[e];
+      }
+      if (ROT == 1) {
+        float y[8];
+        if (P == 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = dpp_mov<kDppXor1>(x[e]);
+        } else if (P == 2) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = dpp_mov<kDppXor2>(x[e]);
+        } else if (P == 4) {
+          const bool up = (c & 4) != 0;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float cs = tc[j][e >> 2][e & 3], sn = ts[j][e >> 2][e & 3];
-            const float r = first ? (x[e] * cs - y[e] * sn) : (y[e] * sn + x[e] * cs);
-            x[e] = rot ? r : x[e];
+            const float l = dpp_mov<kDppShl4>(x[e]), rgt = dpp_mov<kDppShr4>(x[e]);
+            y[e] = up ? rgt : l;
           }
-        } else if (ROT == 2) {
+        } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float cs = tc[j][0][e], sn = ts[j][0][e];
-            const float u = x[2 * e], v = x[2 * e + 1];
-            x[2 * e] = rot ? u * cs - v * sn : u;
-            x[2 * e + 1] = rot ? u * sn + v * cs : v;
-          }
+          for (int e = 0; e < 8; ++e) y[e] = dpp_mov<kDppRor8>(x[e]);
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = vw[j] ? x[e] * qscale : 0.f;
-        const int row = 32 * (4 * hb + j) + grp;  // 0 .. 255
-        const int rr = row & 63;
-        *(u32x4*)(qstage(row >> 6) + rr * HD + ((c ^ (rr & 15)) << 3)) = pack8(x);
+        for (int e = 0; e < 8; ++e) {
+          const float cs = tc[j][e >> 2][e & 3], sn = ts[j][e >> 2][e & 3];
+          const float r = first ? (x[e] * cs - y[e] * sn) : (y[e] * sn + x[e] * cs);
+          x[e] = rot ? r : x[e];
+        }
+      } else if (ROT == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float cs = tc[j][0][e], sn = ts[j][0][e];
+          const float u = x[2 * e], v = x[2 * e + 1];
+          x[2 * e] = rot ? u * cs - v * sn : u;
+          x[2 * e + 1] = rot ? u * sn + v * cs : v;
+        }
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = vw[j] ? x[e] * qscale : 0.f;
+      const int row = 32 * (NP * hb + j) + grp;  // 0 .. 255
+      const int rr = row & 63;
+      *(u32x4*)(qstage(row >> 6) + rr * HD + ((c ^ (rr & 15)) << 3)) = pack8(x);
+    }
     }
   }
   __syncthreads();  // staging complete
@@ -731,24 +811,47 @@ hipError_t launch_attn_norm(const StreamArgs& sa, hipStream_t s) {
 }
 
 template <int ROT, bool NORM>
-hipError_t launch_prep(const AttnArgs& a, const PrepOut& po, hipStream_t stream) {
-  const int64_t nrows = (int64_t)a.B * (a.S - po.j0) * a.Hkv;
-  if (nrows == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_prep_kernel<ROT, NORM>), dim3((unsigned)((nrows + 15) / 16)), dim3(256),
-                     0, stream, a, po, nrows);
+hipError_t launch_rows(const AttnArgs& a, const RowJob& jb, int B, hipStream_t stream) {
+  const int64_t ng = (int64_t)(jb.pend - jb.p0) * ((jb.H + kHeadsPerGroup - 1) / kHeadsPerGroup);
+  if (ng <= 0 || B == 0) return hipSuccess;
+  hipLaunchKernelGGL((rows_prep_kernel<ROT, NORM>), dim3((unsigned)((ng + 15) / 16), (unsigned)B),
+                     dim3(256), 0, stream, a, jb);
   return hipGetLastError();
 }
 
-hipError_t dispatch_prep(const AttnArgs& a, const PrepOut& po, hipStream_t stream) {
+hipError_t dispatch_rows(const AttnArgs& a, const RowJob& jb, bool norm, hipStream_t stream) {
   const int rot = a.R == 0 ? 0 : (a.style == 0 ? 1 : 2);
-  switch (rot * 2 + (a.qk_norm ? 1 : 0)) {
-    case 0: return hipSuccess;  // nothing to prepare
-    case 1: return launch_prep<0, true>(a, po, stream);
-    case 2: return launch_prep<1, false>(a, po, stream);
-    case 3: return launch_prep<1, true>(a, po, stream);
-    case 4: return launch_prep<2, false>(a, po, stream);
-    default: return launch_prep<2, true>(a, po, stream);
+  switch (rot * 2 + (norm ? 1 : 0)) {
+    case 0: return launch_rows<0, false>(a, jb, a.B, stream);
+    case 1: return launch_rows<0, true>(a, jb, a.B, stream);
+    case 2: return launch_rows<1, false>(a, jb, a.B, stream);
+    case 3: return launch_rows<1, true>(a, jb, a.B, stream);
+    case 4: return launch_rows<2, false>(a, jb, a.B, stream);
+    default: return launch_rows<2, true>(a, jb, a.B, stream);
   }
+}
+
+// Keys j0 .. S-1: the new ones (j >= n_cached) normed and rotated, the others copied as stored.
+hipError_t dispatch_prep(const AttnArgs& a, const PrepOut& po, hipStream_t stream) {
+  if (a.R == 0 && !a.qk_norm && po.p == (uint16_t*)a.k) return hipSuccess;  // nothing to do
+  RowJob jb;
+  jb.src = (const uint16_t*)a.k;
+  jb.sb = a.k_b;
+  jb.sp = a.k_j;
+  jb.sh = a.k_h;
+  jb.dst = po.p;
+  jb.db = po.ob;
+  jb.dp = po.oj;
+  jb.pos = a.kpos;
+  jb.pos_b = a.kpos_b;
+  jb.w = (const uint16_t*)a.kw;
+  jb.H = a.Hkv;
+  jb.p0 = po.j0;
+  jb.pend = a.S;
+  jb.pofs = po.jofs;
+  jb.fresh_from = a.n_cached;
+  jb.mul = 1.0f;
+  return dispatch_rows(a, jb, a.qk_norm != 0, stream);
 }
 
 }  // namespace
