@@ -24,7 +24,10 @@ half-split pairing of the study guide; deinterleave equivalence; norm preservati
 position; RMS of the normed vector; soft-cap limits; integer mask probes (windows, chunks with
 and without lookback, floor chunks of negative positions); the sink's closed forms (one key: a
 logistic weight; constant values: the share the keys keep) and torch's SDPA with the sink as one
-more key; chunks without lookback restarting the sequence; window and GQA equivalences; decode == last prefill row; chunked prefill == tail of full prefill; brute-force
+more key; chunks without lookback restarting the sequence; paged rows equal the contiguous
+cache under identity and permuted block tables, paged update writes exactly the next slots, and
+decode over a pool filled by append_rows equals the last prefill row; window and GQA
+equivalences; decode == last prefill row; chunked prefill == tail of full prefill; brute-force
 scalar loops; and torch's CPU scaled_dot_product_attention in float64.  No function here is
 "parity unpinned".
 """
@@ -356,3 +359,55 @@ def attn_decode(q, kcache, vcache, lens, **kw):
     """attn_decode_one over a batch: q [B, Hq, D], caches [B, Hkv, Smax, D], lens [B]."""
     return np.stack([attn_decode_one(q[b], kcache[b], vcache[b], int(lens[b]), **kw)
                      for b in range(len(lens))])
+
+
+# ----------------------------------------------------------------------------------------------
+# Paged KV cache (reading of the pages' block manager, [Models] "Sliding windows" and the MLA
+# section's paged pool; [Guide] §3.3 KVCache for what update computes)
+# ----------------------------------------------------------------------------------------------
+# Reading: a pool holds num_blocks blocks of block_size token slots for every KV head, laid out
+# [num_blocks, Hkv, block_size, D]; sequence b's logical slot j (position j) lives in physical
+# block table[b, j // block_size], slot j % block_size.  cache.update writes the step's rows at
+# the sequence's next slots; attention then reads slots 0 .. len-1 in order.
+def paged_rows(pool, table, b, n, block_size):
+    """Logical rows 0 .. n-1 of sequence b: [Hkv, n, D] gathered slot by slot."""
+    pool = np.asarray(pool)
+    Hkv, D = pool.shape[1], pool.shape[3]
+    out = np.empty((Hkv, n, D), dtype=np.float64)
+    for j in range(n):
+        blk = int(table[b][j // block_size])
+        out[:, j] = pool[blk, :, j % block_size]
+    return out
+
+
+def paged_update(pool, table, start, rows, block_size):
+    """cache.update on a paged pool: rows [B, L, Hkv, D] go to logical slots start[b] .. start[b] +
+    L - 1 of each sequence; returns the new pool (a copy)."""
+    pool = np.array(pool, copy=True)
+    B, L = rows.shape[0], rows.shape[1]
+    for b in range(B):
+        for i in range(L):
+            j = int(start[b]) + i
+            pool[int(table[b][j // block_size]), :, j % block_size] = rows[b, i]
+    return pool
+
+
+def append_rows(k_new, key_positions, *, inv_freq, style="half", k_norm_w=None, eps=1e-6,
+                attention_factor=1.0):
+    """The rows cache.update receives for new keys ([Models] "What differs": k-norm when
+    weighted, then rotation at the keys' positions; values are stored as they are)."""
+    k = np.asarray(k_new, np.float64)
+    if k_norm_w is not None:
+        k = rms_norm(k, k_norm_w, eps)
+    return rotate(k, np.asarray(key_positions)[..., None], inv_freq, style, attention_factor)
+
+
+def attn_decode_paged(q, k_pool, v_pool, table, lens, block_size, **kw):
+    """attn_decode over a paged pool: each sequence's cache rows gathered through its table."""
+    outs = []
+    for b in range(len(lens)):
+        n = int(lens[b])
+        kk = paged_rows(k_pool, table, b, n, block_size)
+        vv = paged_rows(v_pool, table, b, n, block_size)
+        outs.append(attn_decode_one(q[b], kk, vv, n, **kw))
+    return np.stack(outs)

@@ -613,3 +613,81 @@ def test_decode_equals_last_prefill_row_with_sinks_and_chunks():
         dec = oracle.attn_decode_one(x["q"][0, -1], kc, vc, 37, inv_freq=inv, sinks=sinks,
                                      chunk=chunk, chunk_lookback=lookback)
         np.testing.assert_allclose(dec, full, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------------------------
+# Paged cache
+# ----------------------------------------------------------------------------------------------
+def _contiguous_to_pool(cache, block_size, perm):
+    """A [B, Hkv, Smax, D] cache cut into blocks; logical block i of sequence b goes to physical
+    block perm[b * nbps + i]."""
+    B, Hkv, Smax, D = cache.shape
+    nbps = Smax // block_size
+    pool = np.full((B * nbps, Hkv, block_size, D), np.nan)
+    table = np.zeros((B, nbps), np.int32)
+    for b in range(B):
+        for i in range(nbps):
+            phys = perm[b * nbps + i]
+            pool[phys] = cache[b, :, i * block_size:(i + 1) * block_size]
+            table[b, i] = phys
+    return pool, table
+
+
+@pytest.mark.parametrize("block_size", [1, 4, 16])
+def test_paged_rows_read_the_contiguous_cache(block_size):
+    # [Guide] §3.3: the cache holds slot j of sequence b at position j; a paged pool holds the same
+    # rows behind a block table, whatever the physical order
+    B, Hkv, Smax, D = 3, 2, 32, 8
+    cache = rng.standard_normal((B, Hkv, Smax, D))
+    for perm in (np.arange(B * Smax // block_size),
+                 rng.permutation(B * Smax // block_size)):
+        pool, table = _contiguous_to_pool(cache, block_size, perm)
+        for b, n in ((0, 1), (1, 17), (2, 32)):
+            np.testing.assert_array_equal(oracle.paged_rows(pool, table, b, n, block_size),
+                                          cache[b, :, :n])
+
+
+def test_paged_update_appends_and_leaves_other_slots():
+    # [Guide] §3.3 update: the L new rows land at slots len .. len+L-1, everything else is kept
+    B, Hkv, D, bs = 2, 2, 4, 4
+    pool = rng.standard_normal((10, Hkv, bs, D))
+    table = np.array([[7, 2, 5], [0, 9, 3]], np.int32)
+    start = np.array([3, 6])
+    rows = rng.standard_normal((B, 5, Hkv, D))
+    new = oracle.paged_update(pool, table, start, rows, bs)
+    for b in range(B):
+        got = oracle.paged_rows(new, table, b, int(start[b]) + 5, bs)
+        np.testing.assert_array_equal(got[:, :start[b]],
+                                      oracle.paged_rows(pool, table, b, int(start[b]), bs))
+        np.testing.assert_array_equal(got[:, start[b]:], rows[b].transpose(1, 0, 2))
+    touched = {(int(table[b][(int(start[b]) + i) // bs]), (int(start[b]) + i) % bs)
+               for b in range(B) for i in range(5)}
+    for blk in range(10):
+        for s in range(bs):
+            if (blk, s) not in touched:
+                np.testing.assert_array_equal(new[blk, :, s], pool[blk, :, s])
+
+
+def test_paged_decode_after_append_equals_last_prefill_row():
+    # the whole step: new keys normed and rotated by append_rows, written through a permuted
+    # table, then decode over the pool == the last row of prefill over the same sequence
+    wl = _small("llama31_decode_bf16", B=2, L=37, S=37, Hq=8, Hkv=2, D=32, rotary_dim=32,
+                qk_norm=True, window=20)
+    x = prefill_inputs(wl.with_(kind="prefill"), seed=17)
+    inv = oracle.rope_inv_freq(32, 5e5, "llama3", 8.0, 1.0, 4.0, 8192.0)
+    bs, nbps = 4, 10
+    perm = rng.permutation(2 * nbps)
+    table = perm.reshape(2, nbps).astype(np.int32)
+    kpool = np.zeros((2 * nbps, 2, bs, 32))
+    vpool = np.zeros_like(kpool)
+    krows = oracle.append_rows(x["k"], x["key_positions"], inv_freq=inv, k_norm_w=x["k_norm_w"],
+                               eps=wl.eps)
+    start = np.zeros(2, np.int64)
+    kpool = oracle.paged_update(kpool, table, start, krows, bs)
+    vpool = oracle.paged_update(vpool, table, start, x["v"], bs)
+    sinks = np.array([0.5, -1.0, 2.0, 0.0, 1.0, -3.0, 0.25, 4.0])
+    dec = oracle.attn_decode_paged(x["q"][:, -1], kpool, vpool, table, np.full(2, 37), bs,
+                                   inv_freq=inv, window=20, q_norm_w=x["q_norm_w"], eps=wl.eps,
+                                   sinks=sinks)
+    full = _prefill(wl, x, inv_freq=inv, sinks=sinks)[:, -1]
+    np.testing.assert_allclose(dec, full, atol=1e-13)
