@@ -19,7 +19,8 @@ from typing import Optional, Sequence
 __all__ = [
     "GQAError", "RopeSpec", "AttnConfig", "library", "rope_inv_freq", "rope_tables",
     "rope_attention_factor", "rope_softmax_scale",
-    "attn_prefill", "attn_decode", "decode_workspace_bytes", "prefill_workspace_bytes", "prep_keys", "last_error", "set_kernel_policy",
+    "attn_prefill", "attn_decode", "decode_workspace_bytes", "PagedKV", "paged_append",
+    "paged_decode_workspace_bytes", "attn_decode_paged", "prefill_workspace_bytes", "prep_keys", "last_error", "set_kernel_policy",
     "LIB_PATH", "EXPORTS",
 ]
 
@@ -63,6 +64,13 @@ class _AttnCfg(ctypes.Structure):
                 ("chunk_size", ctypes.c_int32), ("chunk_lookback", ctypes.c_int32)]
 
 
+class _PagedKV(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 _P = ctypes.c_void_p
 _I32, _I64, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 # name -> (restype, argtypes); every function declared in include/gqa_rope.h
@@ -80,6 +88,12 @@ EXPORTS = {
     "gqa_decode_workspace_bytes": (_SZ, [ctypes.POINTER(_AttnCfg), _I32, _I32]),
     "gqa_attn_decode": (_I32, [ctypes.POINTER(_AttnCfg), _P, _P, _P, _P, _I32, _I32, _I32, _P, _P,
                                _SZ, _P]),
+    "gqa_paged_append": (_I32, [ctypes.POINTER(_AttnCfg), ctypes.POINTER(_PagedKV), _P, _P, _P,
+                                _I64, _P, _I32, _I32, _P]),
+    "gqa_paged_decode_workspace_bytes": (_SZ, [ctypes.POINTER(_AttnCfg), ctypes.POINTER(_PagedKV),
+                                               _I32]),
+    "gqa_attn_decode_paged": (_I32, [ctypes.POINTER(_AttnCfg), _P, ctypes.POINTER(_PagedKV), _P,
+                                     _I32, _I32, _P, _P, _SZ, _P]),
     "gqa_set_kernel_policy": (_I32, [_I32]),
     "gqa_last_error": (ctypes.c_char_p, []),
     "gqa_version": (ctypes.c_char_p, []),
@@ -392,4 +406,77 @@ def attn_decode(cfg: AttnConfig, q, kcache, vcache, lens, window=0, out=None, wo
     c = cfg.c_struct()
     _check(library().gqa_attn_decode(ctypes.byref(c), pq, pk, pv, pl, B, Smax, int(window), po, pw,
                                      nbytes, _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+@dataclass
+class PagedKV:
+    """Paged KV pool: k_pool, v_pool [num_blocks, Hkv, block_size, D] and block_table int32
+    [B, max_blocks] (device tensors); slot j of sequence b is row j % block_size of block
+    block_table[b, j // block_size]."""
+    k_pool: object
+    v_pool: object
+    block_table: object
+
+    def c_struct(self, cfg: AttnConfig):
+        torch = _torch()
+        nb, hkv, bs, d = (int(x) for x in self.k_pool.shape)
+        pk = _need(self.k_pool, "k_pool", (nb, cfg.num_kv_heads, bs, cfg.head_dim), cfg.torch_dtype)
+        pv = _need(self.v_pool, "v_pool", (nb, cfg.num_kv_heads, bs, cfg.head_dim), cfg.torch_dtype)
+        if self.block_table.dim() != 2:
+            raise GQAError(2, "block_table must be [B, max_blocks]")
+        pt = _need(self.block_table, "block_table", tuple(self.block_table.shape), torch.int32)
+        return _PagedKV(pk.value, pv.value, pt.value, int(self.block_table.shape[1]), bs, nb, 0)
+
+
+def paged_append(cfg: AttnConfig, kv: PagedKV, k_new, v_new, key_positions, start, stream=None):
+    """cache.update with the key preparation fused in: k_new, v_new [B, L, Hkv, D] go to slots
+    start[b] .. start[b] + L - 1 (keys normed and rotated at key_positions [B, L] or [L])."""
+    torch = _torch()
+    B, L = int(k_new.shape[0]), int(k_new.shape[1])
+    dt = cfg.torch_dtype
+    pk = _need(k_new, "k_new", (B, L, cfg.num_kv_heads, cfg.head_dim), dt)
+    pv = _need(v_new, "v_new", (B, L, cfg.num_kv_heads, cfg.head_dim), dt)
+    if key_positions.dim() == 1:
+        pp, stride = _need(key_positions, "key_positions", (L,), torch.int32), 0
+    else:
+        pp, stride = _need(key_positions, "key_positions", (B, L), torch.int32), L
+    ps = _need(start, "start", (B,), torch.int32)
+    c = cfg.c_struct()
+    k = kv.c_struct(cfg)
+    _check(library().gqa_paged_append(ctypes.byref(c), ctypes.byref(k), pk, pv, pp, stride, ps, B,
+                                      L, _stream(stream)))
+
+
+def paged_decode_workspace_bytes(cfg: AttnConfig, kv: PagedKV, B: int) -> int:
+    c = cfg.c_struct()
+    k = kv.c_struct(cfg)
+    n = library().gqa_paged_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(k), int(B))
+    err = last_error()
+    if n == 0 and err:
+        raise GQAError(2, err)
+    return int(n)
+
+
+def attn_decode_paged(cfg: AttnConfig, q, kv: PagedKV, lens, window=0, out=None, workspace=None,
+                      stream=None):
+    """q [B, Hq, D] against a paged pool, lens [B] int32.  Returns out [B, Hq, D]."""
+    torch = _torch()
+    B = int(q.shape[0])
+    dt = cfg.torch_dtype
+    pq = _need(q, "q", (B, cfg.num_q_heads, cfg.head_dim), dt)
+    pl = _need(lens, "lens", (B,), torch.int32)
+    if out is None:
+        out = torch.empty_like(q)
+    po = _need(out, "out", tuple(q.shape), dt)
+    if workspace is None:
+        workspace = torch.empty(paged_decode_workspace_bytes(cfg, kv, B), dtype=torch.uint8,
+                                device=q.device)
+    pw = _need(workspace, "workspace", (workspace.numel(),), torch.uint8)
+    c = cfg.c_struct()
+    k = kv.c_struct(cfg)
+    _check(library().gqa_attn_decode_paged(ctypes.byref(c), pq, ctypes.byref(k), pl, B,
+                                           int(window), po, pw, workspace.numel(),
+                                           _stream(stream)))
     return out

@@ -58,6 +58,10 @@ struct DecodeArgs {
   float* part_ml;     // [B, Hkv, nsplit, G, 2] running max (log2 units) and sum
   uint16_t* qprep;    // [B, Hq, D] prepared queries (bf16, log2 units)
   int32_t nsplit;     // splits per (b, g) allotted in the workspace
+  // paged cache (table non-null): a.k, a.v are pools [num_blocks, Hkv, 2^log2bs, D]; slot j of
+  // sequence b is row j % bs of block table[b * max_blocks + j / bs]
+  const int32_t* table;
+  int32_t max_blocks, log2bs, num_blocks;
 };
 
 __device__ __forceinline__ int vt_off(int r, int c) { return r * HD + ((c ^ (r & 15)) << 3); }
@@ -161,9 +165,10 @@ __device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rk, __amdgpu_b
 }
 
 // A work item as one wavefront sees it (all fields wave-uniform).  A null item (none left) has
-// we = 0 and empty descriptor ranges.
+// we = 0 and empty descriptor ranges.  klo: first visible key (the paged walk starts below it,
+// at a multiple of KBLK, and masks the keys in between).
 struct Item {
-  int b, g, sp, ws, we, nblk;
+  int b, g, sp, ws, we, nblk, klo;
   bool valid;
 };
 
@@ -174,7 +179,54 @@ __device__ __forceinline__ int first_key(const AttnArgs& a, int n) {
   return a.has_floor() ? (int)max<int64_t>(0, key_floor(a, (int64_t)n - 1)) : 0;
 }
 
-template <bool CAP>
+// First slot of a sequence's split walk: the first visible key, rounded down to a multiple of
+// KBLK for a paged cache (so that every 16-key half of a block lies in one cache block).
+__device__ __forceinline__ int walk_start(const AttnArgs& a, int n, bool paged) {
+  const int f = first_key(a, n);
+  return paged ? f & ~(KBLK - 1) : f;
+}
+
+// Paged loads of the block of 32 keys starting at kb0 (a multiple of KBLK) of sequence b: each
+// 16-key half lies in one cache block and gets its own descriptors; keys at or past `we`, and a
+// half wholly below the first visible key klo, are out of range (read as zero, no access), so a
+// cache block that holds no visible key is never touched.  The table entries are wave-uniform
+// scalar loads (adjacent blocks share a scalar cache line).
+__device__ __forceinline__ void load_block_paged(const DecodeArgs& da, int b, int g, int we,
+                                                 int klo, int kb0, BlockRegs& br) {
+  const int lane = threadIdx.x & 63;
+  const AttnArgs& a = da.a;
+  const int bs = 1 << da.log2bs;
+  const int32_t* trow = da.table + (int64_t)b * da.max_blocks;
+  __amdgpu_buffer_rsrc_t rk[2], rv[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j0 = kb0 + 16 * h;
+    const int ti = min(j0 >> da.log2bs, da.max_blocks - 1);
+    int phys = __builtin_amdgcn_readfirstlane(trow[ti]);
+    phys = min(max(phys, 0), da.num_blocks - 1);
+    const int64_t row = ((int64_t)phys * a.Hkv + g) * bs + (j0 & (bs - 1));
+    const int cnt = j0 + 16 <= klo ? 0 : min(max(we - j0, 0), 16);
+    rk[h] = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.k + row * HD), 0,
+                                              cnt * HD * 2, kRsrcFlags);
+    rv[h] = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.v + row * HD), 0,
+                                              cnt * HD * 2, kRsrcFlags);
+  }
+  const int kofs = ((lane & 15) * HD + 8 * (lane >> 4)) * 2;
+  const int vofs = ((lane >> 4) * HD + 8 * (lane & 15)) * 2;
+#pragma unroll
+  for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      br.k[kq][s] = __builtin_amdgcn_raw_buffer_load_b128(rk[kq], kofs + 32 * s * 2, 0,
+                                                          kStreamPolicy);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    br.v[e] = __builtin_amdgcn_raw_buffer_load_b128(rv[e >> 2], vofs + 4 * (e & 3) * HD * 2, 0,
+                                                    kStreamPolicy);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool CAP, bool PAGED>
 __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs da) {
   __shared__ SplitSmem sm;
   const AttnArgs& a = da.a;
@@ -185,7 +237,7 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
   // ---- plan: items of sequence i = Hkv * (splits of its window); exclusive prefix in LDS -------
   for (int i = tid; i < B; i += DT) {
     const int n = min(max(a.lens[i], 0), a.S);
-    const int start = first_key(a, n);
+    const int start = walk_start(a, n, PAGED);
     sm.len[i] = n;
     sm.plan[i] = ((n - start + SPLIT - 1) / SPLIT) * Hkv;
   }
@@ -222,7 +274,7 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
     Item it;
     it.valid = t < total;
     if (!it.valid) {
-      it.b = it.g = it.sp = it.ws = it.we = it.nblk = 0;
+      it.b = it.g = it.sp = it.ws = it.we = it.nblk = it.klo = 0;
       return it;
     }
     int lo = 0, hi = B;
@@ -239,7 +291,8 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
     it.b = lo;
     it.g = r / nsp;
     it.sp = r - it.g * nsp;
-    const int start = first_key(a, n);
+    const int start = walk_start(a, n, PAGED);
+    it.klo = first_key(a, n);
     const int ks = start + it.sp * SPLIT;
     const int ke = min(ks + SPLIT, n);
     it.ws = ks + w * SUB;
@@ -276,7 +329,7 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
   float m, lsum;
   bf16x8 qop[4];
 
-  auto block = [&](const BlockRegs& cur, int kb0, int we) {
+  auto block = [&](const BlockRegs& cur, int kb0, int we, int klo) {
     // stage V rows of this block in the wave's LDS buffer
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -305,7 +358,7 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
           x = copysignf(cap2 * (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e), y);
         }
         const int key = kb0 + kq * 16 + 4 * (lane >> 4) + r;
-        sk[kq][r] = key < we ? x : -INFINITY;
+        sk[kq][r] = (key < we && (!PAGED || key >= klo)) ? x : -INFINITY;
       }
 
     float mt = fmaxf(fmaxf(fmaxf(sk[0][0], sk[0][1]), fmaxf(sk[0][2], sk[0][3])),
@@ -384,6 +437,14 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
     __builtin_amdgcn_raw_buffer_store_b64(mlw, rml, tid < MAXG ? row * 8 : INT32_MIN, 0, 0);
   };
 
+  auto load_blk = [&](const Item& it, __amdgpu_buffer_rsrc_t rk_, __amdgpu_buffer_rsrc_t rv_,
+                      int kb0, BlockRegs& br) {
+    if (PAGED)
+      load_block_paged(da, it.b, it.g, it.we, it.klo, kb0, br);
+    else
+      load_block(rk_, rv_, kb0, br);
+  };
+
   // ---- the item loop ----
   int t = blockIdx.x;
   Item cur = locate(t);
@@ -391,7 +452,7 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
   u32x4 qv[4];
   load_q(q_rsrc(cur), qv);
   BlockRegs ra;
-  load_block(rk, rv, cur.ws, ra);
+  load_blk(cur, rk, rv, cur.ws, ra);
   // partial-output descriptors of the previous item: none before the first
   __amdgpu_buffer_rsrc_t ro = rsrc(da.part_o, 0), rml = rsrc(da.part_ml, 0);
   while (true) {
@@ -407,10 +468,10 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
     for (int db = 0; db < 8; ++db) o[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
     m = kNegBig;
     lsum = 0.f;
-    block(ra, cur.ws, cur.we);  // (all keys masked when this wavefront has none)
+    block(ra, cur.ws, cur.we, cur.klo);  // (all keys masked when this wavefront has none)
     for (int i = 1; i < cur.nblk; ++i) {
-      load_block(rk, rv, cur.ws + i * KBLK, ra);
-      block(ra, cur.ws + i * KBLK, cur.we);
+      load_blk(cur, rk, rv, cur.ws + i * KBLK, ra);
+      block(ra, cur.ws + i * KBLK, cur.we, cur.klo);
     }
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
@@ -433,7 +494,7 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
     rk = kv_rsrc(cur, a.k);
     rv = kv_rsrc(cur, a.v);
     load_q(q_rsrc(cur), qv);
-    load_block(rk, rv, cur.ws, ra);
+    load_blk(cur, rk, rv, cur.ws, ra);
     if (!cur.valid) {
       lds_barrier();
       merge_store(ro, rml);
@@ -454,7 +515,7 @@ __global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs da) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int G = a.G, g = h / G, hs = h % G;
   const int n = min(max(a.lens[b], 0), a.S);
-  const int start = first_key(a, n);
+  const int start = walk_start(a, n, da.table != nullptr);
   const int nsp = (n - start + SPLIT - 1) / SPLIT;
   const int64_t item0 = (((int64_t)b * a.Hkv + g) * da.nsplit) * G + hs;
   const float* ml = da.part_ml;
@@ -538,10 +599,15 @@ size_t decode_mfma_workspace_bytes(int B, int Hkv, int G, int D, int Smax) {
          (size_t)B * Hkv * G * D * sizeof(uint16_t);
 }
 
-hipError_t launch_decode_mfma(const AttnArgs& a, void* workspace, hipStream_t stream) {
+hipError_t launch_decode_mfma(const AttnArgs& a, void* workspace, hipStream_t stream,
+                              const PagedKV* paged) {
   if (a.B == 0) return hipSuccess;
   DecodeArgs d;
   d.a = a;
+  d.table = paged ? paged->table : nullptr;
+  d.max_blocks = paged ? paged->max_blocks : 0;
+  d.log2bs = paged ? paged->log2bs : 0;
+  d.num_blocks = paged ? paged->num_blocks : 0;
   d.nsplit = (a.S + SPLIT - 1) / SPLIT;
   const int64_t items = (int64_t)a.B * a.Hkv * d.nsplit * a.G;
   char* ws = (char*)workspace;
@@ -578,10 +644,19 @@ hipError_t launch_decode_mfma(const AttnArgs& a, void* workspace, hipStream_t st
     c.part_ml = d.part_ml + (int64_t)b0 * per_seq * a.G * 2;
     c.qprep = d.qprep + (int64_t)b0 * a.Hq * HD;
     const int nwg = (int)std::min<int64_t>((int64_t)nb * per_seq, resident);
-    if (a.softcap > 0.f)
-      hipLaunchKernelGGL(decode_split_kernel<true>, dim3(nwg), dim3(DT), 0, stream, c);
-    else
-      hipLaunchKernelGGL(decode_split_kernel<false>, dim3(nwg), dim3(DT), 0, stream, c);
+    if (d.table) {
+      c.a.k = a.k;  // the pools are shared by all sequences
+      c.a.v = a.v;
+      c.table = d.table + (int64_t)b0 * d.max_blocks;
+      if (a.softcap > 0.f)
+        hipLaunchKernelGGL((decode_split_kernel<true, true>), dim3(nwg), dim3(DT), 0, stream, c);
+      else
+        hipLaunchKernelGGL((decode_split_kernel<false, true>), dim3(nwg), dim3(DT), 0, stream, c);
+    } else if (a.softcap > 0.f) {
+      hipLaunchKernelGGL((decode_split_kernel<true, false>), dim3(nwg), dim3(DT), 0, stream, c);
+    } else {
+      hipLaunchKernelGGL((decode_split_kernel<false, false>), dim3(nwg), dim3(DT), 0, stream, c);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

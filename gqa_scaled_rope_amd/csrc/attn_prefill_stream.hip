@@ -155,8 +155,12 @@ __device__ __forceinline__ float row16_sum(float s) {
 
 // Rows (b, p, h) for position indices p in [p0, pend) of a [B, *, H, 128] bf16 source are normed
 // (gain w), rotated at pos[b * pos_b + p] and multiplied by mul, then stored as bf16 at
-// dst + b*db + (p - pofs)*dp + h*128.  Rows with p < fresh_from are copied as stored.
+// dst + b*db + (p - pofs)*dp + h*128 -- or, with a block table, at slot slot0[b] + p - p0 of a
+// paged pool dst [num_blocks, H, 2^log2bs, 128].  Rows with p < fresh_from are copied as stored.
 struct RowJob {
+  const int32_t* ptable;  // paged destination when non-null
+  const int32_t* slot0;
+  int32_t pmax_blocks, plog2bs, pnum_blocks;
   const uint16_t* src;
   int64_t sb, sp, sh;
   uint16_t* dst;
@@ -270,8 +274,21 @@ __global__ __launch_bounds__(256) void rows_prep_kernel(AttnArgs a, RowJob jb) {
       for (int e = 0; e < 8; ++e) x[e] *= jb.mul;
     }
     if (valid && h0 + k < jb.H) {
-      uint16_t* dst =
-          jb.dst + (int64_t)b * jb.db + (int64_t)(p - jb.pofs) * jb.dp + (int64_t)(h0 + k) * HD;
+      uint16_t* dst;
+      if (jb.ptable) {
+        // slot and table index clamped into the table: a violated precondition writes wrong
+        // slots, never outside the pool
+        const int64_t cap = (int64_t)jb.pmax_blocks << jb.plog2bs;
+        const int64_t slot = min<int64_t>(max<int64_t>((int64_t)jb.slot0[b] + (p - jb.p0), 0),
+                                          cap - 1);
+        int phys = jb.ptable[(int64_t)b * jb.pmax_blocks + (slot >> jb.plog2bs)];
+        phys = min(max(phys, 0), jb.pnum_blocks - 1);
+        const int64_t row = ((((int64_t)phys * jb.H + h0 + k) << jb.plog2bs) |
+                             (slot & ((1 << jb.plog2bs) - 1)));
+        dst = jb.dst + row * HD;
+      } else {
+        dst = jb.dst + (int64_t)b * jb.db + (int64_t)(p - jb.pofs) * jb.dp + (int64_t)(h0 + k) * HD;
+      }
       *(u32x4*)(dst + 8 * c) = pack8(x);
     }
   }
@@ -834,7 +851,7 @@ hipError_t dispatch_rows(const AttnArgs& a, const RowJob& jb, bool norm, hipStre
 // Keys j0 .. S-1: the new ones (j >= n_cached) normed and rotated, the others copied as stored.
 hipError_t dispatch_prep(const AttnArgs& a, const PrepOut& po, hipStream_t stream) {
   if (a.R == 0 && !a.qk_norm && po.p == (uint16_t*)a.k) return hipSuccess;  // nothing to do
-  RowJob jb;
+  RowJob jb{};
   jb.src = (const uint16_t*)a.k;
   jb.sb = a.k_b;
   jb.sp = a.k_j;
@@ -855,6 +872,38 @@ hipError_t dispatch_prep(const AttnArgs& a, const PrepOut& po, hipStream_t strea
 }
 
 }  // namespace
+
+hipError_t launch_paged_append(const AttnArgs& a, const PagedKV& kv, void* k_pool, void* v_pool,
+                               const int32_t* start, hipStream_t stream) {
+  RowJob jb{};
+  jb.ptable = kv.table;
+  jb.slot0 = start;
+  jb.pmax_blocks = kv.max_blocks;
+  jb.plog2bs = kv.log2bs;
+  jb.pnum_blocks = kv.num_blocks;
+  jb.pos = a.kpos;
+  jb.pos_b = a.kpos_b;
+  jb.w = (const uint16_t*)a.kw;
+  jb.H = a.Hkv;
+  jb.p0 = 0;
+  jb.pend = a.L;
+  jb.pofs = 0;
+  jb.fresh_from = 0;
+  jb.mul = 1.0f;
+  // keys: norm and rotation; values: copied
+  jb.src = (const uint16_t*)a.k;
+  jb.sb = a.k_b;
+  jb.sp = a.k_j;
+  jb.sh = a.k_h;
+  jb.dst = (uint16_t*)k_pool;
+  hipError_t e = dispatch_rows(a, jb, a.qk_norm != 0, stream);
+  if (e != hipSuccess) return e;
+  AttnArgs av = a;
+  av.R = 0;
+  jb.src = (const uint16_t*)a.v;
+  jb.dst = (uint16_t*)v_pool;
+  return dispatch_rows(av, jb, false, stream);
+}
 
 bool prep_keys_supported(const AttnArgs& a) {
   if (a.D != HD) return false;

@@ -491,4 +491,135 @@ gqa_status gqa_attn_decode(const gqa_attn_cfg* cfg, const void* q, const void* k
                     "decode (generic) launch");
 }
 
+static gqa_status check_paged(const gqa_attn_cfg* cfg, const gqa_paged_kv* kv, gqa::PagedKV* out) {
+  if (!kv) return fail(GQA_E_NULL, "paged kv pointer is null");
+  if (!kv->k_pool || !kv->v_pool || !kv->block_table)
+    return fail(GQA_E_NULL, "k_pool, v_pool and block_table are required");
+  if (!aligned16(kv->k_pool) || !aligned16(kv->v_pool))
+    return fail(GQA_E_VALUE, "k_pool and v_pool must be 16-byte aligned");
+  const int bs = kv->block_size;
+  if (bs < 16 || bs > 1024 || (bs & (bs - 1)))
+    return fail(GQA_E_VALUE, "block_size must be a power of two in [16, 1024], got %d", bs);
+  if (kv->max_blocks < 1 || kv->num_blocks < 1)
+    return fail(GQA_E_SHAPE, "max_blocks and num_blocks must be >= 1, got %d, %d", kv->max_blocks,
+                kv->num_blocks);
+  if ((int64_t)kv->max_blocks * bs * cfg->head_dim * 2 > INT32_MAX)
+    return fail(GQA_E_SHAPE, "max_blocks * block_size is too large (%d * %d)", kv->max_blocks, bs);
+  if (kv->reserved != 0) return fail(GQA_E_VALUE, "paged kv reserved field must be 0");
+  if (cfg->dtype != GQA_BF16 || cfg->head_dim != 128)
+    return fail(GQA_E_UNSUPPORTED, "the paged pool takes bf16 with head_dim 128");
+  out->table = kv->block_table;
+  out->max_blocks = kv->max_blocks;
+  int l2 = 0;
+  while ((1 << l2) < bs) ++l2;
+  out->log2bs = l2;
+  out->num_blocks = kv->num_blocks;
+  return ok();
+}
+
+gqa_status gqa_paged_append(const gqa_attn_cfg* cfg, const gqa_paged_kv* kv, const void* k_new,
+                            const void* v_new, const int32_t* key_positions,
+                            int64_t kpos_batch_stride, const int32_t* start, int32_t B, int32_t L,
+                            hipStream_t stream) {
+  gqa_status st = check_cfg(cfg);
+  if (st != GQA_OK) return st;
+  gqa::PagedKV pk;
+  st = check_paged(cfg, kv, &pk);
+  if (st != GQA_OK) return st;
+  if (B < 0 || L < 0) return fail(GQA_E_SHAPE, "B and L must be >= 0, got %d, %d", B, L);
+  if (B > 65535) return fail(GQA_E_SHAPE, "B must be <= 65535, got %d", B);
+  if ((int64_t)L * cfg->num_kv_heads > INT32_MAX / 8)
+    return fail(GQA_E_SHAPE, "L * num_kv_heads is too large");
+  if (kpos_batch_stride < 0) return fail(GQA_E_SHAPE, "kpos_batch_stride must be >= 0");
+  gqa::AttnArgs a = base_args(cfg);
+  if (!gqa::prep_keys_supported(a))
+    return fail(GQA_E_UNSUPPORTED, "paged append covers the rotary widths of gqa_prep_keys");
+  if (B == 0 || L == 0) return ok();
+  if (!k_new || !v_new || !start || (cfg->rotary_dim > 0 && !key_positions))
+    return fail(GQA_E_NULL, "k_new, v_new, start and (with rotation) key_positions are required");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(GQA_E_VALUE, "k_new and v_new must be 16-byte aligned");
+  const int64_t D = cfg->head_dim;
+  a.k = k_new;
+  a.v = v_new;
+  a.k_h = D;
+  a.k_j = (int64_t)a.Hkv * D;
+  a.k_b = (int64_t)L * a.k_j;
+  a.kpos = key_positions;
+  a.kpos_b = kpos_batch_stride;
+  a.B = B;
+  a.L = L;
+  a.S = L;
+  a.n_cached = 0;
+  return hip_status(gqa::launch_paged_append(a, pk, kv->k_pool, kv->v_pool, start, stream),
+                    "paged append launch");
+}
+
+size_t gqa_paged_decode_workspace_bytes(const gqa_attn_cfg* cfg, const gqa_paged_kv* kv,
+                                        int32_t B) {
+  if (check_cfg(cfg) != GQA_OK) return 0;
+  gqa::PagedKV pk;
+  if (check_paged(cfg, kv, &pk) != GQA_OK) return 0;
+  if (B < 0) {
+    fail(GQA_E_SHAPE, "B must be >= 0, got %d", B);
+    return 0;
+  }
+  if (cfg->num_q_heads / cfg->num_kv_heads > 16) {
+    fail(GQA_E_UNSUPPORTED, "paged decode takes at most 16 query heads per KV head");
+    return 0;
+  }
+  return gqa::decode_mfma_workspace_bytes(B, cfg->num_kv_heads,
+                                          cfg->num_q_heads / cfg->num_kv_heads, cfg->head_dim,
+                                          kv->max_blocks * kv->block_size);
+}
+
+gqa_status gqa_attn_decode_paged(const gqa_attn_cfg* cfg, const void* q, const gqa_paged_kv* kv,
+                                 const int32_t* lens, int32_t B, int32_t window, void* out,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  gqa_status st = check_cfg(cfg);
+  if (st != GQA_OK) return st;
+  gqa::PagedKV pk;
+  st = check_paged(cfg, kv, &pk);
+  if (st != GQA_OK) return st;
+  if (B < 0) return fail(GQA_E_SHAPE, "B must be >= 0, got %d", B);
+  if (B > 65535) return fail(GQA_E_SHAPE, "B must be <= 65535, got %d", B);
+  if (window < 0) return fail(GQA_E_SHAPE, "window must be >= 0, got %d", window);
+  gqa::AttnArgs a = base_args(cfg);
+  const int Smax = kv->max_blocks * kv->block_size;
+  a.S = Smax;
+  if (!gqa::decode_mfma_supported(a))
+    return fail(GQA_E_UNSUPPORTED, "paged decode takes at most 16 query heads per KV head");
+  if (B == 0) return ok();
+  if (!q || !lens || !out) return fail(GQA_E_NULL, "q, lens and out are required");
+  if (!aligned16(q) || !aligned16(out)) return fail(GQA_E_VALUE, "q and out must be 16-byte aligned");
+  const size_t need = gqa::decode_mfma_workspace_bytes(B, a.Hkv, a.G, cfg->head_dim, Smax);
+  if (!workspace || workspace_bytes < need)
+    return fail(GQA_E_WORKSPACE, "paged decode needs a workspace of %zu bytes, got %zu%s", need,
+                workspace_bytes, workspace ? "" : " (null)");
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(GQA_E_WORKSPACE, "workspace must be 256-byte aligned");
+  const int64_t D = cfg->head_dim;
+  a.q = q;
+  a.k = kv->k_pool;
+  a.v = kv->v_pool;
+  a.out = out;
+  a.q_h = D;
+  a.q_i = 0;
+  a.q_b = (int64_t)a.Hq * D;
+  a.o_h = D;
+  a.o_i = 0;
+  a.o_b = a.q_b;
+  a.k_j = D;
+  a.k_h = 0;
+  a.k_b = 0;
+  a.qpos = nullptr;
+  a.kpos = nullptr;
+  a.lens = lens;
+  a.B = B;
+  a.L = 1;
+  a.n_cached = Smax;
+  a.window = window;
+  return hip_status(gqa::launch_decode_mfma(a, workspace, stream, &pk), "paged decode launch");
+}
+
 }  // extern "C"

@@ -34,11 +34,25 @@ hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t
 bool prep_keys_supported(const AttnArgs& a);
 hipError_t launch_prep_keys(const AttnArgs& a, void* k_out, hipStream_t stream);
 
+// Paged KV pool: pools [num_blocks, Hkv, 2^log2bs, D]; slot j of sequence b is row j % bs of
+// block table[b * max_blocks + j / bs] (entries are clamped into [0, num_blocks)).
+struct PagedKV {
+  const int32_t* table;
+  int32_t max_blocks, log2bs, num_blocks;
+};
+
 // bf16 split-KV decode for head_dim 128 (query preparation, split kernel, combine kernel); the
-// workspace holds the split partials and the prepared queries.
+// workspace holds the split partials and the prepared queries.  With `paged`, a.k and a.v are
+// the pools and a.S = max_blocks * block size.
 bool decode_mfma_supported(const AttnArgs& a);
 size_t decode_mfma_workspace_bytes(int B, int Hkv, int G, int D, int Smax);
-hipError_t launch_decode_mfma(const AttnArgs& a, void* workspace, hipStream_t stream);
+hipError_t launch_decode_mfma(const AttnArgs& a, void* workspace, hipStream_t stream,
+                              const PagedKV* paged = nullptr);
+
+// cache.update into a paged pool: rows i < a.L of a.k (normed and rotated at a.kpos, as the key
+// preparation does) and of a.v (copied) go to slots start[b] + i.
+hipError_t launch_paged_append(const AttnArgs& a, const PagedKV& kv, void* k_pool, void* v_pool,
+                               const int32_t* start, hipStream_t stream);
 int decode_split_keys();
 
 }  // namespace gqa

@@ -210,6 +210,52 @@ gqa_status gqa_attn_decode(const gqa_attn_cfg* cfg, const void* q, const void* k
                            int32_t window, void* out, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* Paged KV pool (the block manager's layout behind cache.update: [Models] "What differs" (the
+ * cache.update call), "Sliding windows" (blocks that leave every window can be recycled) and the
+ * multi-head latent attention section's paged pool; [Guide] section 3.3 for what the cache holds).
+ *   k_pool, v_pool  device [num_blocks, Hkv, block_size, D] in cfg.dtype, caller-owned
+ *   block_table     device int32 [B, max_blocks]: slot j of sequence b (the key at position j) is
+ *                   row j % block_size of physical block block_table[b * max_blocks + j /
+ *                   block_size]
+ *   block_size      a power of two in [16, 1024]
+ *   num_blocks      blocks in each pool; table entries are clamped into [0, num_blocks), so a bad
+ *                   entry reads or writes a wrong block, never outside the pools
+ * Only the entries of blocks that hold a visible slot are read: with a window (or chunks) the
+ * entries of blocks wholly before it may be stale or reused for other sequences (recycling). */
+typedef struct gqa_paged_kv {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* block_table;
+  int32_t max_blocks;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t reserved;  /* must be 0 */
+} gqa_paged_kv;
+
+/* cache.update with the key preparation fused in ([Models] "What differs": k-norm, rotation,
+ * then cache.update; [Guide] section 3.3 update): rows k_new, v_new device [B, L, Hkv, D]
+ * (contiguous) go to slots start[b] .. start[b] + L - 1 of each sequence; each key row is
+ * RMS-normed with cfg.k_norm_w when cfg.qk_norm, then rotated at key_positions[b *
+ * kpos_batch_stride + i]; value rows are copied.  start: device int32 [B] (the sequences' lengths
+ * before the append); start[b] + L <= max_blocks * block_size is the caller's to keep (slots past
+ * it are clamped into the table).  bf16, head_dim 128 and the rotary widths of gqa_prep_keys. */
+gqa_status gqa_paged_append(const gqa_attn_cfg* cfg, const gqa_paged_kv* kv, const void* k_new,
+                            const void* v_new, const int32_t* key_positions,
+                            int64_t kpos_batch_stride, const int32_t* start, int32_t B, int32_t L,
+                            hipStream_t stream);
+
+/* Bytes of device workspace gqa_attn_decode_paged needs (0 on invalid arguments). */
+size_t gqa_paged_decode_workspace_bytes(const gqa_attn_cfg* cfg, const gqa_paged_kv* kv,
+                                        int32_t B);
+
+/* gqa_attn_decode over a paged pool: sequence b's keys are its slots 0 .. lens[b]-1, the query
+ * sits at position lens[b]-1 and is normed and rotated there; 1 <= lens[b] <= max_blocks *
+ * block_size.  q, out device [B, Hq, D].  bf16, head_dim 128, Hq/Hkv <= 16; workspace as for
+ * gqa_attn_decode.  Two calls that share a workspace must be ordered on one stream. */
+gqa_status gqa_attn_decode_paged(const gqa_attn_cfg* cfg, const void* q, const gqa_paged_kv* kv,
+                                 const int32_t* lens, int32_t B, int32_t window, void* out,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Kernel selection, for tests and comparisons: 0 (default) = bf16 problems run on the MFMA
  * kernels wherever their shape is covered; 1 = every problem runs on the generic kernel (one
  * wavefront per query row and head, fp32 arithmetic).  Process-wide; not thread-safe. */

@@ -194,6 +194,19 @@ def draw_sinks(wl: Workload, seed=None):
     return s
 
 
+def paged_pool_inputs(B, Hkv, D, block_size, max_blocks, dtype="bf16", spare=4, seed=0):
+    """A paged KV pool with room for every sequence's max_blocks blocks plus `spare` blocks:
+    k_pool, v_pool [B * max_blocks + spare, Hkv, block_size, D] of N(0, 1) draws rounded to the
+    run dtype, and a block table [B, max_blocks] that is a seeded random permutation of the first
+    B * max_blocks of all blocks (the remaining spares stay unreferenced)."""
+    rng = np.random.default_rng([seed, 424242])
+    nb = B * max_blocks + spare
+    kp = round_to(rng.standard_normal((nb, Hkv, block_size, D), dtype=np.float32), dtype)
+    vp = round_to(rng.standard_normal((nb, Hkv, block_size, D), dtype=np.float32), dtype)
+    table = rng.permutation(nb)[: B * max_blocks].reshape(B, max_blocks).astype(np.int32)
+    return kp, vp, table
+
+
 def rope_params(wl: Workload):
     """Keyword arguments describing the rotation (plain data)."""
     return dict(rotary_dim=wl.rotary_dim, theta=wl.theta, kind=wl.rope_kind, factor=wl.factor,

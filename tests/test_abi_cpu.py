@@ -284,7 +284,8 @@ def test_c_struct_layout_matches_ctypes(tmp_path):
     if shutil.which("gcc") is None:
         pytest.skip("gcc not available")
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    fields = {"gqa_attn_cfg": g._AttnCfg, "gqa_rope_params": g._RopeParams}
+    fields = {"gqa_attn_cfg": g._AttnCfg, "gqa_rope_params": g._RopeParams,
+              "gqa_paged_kv": g._PagedKV}
     lines = []
     for cname, py in fields.items():
         lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -305,3 +306,56 @@ def test_c_struct_layout_matches_ctypes(tmp_path):
         py = fields[cname]
         want = ctypes.sizeof(py) if what == "size" else getattr(py, what).offset
         assert int(val) == want, line
+
+
+def _paged(**kw):
+    base = dict(k_pool=FAKE, v_pool=FAKE, block_table=FAKE, max_blocks=8, block_size=16,
+                num_blocks=32, reserved=0)
+    base.update(kw)
+    p = g._PagedKV()
+    for k, v in base.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(block_size=24), 7, "power of two"),
+    (dict(block_size=8), 7, "power of two"),
+    (dict(block_size=2048), 7, "power of two"),
+    (dict(max_blocks=0), 2, "max_blocks"),
+    (dict(num_blocks=0), 2, "num_blocks"),
+    (dict(k_pool=None), 1, "k_pool"),
+    (dict(block_table=None), 1, "block_table"),
+    (dict(v_pool=FAKE + 8), 7, "aligned"),
+    (dict(reserved=3), 7, "reserved"),
+])
+def test_paged_validation(kw, status, msg):
+    c = _cfg()
+    kv = _paged(**kw)
+    st = lib.gqa_attn_decode_paged(ctypes.byref(c), FAKE, ctypes.byref(kv), FAKE, 2, 0, FAKE, FAKE,
+                                   1 << 30, None)
+    assert st == status and msg in g.last_error()
+    st = lib.gqa_paged_append(ctypes.byref(c), ctypes.byref(kv), FAKE, FAKE, FAKE, 0, FAKE, 2, 1,
+                              None)
+    assert st == status and msg in g.last_error()
+    assert lib.gqa_paged_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(kv), 2) == 0
+
+
+def test_paged_workspace_and_support():
+    c = _cfg()
+    kv = _paged()
+    # same split partials as a contiguous cache of max_blocks * block_size slots
+    assert (lib.gqa_paged_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(kv), 64) ==
+            lib.gqa_decode_workspace_bytes(ctypes.byref(c), 64, 8 * 16))
+    assert lib.gqa_attn_decode_paged(ctypes.byref(_cfg(dtype=0)), FAKE, ctypes.byref(kv), FAKE, 2,
+                                     0, FAKE, FAKE, 1 << 30, None) == 4
+    assert lib.gqa_attn_decode_paged(ctypes.byref(_cfg(num_q_heads=64, num_kv_heads=2)), FAKE,
+                                     ctypes.byref(kv), FAKE, 2, 0, FAKE, FAKE, 1 << 30, None) == 4
+    need = lib.gqa_paged_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(kv), 2)
+    assert lib.gqa_attn_decode_paged(ctypes.byref(c), FAKE, ctypes.byref(kv), FAKE, 2, 0, FAKE,
+                                     FAKE, need - 1, None) == 5
+    # empty problems are no-ops
+    assert lib.gqa_attn_decode_paged(ctypes.byref(c), None, ctypes.byref(kv), None, 0, 0, None,
+                                     None, 0, None) == 0
+    assert lib.gqa_paged_append(ctypes.byref(c), ctypes.byref(kv), None, None, None, 0, None, 3, 0,
+                                None) == 0

@@ -556,3 +556,101 @@ def test_decode_rope_schedules(name, policy):
                              q_norm_w=qw, eps=wl.eps, softcap=wl.softcap, attention_factor=af,
                              scale=sc)
     check(out.float().cpu().numpy(), ref, head_axis=1)
+
+
+# ----------------------------------------------------------------------------------------------
+# Paged KV pool: the fused append (cache.update) and decode through block tables
+# ----------------------------------------------------------------------------------------------
+from synth import paged_pool_inputs, round_to  # noqa: E402
+
+
+def _paged_kv(kp, vp, table):
+    return g.PagedKV(dev(kp), dev(vp), dev(table, torch.int32))
+
+
+@pytest.mark.parametrize("bs,L,R,style,norm", [
+    (16, 1, 128, "half", True), (64, 37, 64, "interleaved", False), (32, 50, 128, "half", False),
+    (16, 20, 0, "half", True), (128, 3, 32, "half", True),
+])
+def test_paged_append_matches_oracle(bs, L, R, style, norm):
+    B, Hkv, D = 3, 2, 128
+    start = np.array([0, 5, 77], np.int32)
+    max_blocks = (int(start.max()) + L + bs - 1) // bs + 1
+    say("paged append", bs, L, R, style, norm)
+    kp, vp, table = paged_pool_inputs(B, Hkv, D, bs, max_blocks, seed=bs + L)
+    r = np.random.default_rng(bs * 7 + L)
+    k_new = round_to(r.standard_normal((B, L, Hkv, D)).astype(np.float32), "bf16")
+    v_new = round_to(r.standard_normal((B, L, Hkv, D)).astype(np.float32), "bf16")
+    kw = round_to((1.0 + 0.02 * r.standard_normal(D)).astype(np.float32), "bf16")
+    kpos = (start[:, None] + np.arange(L)[None, :]).astype(np.int32)
+    wl = BASE.with_(Hq=4, Hkv=Hkv, rotary_dim=R, style=style, theta=1e4, qk_norm=norm)
+    tl = int(kpos.max()) + 1
+    cos, sin = g.rope_tables(spec(wl), tl) if R else (None, None)
+    cfg = g.AttnConfig("bf16", D, 4, Hkv, R, style, cos, sin, norm, wl.eps,
+                       dev(kw) if norm else None, dev(kw) if norm else None)
+    kv = _paged_kv(kp, vp, table)
+    g.paged_append(cfg, kv, dev(k_new), dev(v_new), dev(kpos, torch.int32),
+                   dev(start, torch.int32))
+    torch.cuda.synchronize()
+    got_k = kv.k_pool.float().cpu().numpy()
+    got_v = kv.v_pool.float().cpu().numpy()
+    rows = oracle.append_rows(k_new, kpos, inv_freq=inv_freq(wl), style=style,
+                              k_norm_w=kw if norm else None, eps=wl.eps)
+    ref_k = oracle.paged_update(kp, table, start, rows, bs)
+    ref_v = oracle.paged_update(vp, table, start, v_new, bs)
+    np.testing.assert_array_equal(got_v, ref_v)                       # values: copied
+    np.testing.assert_allclose(got_k, ref_k, rtol=2 ** -8, atol=1e-6)  # keys: one bf16 rounding
+    written = oracle.paged_update(np.zeros(kp.shape, bool), table, start,
+                                  np.ones(k_new.shape, bool), bs)
+    np.testing.assert_array_equal(got_k[~written], kp[~written])      # other slots untouched
+
+
+PAGED_DEC = {
+    "bs16": (16, {}),
+    "bs32_window": (32, dict(window=300)),
+    "bs256_sinks_chunk": (256, dict(chunk=500, chunk_lookback=1, sinks=True)),
+    "bs16_window_recycled": (16, dict(window=100)),
+    "bs64_cap_G16_recycled": (64, dict(softcap=5.0, Hq=32, Hkv=2, window=700)),
+    "bs128_qknorm_interleaved": (128, dict(qk_norm=True, rotary_dim=64, style="interleaved",
+                                           rope_kind="default", theta=1e4)),
+}
+
+
+@pytest.mark.parametrize("name", list(PAGED_DEC))
+def test_paged_decode_matches_oracle(name):
+    bs, kw = PAGED_DEC[name]
+    wl = DEC.with_(**kw)
+    say("paged decode", name)
+    lens, q, qw = decode_lens_q(wl, seed=29)
+    lens[0], lens[1] = 1, wl.S
+    max_blocks = (wl.S + bs - 1) // bs
+    kp, vp, table = paged_pool_inputs(wl.B, wl.Hkv, wl.D, bs, max_blocks, spare=1, seed=bs)
+    gpu_table = table.copy()
+    if name.endswith("recycled"):
+        # the one spare block is poisoned with NaN; blocks wholly before a sequence's window and
+        # wholly past its length point there, as recycled (or unused) entries may: the kernel must
+        # never read them
+        nan_blk = kp.shape[0] - 1
+        kp[nan_blk] = np.nan
+        vp[nan_blk] = np.nan
+        for b in range(wl.B):
+            n = int(lens[b])
+            first = max(0, n - wl.window) if wl.window else 0
+            for i in range(max_blocks):
+                if (i + 1) * bs <= first or i * bs >= n:
+                    gpu_table[b, i] = nan_blk
+    cos, sin = g.rope_tables(spec(wl), wl.S)
+    cfg = g.AttnConfig(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
+                       wl.qk_norm, wl.eps, dev(qw) if wl.qk_norm else None,
+                       dev(qw) if wl.qk_norm else None, 0.0, wl.softcap, **cfg_extra(wl))
+    out = g.attn_decode_paged(cfg, dev(q), _paged_kv(kp, vp, gpu_table), dev(lens, torch.int32),
+                              wl.window)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    kpf = np.nan_to_num(kp)
+    vpf = np.nan_to_num(vp)
+    ref = oracle.attn_decode_paged(q, kpf, vpf, table, lens, bs, inv_freq=inv_freq(wl),
+                                   style=wl.style, window=wl.window, q_norm_w=qw, eps=wl.eps,
+                                   softcap=wl.softcap, **mask_kw(wl))
+    check(got, ref, head_axis=1)
