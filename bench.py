@@ -202,6 +202,43 @@ def run_decode(wl, steps, warmup, torch, g):
     return x, sum(ms) / len(ms), ms[len(ms) // 2]
 
 
+def run_decode_paged(wl, dx, block_size, steps, warmup, torch, g):
+    """The decode workload again, its cache rows moved into a paged pool of block_size slots per
+    block whose blocks are laid out in a seeded random order (a block table per sequence)."""
+    B, Hkv, Smax, D = (int(t) for t in dx["k"].shape)
+    nbps = (Smax + block_size - 1) // block_size
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(1234 + block_size)
+    perm = torch.randperm(B * nbps, generator=gen).to("cuda")
+    table = perm.view(B, nbps).to(torch.int32).contiguous()
+
+    def to_pool(cache):
+        blocks = cache.view(B, Hkv, nbps, block_size, D).permute(0, 2, 1, 3, 4).reshape(
+            B * nbps, Hkv, block_size, D)
+        pool = torch.empty_like(blocks)
+        pool[perm] = blocks
+        return pool
+    kv = g.PagedKV(to_pool(dx["k"]), to_pool(dx["v"]), table)
+    cfg = dx["cfg"]
+    ws = torch.empty(g.paged_decode_workspace_bytes(cfg, kv, B), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(dx["q"])
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        g.attn_decode_paged(cfg, dx["q"], kv, dx["lens"], wl.window, out, ws)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        g.attn_decode_paged(cfg, dx["q"], kv, dx["lens"], wl.window, out, ws)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    same = bool(torch.equal(out, dx["out"]))
+    del kv, ws
+    return sum(ms) / len(ms), ms[len(ms) // 2], same
+
+
 def cpu_baseline_prefill(wl, x, torch, budget_s=15.0):
     """Time the oracle on a bounded sample -- whole sequences, in order, until about budget_s of
     CPU time -- check the GPU output on the same sample, and report the rate in TFLOP/s."""
@@ -295,6 +332,9 @@ def main(argv=None):
     ap.add_argument("--decode-workload", default="llama31_decode_bf16")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--paged-block", type=int, default=16, metavar="N",
+                    help="also time the decode workload through a paged pool of N-slot blocks "
+                         "(0: skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (three times), the "
                          "known-size reference for scaling HBM byte counters")
@@ -375,6 +415,16 @@ def main(argv=None):
                             "kernel_ms_mean": round(dms, 4), "kernel_ms_median": round(dmed, 4)}}
         if not args.no_cpu_baseline:
             dec["cpu_baseline"] = cpu_baseline_decode(dwl, dx, torch)
+        if args.paged_block:
+            pms, pmed, same = run_decode_paged(dwl, dx, args.paged_block, args.steps, args.warmup,
+                                               torch, g)
+            pgbs = nbytes / (pms * 1e-3) / 1e9
+            log(f"[bench] paged decode (blocks of {args.paged_block}) {pms:.3f} ms -> "
+                f"{pgbs:.0f} GB/s, bit-identical to the contiguous cache: {same}")
+            dec["paged"] = {"block_size": args.paged_block, "value": round(pgbs, 1), "unit": "GB/s",
+                            "ms_per_call": round(pms, 4), "ms_median": round(pmed, 4),
+                            "frac": round(pgbs / HBM_PEAK_GBS, 4),
+                            "identical_to_contiguous": same}
         line["decode"] = dec
     print(json.dumps(line), flush=True)
     return 0
