@@ -26,8 +26,9 @@ and without lookback, floor chunks of negative positions); the sink's closed for
 logistic weight; constant values: the share the keys keep) and torch's SDPA with the sink as one
 more key; chunks without lookback restarting the sequence; paged rows equal the contiguous
 cache under identity and permuted block tables, paged update writes exactly the next slots, and
-decode over a pool filled by append_rows equals the last prefill row; window and GQA
-equivalences; decode == last prefill row; chunked prefill == tail of full prefill; brute-force
+decode over a pool filled by append_rows equals the last prefill row; the latent-attention core
+equals decompressed attention (the absorption identity) and one-head attention by brute force;
+window and GQA equivalences; decode == last prefill row; chunked prefill == tail of full prefill; brute-force
 scalar loops; and torch's CPU scaled_dot_product_attention in float64.  No function here is
 "parity unpinned".
 """
@@ -411,3 +412,29 @@ def attn_decode_paged(q, k_pool, v_pool, table, lens, block_size, **kw):
         vv = paged_rows(v_pool, table, b, n, block_size)
         outs.append(attn_decode_one(q[b], kk, vv, n, **kw))
     return np.stack(outs)
+
+
+# ----------------------------------------------------------------------------------------------
+# Multi-head latent attention, absorbed decode core ([Models] "Multi-head latent attention",
+# paged_forward)
+# ----------------------------------------------------------------------------------------------
+MLA_LATENT = 512   # kv_lora_rank of DeepSeek-V2/V3 and Kimi K2
+MLA_ROPE = 64      # qk_rope_head_dim
+
+
+def mla_decode_one(q, rows, n, scale):
+    """One sequence: q [H, 576] (the absorbed query W_uk^T q_nope followed by the rotated q_rope),
+    rows [>= n, 576] (the cached [c, k_rope] rows, slot j at position j).  Multi-query attention
+    with one KV head of width 576 whose values are the first 512 features of the same rows:
+    out [H, 512] = softmax(scale * q rows^T) rows[:, :512].  The query sits at position n - 1 and
+    sees every cached row."""
+    q = np.asarray(q, np.float64)
+    rows = np.asarray(rows[:n], np.float64)
+    allowed = np.ones((q.shape[0], n), bool)
+    return softmax_attention(q, rows, rows[:, :MLA_LATENT], allowed, float(scale))
+
+
+def mla_decode(q, cache, lens, scale):
+    """mla_decode_one over a batch: q [B, H, 576], cache [B, Smax, 576], lens [B]."""
+    return np.stack([mla_decode_one(q[b], cache[b], int(lens[b]), scale)
+                     for b in range(len(lens))])

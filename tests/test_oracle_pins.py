@@ -691,3 +691,48 @@ def test_paged_decode_after_append_equals_last_prefill_row():
                                    sinks=sinks)
     full = _prefill(wl, x, inv_freq=inv, sinks=sinks)[:, -1]
     np.testing.assert_allclose(dec, full, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------------------------
+# Multi-head latent attention: the absorbed core
+# ----------------------------------------------------------------------------------------------
+def test_mla_absorbed_core_equals_decompressed_attention():
+    # [Models] "Multi-head latent attention": q_nope . (W_uk c) + q_rope . k_rope =
+    # (W_uk^T q_nope) . c + q_rope . k_rope, and W_uv is applied after attention; so the absorbed
+    # core over the cached [c, k_rope] rows equals ordinary attention with decompressed keys and
+    # values.  Small sizes stand in for 128 heads x (128 nope + 64 rope), 512 latents.
+    H, n, dn, dr, dv, r = 4, 23, 16, 8, 12, oracle.MLA_LATENT
+    W_uk = rng.standard_normal((H, dn, r)) / np.sqrt(r)
+    W_uv = rng.standard_normal((H, dv, r)) / np.sqrt(r)
+    c = rng.standard_normal((n, r))
+    k_rope = rng.standard_normal((n, oracle.MLA_ROPE))
+    q_nope = rng.standard_normal((H, dn))
+    q_rope = rng.standard_normal((H, oracle.MLA_ROPE))
+    scale = (dn + dr) ** -0.5
+    # decompressed: per head, keys [W_uk c, k_rope], values W_uv c
+    full = np.stack([oracle.softmax_attention(
+        np.concatenate([q_nope[h], q_rope[h]])[None],
+        np.concatenate([c @ W_uk[h].T, k_rope], axis=1), c @ W_uv[h].T,
+        np.ones((1, n), bool), scale)[0] for h in range(H)])
+    # absorbed: one 576-wide head
+    q_lat = np.einsum("hd,hdr->hr", q_nope, W_uk)
+    q = np.concatenate([q_lat, q_rope], axis=1)
+    rows = np.concatenate([c, k_rope], axis=1)
+    lat = oracle.mla_decode_one(q, rows, n, scale)                 # [H, 512]
+    absorbed = np.einsum("hr,hvr->hv", lat, W_uv)
+    np.testing.assert_allclose(absorbed, full, atol=1e-12)
+
+
+def test_mla_core_is_one_head_attention_with_values_in_the_rows():
+    # the core equals attention with a single KV head whose values are the rows' first 512
+    # features, the same for every query head (brute force per head with math.exp)
+    H, n = 3, 9
+    q = rng.standard_normal((H, 576))
+    rows = rng.standard_normal((n + 4, 576))
+    got = oracle.mla_decode_one(q, rows, n, 0.05)
+    for h in range(H):
+        s = [0.05 * float(q[h] @ rows[j]) for j in range(n)]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        ref = sum(w[j] * rows[j, :512] for j in range(n)) / sum(w)
+        np.testing.assert_allclose(got[h], ref, rtol=1e-12)
