@@ -20,7 +20,8 @@ __all__ = [
     "GQAError", "RopeSpec", "AttnConfig", "library", "rope_inv_freq", "rope_tables",
     "rope_attention_factor", "rope_softmax_scale",
     "attn_prefill", "attn_decode", "decode_workspace_bytes", "PagedKV", "paged_append",
-    "paged_decode_workspace_bytes", "attn_decode_paged", "prefill_workspace_bytes", "prep_keys", "last_error", "set_kernel_policy",
+    "paged_decode_workspace_bytes", "attn_decode_paged", "mla_decode_workspace_bytes",
+    "mla_decode", "prefill_workspace_bytes", "prep_keys", "last_error", "set_kernel_policy",
     "LIB_PATH", "EXPORTS",
 ]
 
@@ -94,6 +95,8 @@ EXPORTS = {
                                                _I32]),
     "gqa_attn_decode_paged": (_I32, [ctypes.POINTER(_AttnCfg), _P, ctypes.POINTER(_PagedKV), _P,
                                      _I32, _I32, _P, _P, _SZ, _P]),
+    "gqa_mla_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "gqa_mla_decode": (_I32, [_P, _P, _P, _I32, _I32, _I32, ctypes.c_double, _P, _P, _SZ, _P]),
     "gqa_set_kernel_policy": (_I32, [_I32]),
     "gqa_last_error": (ctypes.c_char_p, []),
     "gqa_version": (ctypes.c_char_p, []),
@@ -479,4 +482,37 @@ def attn_decode_paged(cfg: AttnConfig, q, kv: PagedKV, lens, window=0, out=None,
     _check(library().gqa_attn_decode_paged(ctypes.byref(c), pq, ctypes.byref(k), pl, B,
                                            int(window), po, pw, workspace.numel(),
                                            _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+MLA_WIDTH, MLA_LATENT = 576, 512
+
+
+def mla_decode_workspace_bytes(B: int, H: int, Smax: int) -> int:
+    n = library().gqa_mla_decode_workspace_bytes(int(B), int(H), int(Smax))
+    err = last_error()
+    if n == 0 and err:
+        raise GQAError(2, err)
+    return int(n)
+
+
+def mla_decode(q, cache, lens, scale, out=None, workspace=None, stream=None):
+    """Absorbed latent-attention decode core: q [B, H, 576] bf16, cache [B, Smax, 576] bf16, lens
+    [B] int32.  Returns out [B, H, 512] bf16 (before W_uv)."""
+    torch = _torch()
+    B, H = int(q.shape[0]), int(q.shape[1])
+    Smax = int(cache.shape[1])
+    pq = _need(q, "q", (B, H, MLA_WIDTH), torch.bfloat16)
+    pc = _need(cache, "cache", (B, Smax, MLA_WIDTH), torch.bfloat16)
+    pl = _need(lens, "lens", (B,), torch.int32)
+    if out is None:
+        out = torch.empty((B, H, MLA_LATENT), dtype=torch.bfloat16, device=q.device)
+    po = _need(out, "out", (B, H, MLA_LATENT), torch.bfloat16)
+    if workspace is None:
+        workspace = torch.empty(mla_decode_workspace_bytes(B, H, Smax), dtype=torch.uint8,
+                                device=q.device)
+    pw = _need(workspace, "workspace", (workspace.numel(),), torch.uint8)
+    _check(library().gqa_mla_decode(pq, pc, pl, B, H, Smax, float(scale), po, pw, workspace.numel(),
+                                    _stream(stream)))
     return out

@@ -622,4 +622,40 @@ gqa_status gqa_attn_decode_paged(const gqa_attn_cfg* cfg, const void* q, const g
   return hip_status(gqa::launch_decode_mfma(a, workspace, stream, &pk), "paged decode launch");
 }
 
+size_t gqa_mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t Smax) {
+  if (B < 0 || H < 16 || H % 16 || H > 65535 || Smax < 1) {
+    fail(GQA_E_SHAPE, "need B >= 0, H a multiple of 16 in [16, 65535] and Smax >= 1, got %d, %d, %d",
+         B, H, Smax);
+    return 0;
+  }
+  ok();
+  return gqa::mla_decode_workspace_bytes(B, H, Smax);
+}
+
+gqa_status gqa_mla_decode(const void* q, const void* cache, const int32_t* lens, int32_t B,
+                          int32_t H, int32_t Smax, double scale, void* out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || B > 65535) return fail(GQA_E_SHAPE, "B must be in [0, 65535], got %d", B);
+  if (H < 16 || H % 16 || H > 65535)
+    return fail(GQA_E_SHAPE, "H must be a multiple of 16 in [16, 65535], got %d", H);
+  if (Smax < 1) return fail(GQA_E_SHAPE, "Smax must be >= 1, got %d", Smax);
+  if ((int64_t)Smax * 576 * 2 > ((int64_t)1 << 40))
+    return fail(GQA_E_SHAPE, "Smax is too large (%d)", Smax);
+  if (!(std::isfinite(scale) && scale > 0.0))
+    return fail(GQA_E_VALUE, "scale must be finite and > 0, got %g", scale);
+  if (B == 0) return ok();
+  if (!q || !cache || !lens || !out) return fail(GQA_E_NULL, "q, cache, lens and out are required");
+  if (!aligned16(q) || !aligned16(cache) || !aligned16(out))
+    return fail(GQA_E_VALUE, "q, cache and out must be 16-byte aligned");
+  const size_t need = gqa::mla_decode_workspace_bytes(B, H, Smax);
+  if (!workspace || workspace_bytes < need)
+    return fail(GQA_E_WORKSPACE, "latent-attention decode needs a workspace of %zu bytes, got %zu%s",
+                need, workspace_bytes, workspace ? "" : " (null)");
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(GQA_E_WORKSPACE, "workspace must be 256-byte aligned");
+  return hip_status(gqa::launch_mla_decode(q, cache, lens, B, H, Smax, (float)scale, out,
+                                           workspace, stream),
+                    "latent-attention decode launch");
+}
+
 }  // extern "C"

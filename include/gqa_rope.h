@@ -256,6 +256,25 @@ gqa_status gqa_attn_decode_paged(const gqa_attn_cfg* cfg, const void* q, const g
                                  const int32_t* lens, int32_t B, int32_t window, void* out,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Absorbed multi-head latent attention decode core ([Models] "Multi-head latent attention",
+ * paged_forward; DeepSeek-V2/V3 and Kimi K2 widths): multi-query attention with one key/value head
+ * 576 wide (kv_lora_rank 512 + qk_rope_head_dim 64) whose values are the first 512 features of
+ * the same rows.
+ *   q      device bf16 [B, H, 576]: per head, the absorbed query W_uk^T q_nope (512) followed by
+ *          the rotated q_rope (64), as the page builds it before its backend call
+ *   cache  device bf16 [B, Smax, 576]: slot j of sequence b holds [c, k_rope] of position j
+ *   lens   device int32 [B], 0 <= lens[b] <= Smax; the query sees slots 0 .. lens[b]-1 (a
+ *          sequence with none gets a zero output)
+ *   H      query heads, a multiple of 16 in [16, 65535]
+ *   scale  softmax scale (the caller's qk_head_dim^-0.5, times YaRN's m^2 where it applies), > 0
+ *   out    device bf16 [B, H, 512], before W_uv
+ *   workspace  device, >= gqa_mla_decode_workspace_bytes(B, H, Smax) bytes, 256-byte aligned.
+ * Two calls that share a workspace must be ordered on one stream. */
+size_t gqa_mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t Smax);
+gqa_status gqa_mla_decode(const void* q, const void* cache, const int32_t* lens, int32_t B,
+                          int32_t H, int32_t Smax, double scale, void* out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /* Kernel selection, for tests and comparisons: 0 (default) = bf16 problems run on the MFMA
  * kernels wherever their shape is covered; 1 = every problem runs on the generic kernel (one
  * wavefront per query row and head, fp32 arithmetic).  Process-wide; not thread-safe. */

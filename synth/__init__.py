@@ -93,6 +93,11 @@ WORKLOADS = {
     "llama4_chunked_prefill_bf16": Workload("llama4_chunked_prefill_bf16", "prefill", "bf16",
                                             B=1, L=16384, S=16384, Hq=40, Hkv=8, D=128,
                                             rotary_dim=128, theta=5e5, chunk=8192, seed=7),
+    # Absorbed latent-attention decode (DeepSeek-V3 widths): 128 query heads against one KV head
+    # of 576 features (512 latent + 64 rotary); D here is the row width
+    "deepseek_mla_decode_bf16": Workload("deepseek_mla_decode_bf16", "decode", "bf16", B=64, L=1,
+                                         S=32768, Hq=128, Hkv=1, D=576, rotary_dim=64,
+                                         lens_lo=1024, lens_hi=32768, seed=9),
     "sinks_chunk_decode_bf16": Workload("sinks_chunk_decode_bf16", "decode", "bf16", B=64, L=1,
                                         S=32768, Hq=32, Hkv=8, D=128, rotary_dim=128, theta=5e5,
                                         chunk=8192, sinks=True, lens_lo=1024, lens_hi=32768,

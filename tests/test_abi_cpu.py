@@ -359,3 +359,21 @@ def test_paged_workspace_and_support():
                                      None, 0, None) == 0
     assert lib.gqa_paged_append(ctypes.byref(c), ctypes.byref(kv), None, None, None, 0, None, 3, 0,
                                 None) == 0
+
+
+def test_mla_validation_and_workspace():
+    assert lib.gqa_mla_decode_workspace_bytes(2, 24, 100) == 0 and "multiple of 16" in g.last_error()
+    assert lib.gqa_mla_decode_workspace_bytes(2, 16, 0) == 0
+    n = lib.gqa_mla_decode_workspace_bytes(2, 16, 4096)
+    # scaled queries, then per (sequence, split of 2048 keys, head) a 512-wide partial and (m, l)
+    assert n == (2 * 16 * 576 * 2 + 255) // 256 * 256 + 2 * 2 * 16 * 512 * 4 + 2 * 2 * 16 * 2 * 4
+    call = lambda **kw: lib.gqa_mla_decode(*[kw.get(k, d) for k, d in (
+        ("q", FAKE), ("c", FAKE), ("lens", FAKE), ("B", 2), ("H", 16), ("S", 4096),
+        ("scale", 0.1), ("out", FAKE), ("ws", FAKE), ("nb", n), ("st", None))])
+    assert call(H=8) == 2
+    assert call(scale=0.0) == 7 and "scale" in g.last_error()
+    assert call(q=None) == 1
+    assert call(out=FAKE + 4) == 7
+    assert call(nb=n - 1) == 5
+    assert call(ws=FAKE + 16) == 5
+    assert call(B=0, q=None, c=None, lens=None, out=None, ws=None, nb=0) == 0

@@ -654,3 +654,34 @@ def test_paged_decode_matches_oracle(name):
                                    style=wl.style, window=wl.window, q_norm_w=qw, eps=wl.eps,
                                    softcap=wl.softcap, **mask_kw(wl))
     check(got, ref, head_axis=1)
+
+
+# ----------------------------------------------------------------------------------------------
+# Absorbed latent-attention decode core
+# ----------------------------------------------------------------------------------------------
+MLA = WORKLOADS["deepseek_mla_decode_bf16"]
+# DeepSeek-V3: qk_head_dim 192, YaRN factor 40 with mscale_all_dim 1 sharpens the scale by m^2
+MLA_SCALE = oracle.yarn_softmax_scale(192, 40.0, 1.0)
+
+
+@pytest.mark.parametrize("H,Smax,B", [(16, 5000, 4), (128, 2100, 3), (64, 100, 2), (32, 4096, 1)])
+def test_mla_decode_matches_oracle(H, Smax, B):
+    wl = MLA.with_(B=B, Hq=H, S=Smax, lens_lo=1, lens_hi=Smax)
+    say("mla decode", H, Smax, B)
+    lens, q, _ = decode_lens_q(wl, seed=31)
+    lens[0] = 1
+    if B > 1:
+        lens[-1] = Smax
+    if B > 2:
+        lens[1] = 0          # a sequence with no cached row: zero output
+    cache = np.full((B, Smax, 576), np.nan, np.float32)  # slots past a length are never read
+    for b in range(B):
+        if lens[b]:
+            kk, _ = decode_cache_seq(wl, b, int(lens[b]), seed=31)
+            cache[b, :lens[b]] = kk[0]
+    out = g.mla_decode(dev(q), dev(cache), dev(lens, torch.int32), MLA_SCALE)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    ref = oracle.mla_decode(q, np.nan_to_num(cache), lens, MLA_SCALE)
+    check(got, ref, head_axis=1)
