@@ -239,6 +239,49 @@ def run_decode_paged(wl, dx, block_size, steps, warmup, torch, g):
     return sum(ms) / len(ms), ms[len(ms) // 2], same
 
 
+MLA_ROW_BYTES = 576 * 2
+MLA_FLOP_PER_KEY_HEAD = 2 * 576 + 2 * 512   # scores over 576 features, values over 512
+
+
+def mla_scale():
+    """DeepSeek-V3's softmax scale: qk_head_dim 192, YaRN factor 40 with mscale_all_dim 1."""
+    import math
+    m = 0.1 * 1.0 * math.log(40.0) + 1.0
+    return 192 ** -0.5 * m * m
+
+
+def run_mla(wl, steps, warmup, torch, g):
+    """The absorbed latent-attention decode core over a DeepSeek-V3-shaped batch."""
+    from synth import device_normal
+    import numpy as np
+    rng = np.random.default_rng(wl.seed)
+    lens = rng.integers(wl.lens_lo, wl.lens_hi + 1, size=wl.B).astype(np.int32)
+    q = device_normal((wl.B, wl.Hq, wl.D), wl.seed * 10 + 1, "bf16")
+    cache = device_normal((wl.B, wl.S, wl.D), wl.seed * 10 + 2, "bf16")
+    dl = torch.from_numpy(lens).to("cuda")
+    scale = mla_scale()
+    ws = torch.empty(g.mla_decode_workspace_bytes(wl.B, wl.Hq, wl.S), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((wl.B, wl.Hq, 512), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        g.mla_decode(q, cache, dl, scale, out, ws)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        g.mla_decode(q, cache, dl, scale, out, ws)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    keys = int(lens.sum())
+    nbytes = keys * MLA_ROW_BYTES + wl.B * wl.Hq * (576 + 512) * 2 + 4 * wl.B
+    flops = keys * wl.Hq * MLA_FLOP_PER_KEY_HEAD
+    return dict(lens=lens, q=q, cache=cache, out=out, scale=scale), sum(ms) / len(ms), \
+        ms[len(ms) // 2], nbytes, flops
+
+
 def cpu_baseline_prefill(wl, x, torch, budget_s=15.0):
     """Time the oracle on a bounded sample -- whole sequences, in order, until about budget_s of
     CPU time -- check the GPU output on the same sample, and report the rate in TFLOP/s."""
@@ -332,6 +375,8 @@ def main(argv=None):
     ap.add_argument("--decode-workload", default="llama31_decode_bf16")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mla-workload", default="deepseek_mla_decode_bf16",
+                    help="latent-attention decode workload timed after the decode ('' to skip)")
     ap.add_argument("--paged-block", type=int, default=16, metavar="N",
                     help="also time the decode workload through a paged pool of N-slot blocks "
                          "(0: skip)")
@@ -426,6 +471,23 @@ def main(argv=None):
                             "frac": round(pgbs / HBM_PEAK_GBS, 4),
                             "identical_to_contiguous": same}
         line["decode"] = dec
+        del dx
+        torch.cuda.empty_cache()
+    if args.mla_workload:
+        mwl = WORKLOADS[args.mla_workload]
+        log(f"[bench] latent-attention decode workload {mwl.name}")
+        mx, mms, mmed, mbytes, mflops = run_mla(mwl, args.steps, args.warmup, torch, g)
+        mgbs = mbytes / (mms * 1e-3) / 1e9
+        mtf = mflops / (mms * 1e-3) / 1e12
+        log(f"[bench] latent-attention decode {mms:.3f} ms -> {mgbs:.0f} GB/s, {mtf:.1f} TFLOP/s")
+        line["mla_decode"] = {
+            "workload": mwl.name, "value": round(mgbs, 1), "unit": "GB/s",
+            "ms_per_call": round(mms, 4), "ms_median": round(mmed, 4),
+            "algorithmic_bytes": mbytes, "algorithmic_flop": mflops,
+            "roofline": {"bound": "hbm", "achieved": round(mgbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(mgbs / HBM_PEAK_GBS, 4),
+                         "mfma_tflops": round(mtf, 1),
+                         "mfma_frac": round(mtf / MFMA_BF16_PEAK_TFLOPS, 4)}}
     print(json.dumps(line), flush=True)
     return 0
 

@@ -10,13 +10,13 @@
 //
 // The step reads every cached row once per 64 query heads (HBM-bound for 16 heads, balanced
 // against the matrix cores for 128):
-//   mla_prep_q_kernel     q scaled by scale * log2(e) into the workspace (scores in log2 units);
 //   mla_split_kernel      grid (split of 2048 keys, group of 64 heads, sequence); 4 wavefronts,
 //                         16 heads each; the split's rows stream HBM -> LDS in blocks of 32 keys
 //                         (buffer_load ... lds, two LDS stages, one barrier per block) and all
 //                         four wavefronts read them:
 //                           S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K from LDS, the wave's Q
-//                           operands in registers, 18 k-steps over 576 features);
+//                           operands -- q as given, not rounded again -- in registers, 18 k-steps
+//                           over 576 features), times scale * log2(e) in fp32;
 //                           online softmax in log2 units, lazily rescaled;
 //                           O = P V on the same MFMA, V (the rows' first 512 features) read with
 //                           transposing LDS reads, O for 16 heads x 512 features in registers;
@@ -76,26 +76,11 @@ struct MlaArgs {
   const uint16_t* cache;  // [B, Smax, 576]
   const int32_t* lens;    // [B]
   uint16_t* out;          // [B, H, 512]
-  uint16_t* qprep;        // [B, H, 576] workspace
   float* part_o;          // [B, nsplit, H, 512]
   float* part_ml;         // [B, nsplit, H, 2]
   int32_t B, H, Smax, nsplit;
   float qscale;           // scale * log2(e)
 };
-
-__global__ __launch_bounds__(256) void mla_prep_q_kernel(MlaArgs m, int64_t n8) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const u32x4 w = *(const u32x4*)(m.q + 8 * i);
-  u32x4 o;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float lo = __uint_as_float(w[e] << 16) * m.qscale;
-    const float hi = __uint_as_float(w[e] & 0xffff0000u) * m.qscale;
-    o[e] = pack_bf16x2(lo, hi);
-  }
-  *(u32x4*)(m.qprep + 8 * i) = o;
-}
 
 __shared__ __attribute__((aligned(16))) uint16_t g_m0[BUF_BYTES / 2];
 __shared__ __attribute__((aligned(16))) uint16_t g_m1[BUF_BYTES / 2];
@@ -141,7 +126,7 @@ __global__ __launch_bounds__(NWM * 64, 2) void mla_split_kernel(MlaArgs m) {
   u32x4 qop[QKD / 32];
   {
     const int hh = active ? h0 + (lane & 15) : 0;
-    const uint16_t* qr = m.qprep + ((int64_t)b * m.H + hh) * QKD + 8 * (lane >> 4);
+    const uint16_t* qr = m.q + ((int64_t)b * m.H + hh) * QKD + 8 * (lane >> 4);
 #pragma unroll
     for (int s = 0; s < QKD / 32; ++s) qop[s] = *(const u32x4*)(qr + 32 * s);
   }
@@ -173,7 +158,7 @@ __global__ __launch_bounds__(NWM * 64, 2) void mla_split_kernel(MlaArgs m) {
     for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (kb0 + kq * 16 + 4 * gi + r >= ke) sk[kq][r] = -INFINITY;
+        sk[kq][r] = kb0 + kq * 16 + 4 * gi + r < ke ? sk[kq][r] * m.qscale : -INFINITY;
     float mt = fmaxf(fmaxf(fmaxf(sk[0][0], sk[0][1]), fmaxf(sk[0][2], sk[0][3])),
                      fmaxf(fmaxf(sk[1][0], sk[1][1]), fmaxf(sk[1][2], sk[1][3])));
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
@@ -276,8 +261,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t mla_decode_workspace_bytes(int B, int H, int Smax) {
   const int64_t nsplit = (Smax + SPLITM - 1) / SPLITM;
-  return align256((size_t)B * H * QKD * 2) + align256((size_t)B * nsplit * H * LAT * 4) +
-         (size_t)B * nsplit * H * 2 * 4;
+  return align256((size_t)B * nsplit * H * LAT * 4) + (size_t)B * nsplit * H * 2 * 4;
 }
 
 hipError_t launch_mla_decode(const void* q, const void* cache, const int32_t* lens, int B, int H,
@@ -295,18 +279,11 @@ hipError_t launch_mla_decode(const void* q, const void* cache, const int32_t* le
   m.nsplit = (Smax + SPLITM - 1) / SPLITM;
   m.qscale = scale * kLog2e;
   char* ws = (char*)workspace;
-  m.qprep = (uint16_t*)ws;
-  m.part_o = (float*)(ws + align256((size_t)B * H * QKD * 2));
-  m.part_ml = (float*)(ws + align256((size_t)B * H * QKD * 2) +
-                       align256((size_t)B * m.nsplit * H * LAT * 4));
-  const int64_t n8 = (int64_t)B * H * QKD / 8;
-  hipLaunchKernelGGL(mla_prep_q_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
-                     m, n8);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  m.part_o = (float*)ws;
+  m.part_ml = (float*)(ws + align256((size_t)B * m.nsplit * H * LAT * 4));
   hipLaunchKernelGGL(mla_split_kernel, dim3(m.nsplit, (H + NWM * HPW - 1) / (NWM * HPW), B),
                      dim3(NWM * 64), 0, stream, m);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mla_combine_kernel, dim3(H, B), dim3(LAT), 0, stream, m);
   return hipGetLastError();

@@ -56,8 +56,7 @@ hipError_t launch_paged_append(const AttnArgs& a, const PagedKV& kv, void* k_poo
 int decode_split_keys();
 
 // Absorbed multi-head latent attention decode core (bf16): q [B, H, 576], cache [B, Smax, 576],
-// out [B, H, 512]; H a multiple of 16.  The workspace holds the scaled queries and the split
-// partials.
+// out [B, H, 512]; H a multiple of 16.  The workspace holds the split partials.
 size_t mla_decode_workspace_bytes(int B, int H, int Smax);
 hipError_t launch_mla_decode(const void* q, const void* cache, const int32_t* lens, int B, int H,
                              int Smax, float scale, void* out, void* workspace,

@@ -365,8 +365,8 @@ def test_mla_validation_and_workspace():
     assert lib.gqa_mla_decode_workspace_bytes(2, 24, 100) == 0 and "multiple of 16" in g.last_error()
     assert lib.gqa_mla_decode_workspace_bytes(2, 16, 0) == 0
     n = lib.gqa_mla_decode_workspace_bytes(2, 16, 4096)
-    # scaled queries, then per (sequence, split of 2048 keys, head) a 512-wide partial and (m, l)
-    assert n == (2 * 16 * 576 * 2 + 255) // 256 * 256 + 2 * 2 * 16 * 512 * 4 + 2 * 2 * 16 * 2 * 4
+    # per (sequence, split of 2048 keys, head) a 512-wide partial and (m, l)
+    assert n == 2 * 2 * 16 * 512 * 4 + 2 * 2 * 16 * 2 * 4
     call = lambda **kw: lib.gqa_mla_decode(*[kw.get(k, d) for k, d in (
         ("q", FAKE), ("c", FAKE), ("lens", FAKE), ("B", 2), ("H", 16), ("S", 4096),
         ("scale", 0.1), ("out", FAKE), ("ws", FAKE), ("nb", n), ("st", None))])

@@ -685,3 +685,17 @@ def test_mla_decode_matches_oracle(H, Smax, B):
     assert np.isfinite(got).all()
     ref = oracle.mla_decode(q, np.nan_to_num(cache), lens, MLA_SCALE)
     check(got, ref, head_axis=1)
+
+
+def test_full_size_mla_decode_sampled():
+    # the bench's DeepSeek-V3-shaped batch and launch, sampled sequences checked by the oracle
+    import bench
+    mx, _, _, _, _ = bench.run_mla(MLA, 1, 0, torch, g)
+    lens = mx["lens"]
+    got = mx["out"].float().cpu().numpy()
+    assert np.isfinite(got).all()
+    for b in sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0}):
+        n = int(lens[b])
+        ref = oracle.mla_decode_one(mx["q"][b].float().cpu().numpy(),
+                                    mx["cache"][b, :n].float().cpu().numpy(), n, mx["scale"])
+        check(got[b][None], ref[None], head_axis=1)
