@@ -8,20 +8,28 @@
 // caller, as the page does before its backend call), cache [B, Smax, 576], out [B, H, 512]
 // (before W_uv).
 //
-// The step reads every cached row once per 64 query heads (HBM-bound for 16 heads, balanced
-// against the matrix cores for 128):
-//   mla_split_kernel      grid (split of 2048 keys, group of 64 heads, sequence); 4 wavefronts,
-//                         16 heads each; the split's rows stream HBM -> LDS in blocks of 32 keys
-//                         (buffer_load ... lds, two LDS stages, one barrier per block) and all
-//                         four wavefronts read them:
+// Every cached row is read from HBM once per 128 query heads:
+//   mla_split_kernel      grid (kMlaWorkgroups, group of 128 heads); 8 wavefronts, 16 heads each.
+//                         The batch's rows, cut into blocks of 32 keys per sequence and laid end
+//                         to end, are dealt out in equal contiguous shares, one per workgroup, so
+//                         every compute unit gets the same work whatever the length mix; a share
+//                         may span the end of one sequence and the start of the next.  The share's
+//                         blocks stream HBM -> LDS (buffer_load ... lds, four LDS stages, one
+//                         barrier per block) and all eight wavefronts read them:
 //                           S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K from LDS, the wave's Q
-//                           operands -- q as given, not rounded again -- in registers, 18 k-steps
-//                           over 576 features), times scale * log2(e) in fp32;
+//                           operands -- q as given -- in registers, 18 k-steps over 576
+//                           features), times scale * log2(e) in fp32;
 //                           online softmax in log2 units, lazily rescaled;
 //                           O = P V on the same MFMA, V (the rows' first 512 features) read with
 //                           transposing LDS reads, O for 16 heads x 512 features in registers;
-//                         one partial (m, l, O) per (sequence, split, head);
-//   mla_combine_kernel    log-sum-exp merge of a sequence's splits -> bf16.
+//                         one partial (m, l, O) per (share, sequence) piece and head, in slot
+//                         share + sequence (unique: along the pieces both indices only grow);
+//   mla_combine_kernel    log-sum-exp merge of a sequence's pieces -> bf16.
+//
+// LDS layout of a block: row r (key) holds its 72 16-byte chunks at r * 72 + chunk, with the low
+// three chunk bits XORed by a 16-entry row table.  The table makes both LDS read patterns free of
+// bank conflicts: the K operand (16 rows, one 16-byte chunk each, per read) and the transposing V
+// read (8 rows, 32 bytes each); the DMA picks each lane's source chunk so that it lands there.
 #include <algorithm>
 #include <type_traits>
 
@@ -30,22 +38,28 @@
 namespace gqa {
 namespace {
 
-constexpr int QKD = 576;               // row width: latent 512 + rotary 64
-constexpr int LAT = 512;               // value width
-constexpr int KB = 32;                 // keys per block
-constexpr int LROW = 73;               // LDS row stride in 16-byte chunks (72 + 1 pad: no swizzle)
-constexpr int NDMA = (KB * LROW + 63) / 64;  // 1 KB DMA instructions per block
-constexpr int BUF_BYTES = NDMA * 1024;        // what they write (the tail past row 31 is zero)
-constexpr int NWM = 4;                 // wavefronts per workgroup
-constexpr int HPW = 16;                // query heads per wavefront
-constexpr int SPLITM = 2048;           // keys per split
-constexpr int kMlaFlags = 0x00020000;  // raw buffer, range checked
+constexpr int QKD = 576;                 // row width: latent 512 + rotary 64
+constexpr int LAT = 512;                 // value width
+constexpr int CPR = QKD / 8;             // 16-byte chunks per row
+constexpr int KB = 32;                   // keys per block
+constexpr int NDMA = KB * CPR / 64;      // 1 KB DMA instructions per block (36)
+constexpr int BUF_BYTES = NDMA * 1024;
+constexpr int NWM = 8;                   // wavefronts per workgroup
+constexpr int HPW = 16;                  // query heads per wavefront
+constexpr int HPG = NWM * HPW;           // query heads per workgroup
+constexpr int NSTM = 4;                  // LDS stages
+constexpr int kMlaWorkgroups = 256;      // shares of the batch: one per compute unit
+constexpr int kMlaFlags = 0x00020000;    // raw buffer, range checked
+// chunk swizzle per row (low 4 bits of the row): 0,2,4,6,3,1,7,5, 1,3,5,7,2,0,6,4
+constexpr uint64_t kSwz = 0x4602753157136420ull;
+static_assert(NDMA == 36 && NDMA > 4 * NWM, "the DMA split below: 5 loads for waves 0-3, 4 else");
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& w) { return __builtin_bit_cast(bf16x8, w); }
+__device__ __forceinline__ int swz(int r) { return (int)((kSwz >> (4 * (r & 15))) & 7); }
 
 __device__ __forceinline__ i32x4 rsrc_words(const void* base, int nrec) {
   const uint64_t p = (uint64_t)base;
@@ -59,8 +73,8 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, int nrec) {
 
 // HBM -> LDS copy of 16 bytes per lane (lane l's bytes land at dst + 16 l), as assembly so that
 // the compiler's wait counts do not make LDS reads wait for it (correctness rests on the explicit
-// full wait before each barrier that hands a block to its readers; compiler-visible loads retire
-// in issue order, so its own waits stay correct).  Five wait states cover the m0 write and a
+// wait before each barrier that hands a block to its readers; vector memory loads retire in issue
+// order, so the compiler's own waits stay correct).  Five wait states cover the m0 write and a
 // descriptor word written by a VALU instruction just before.
 __device__ __forceinline__ void dma16(i32x4 rsrc, const lds_void* dst, int voff) {
   uint32_t saved;
@@ -76,60 +90,156 @@ struct MlaArgs {
   const uint16_t* cache;  // [B, Smax, 576]
   const int32_t* lens;    // [B]
   uint16_t* out;          // [B, H, 512]
-  float* part_o;          // [B, nsplit, H, 512]
-  float* part_ml;         // [B, nsplit, H, 2]
-  int32_t B, H, Smax, nsplit;
+  float* part_o;          // [kMlaWorkgroups + B, H, 512]
+  float* part_ml;         // [kMlaWorkgroups + B, H, 2]
+  int32_t B, H, Smax;
   float qscale;           // scale * log2(e)
 };
 
-__shared__ __attribute__((aligned(16))) uint16_t g_m0[BUF_BYTES / 2];
-__shared__ __attribute__((aligned(16))) uint16_t g_m1[BUF_BYTES / 2];
+// lengths through the constant address space: scalar loads where b is uniform (a vector load would
+// bring a full vector-memory wait, and with it every block in flight, at each sequence change)
+__device__ __forceinline__ int seq_len(const MlaArgs& m, int b) {
+  const __attribute__((address_space(4))) int32_t* lens =
+      (const __attribute__((address_space(4))) int32_t*)m.lens;
+  return b < m.B ? min(max(lens[b], 0), m.Smax) : 0;
+}
+__device__ __forceinline__ int seq_blocks(const MlaArgs& m, int b) {
+  return (seq_len(m, b) + KB - 1) / KB;
+}
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+  return x;
+}
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+// total blocks of the batch
+__device__ __forceinline__ int total_blocks(const MlaArgs& m, int lane) {
+  int u = 0;
+  for (int base = 0; base < m.B; base += 64) u += wave_sum(seq_blocks(m, base + lane));
+  return u;
+}
+// first block of share c
+__device__ __forceinline__ int share_lo(int c, int U) {
+  return (int)((int64_t)c * U / kMlaWorkgroups);
+}
+// the share that holds block u (the last c with share_lo(c) <= u)
+__device__ __forceinline__ int share_of(int u, int U) {
+  return (int)(((int64_t)(u + 1) * kMlaWorkgroups - 1) / U);
+}
 
-template <int BUF>
-__device__ __forceinline__ uint16_t* mbuf() { return BUF == 0 ? g_m0 : g_m1; }
+// wait until this wavefront's loads of the block about to be read are in: `later` blocks were
+// issued after it, five loads each for waves 0-3 and four for waves 4-7
+__device__ __forceinline__ void wait_block(int later, bool five) {
+  if (later >= 2) {
+    if (five)
+      __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+  } else if (later == 1) {
+    if (five)
+      __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+}
 
-__global__ __launch_bounds__(NWM * 64, 2) void mla_split_kernel(MlaArgs m) {
+// the stages, one block each (a runtime stage index: per-stage constant addresses would not fit
+// the LDS instructions' 16-bit offsets and would cost a register set each)
+__shared__ __attribute__((aligned(16))) uint16_t g_mla[NSTM * BUF_BYTES / 2];
+
+// position in the batch: sequence b, its block j, its length n and block count nb
+struct Cursor {
+  int b, j, n, nb;
+};
+
+__global__ __launch_bounds__(NWM * 64, 1) void mla_split_kernel(MlaArgs m) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int sp = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
-  const int n = min(max(m.lens[b], 0), m.Smax);
-  const int ks = sp * SPLITM;
-  if (ks >= n) return;  // uniform over the workgroup: no barrier is skipped by part of it
-  const int ke = min(ks + SPLITM, n);
-  const int nblk = (ke - ks + KB - 1) / KB;
-  const int h0 = hq * (NWM * HPW) + w * HPW;  // this wavefront's first head
-  const bool active = h0 < m.H;                // (H is a multiple of 16)
+  const int c = blockIdx.x;
 
-  // DMA lane offsets: instruction i of the block fills LDS chunks 64 i .. 64 i + 63, i.e. row
-  // L / 73, chunk L % 73 for L = 64 i + lane; chunk 72 is padding and rows past the block are
-  // out of range (zero).
-  int doff[(NDMA + NWM - 1) / NWM];
-#pragma unroll
-  for (int k = 0; k < (NDMA + NWM - 1) / NWM; ++k) {
-    const int L = 64 * (w + NWM * k) + lane;
-    const int r = L / LROW, c = L - r * LROW;
-    doff[k] = (r < KB && c < QKD / 8) ? r * (QKD * 2) + c * 16 : 0x7ffffff0;
-  }
-  auto issue = [&](int blk, auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    const int kb0 = ks + blk * KB;
-    const i32x4 rs = rsrc_words(m.cache + ((int64_t)b * m.Smax + kb0) * QKD,
-                                min(max(ke - kb0, 0), KB) * QKD * 2);
-#pragma unroll
-    for (int k = 0; k < (NDMA + NWM - 1) / NWM; ++k) {
-      const int i = w + NWM * k;
-      if (i < NDMA) dma16(rs, (const lds_void*)(mbuf<buf>() + i * 512), doff[k]);
+  // this workgroup's share [lo, hi) of the batch's blocks (every wave computes it)
+  const int U = __builtin_amdgcn_readfirstlane(total_blocks(m, lane));
+  const int lo = share_lo(c, U), hi = share_lo(c + 1, U);
+  const int nu = hi - lo;
+  if (nu <= 0) return;  // uniform over the workgroup: no barrier is skipped by part of it
+  Cursor cc;
+  cc.b = m.B;
+  cc.j = 0;
+  {
+    int acc = 0;
+    for (int base = 0; base < m.B; base += 64) {  // lo < U: some sequence holds block lo
+      const int nb = seq_blocks(m, base + lane);
+      const int incl = acc + wave_incl_scan(nb, lane);
+      const uint64_t hit = __ballot(nb > 0 && incl - nb <= lo && lo < incl);
+      if (hit != 0) {
+        const int l = __builtin_ctzll(hit);
+        cc.b = base + l;
+        cc.j = lo - __builtin_amdgcn_readfirstlane(__shfl(incl - nb, l, 64));
+        break;
+      }
+      acc = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
     }
+    cc.b = __builtin_amdgcn_readfirstlane(cc.b);
+    cc.j = __builtin_amdgcn_readfirstlane(cc.j);
+    if (cc.b >= m.B) return;  // (not reached)
+    cc.n = seq_len(m, cc.b);
+    cc.nb = (cc.n + KB - 1) / KB;
+  }
+  auto advance = [&](Cursor& u) {
+    if (++u.j < u.nb) return;
+    u.j = 0;
+    do {
+      ++u.b;
+      u.n = seq_len(m, u.b);
+      u.nb = (u.n + KB - 1) / KB;
+    } while (u.nb == 0 && u.b + 1 < m.B);
+  };
+
+  const int h0 = blockIdx.y * HPG + w * HPW;  // this wavefront's first head
+  const bool active = h0 < m.H;              // (H is a multiple of 16)
+  const bool five = w < NDMA - 4 * NWM;      // waves issuing five loads per block
+
+  // DMA lane offsets (recomputed per block: registers are short): instruction i of the block
+  // fills LDS chunks 64 i .. 64 i + 63; chunk P holds row P / 72 and the chunk whose swizzled
+  // position is P % 72
+  auto dma_off = [&](int i) {
+    const int P = 64 * i + lane;
+    const int r = P / CPR, cp = P - r * CPR;
+    const int ch = (cp & ~7) + ((cp & 7) ^ swz(r));
+    return r * (QKD * 2) + ch * 16;
+  };
+  auto issue = [&](const Cursor& u, int st) {
+    uint16_t* dst = g_mla + st * (BUF_BYTES / 2);
+    const int k0 = u.j * KB;
+    const i32x4 rs = rsrc_words(m.cache + ((int64_t)u.b * m.Smax + k0) * QKD,
+                                min(u.n - k0, KB) * QKD * 2);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      dma16(rs, (const lds_void*)(dst + (w + NWM * k) * 512), dma_off(w + NWM * k));
+    if (five) dma16(rs, (const lds_void*)(dst + (w + NWM * 4) * 512), dma_off(w + NWM * 4));
   };
 
   // query operands: head h0 + (lane & 15), features 32 s + 8 (lane >> 4) .. + 7
   u32x4 qop[QKD / 32];
-  {
-    const int hh = active ? h0 + (lane & 15) : 0;
-    const uint16_t* qr = m.q + ((int64_t)b * m.H + hh) * QKD + 8 * (lane >> 4);
+  const int hh = active ? h0 + (lane & 15) : 0;
+  auto load_q = [&](int bq) {
+    const uint16_t* qr = m.q + ((int64_t)bq * m.H + hh) * QKD + 8 * (lane >> 4);
 #pragma unroll
     for (int s = 0; s < QKD / 32; ++s) qop[s] = *(const u32x4*)(qr + 32 * s);
-  }
+    // wait here (once per sequence) so that no wait for q is left pending into the block loop,
+    // where the compiler would place one before each score MFMA and, not counting the blocks in
+    // flight, drain them all
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  };
 
   f32x4 o[LAT / 16];
 #pragma unroll
@@ -137,19 +247,30 @@ __global__ __launch_bounds__(NWM * 64, 2) void mla_split_kernel(MlaArgs m) {
   float mx = kNegBig, lsum = 0.f;
   const int gi = lane >> 4, si = lane & 15;
 
-  auto compute = [&](int blk, auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    const uint16_t* rows = mbuf<buf>();
-    const int kb0 = ks + blk * KB;
+  // LDS read positions (in bf16 elements).  K operand: row 16 kq + si, chunk 4 s + gi; the
+  // swizzle only flips the low three chunk bits, so chunk 8 t + e sits at 8 t + (e ^ swz(si)).
+  const int ke0 = 8 * (gi ^ swz(si)), ke1 = 8 * ((gi + 4) ^ swz(si));
+  const int krow = si * (CPR * 8);
+  // V operand: rows 4 gi + (si >> 2) (+ 16), bytes 32 db + 8 (si & 3), i.e. chunk
+  // 2 db + ((si >> 1) & 1) at byte 8 (si & 1); the low chunk bits are 2 (db & 3) + ((si >> 1) & 1)
+  const int vrow = 4 * gi + (si >> 2);
+  int vb[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    vb[d] = vrow * (CPR * 8) + 8 * ((2 * d + ((si >> 1) & 1)) ^ swz(vrow)) + 4 * (si & 1);
+
+  auto compute = [&](const Cursor& u, int st) {
+    const uint16_t* rows = g_mla + st * (BUF_BYTES / 2);
+    const int kb0 = u.j * KB;
     // S^T = K Q^T: lane holds head si, keys 16 kq + 4 gi + r
     f32x4 sk[2];
 #pragma unroll
     for (int kq = 0; kq < 2; ++kq) {
       sk[kq] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = rows + (kq * 16 + si) * (LROW * 8) + 8 * gi;
+      const uint16_t* kr = rows + kq * 16 * (CPR * 8) + krow;
 #pragma unroll
       for (int s = 0; s < QKD / 32; ++s) {
-        const u32x4 ka = *(const u32x4*)(kr + 32 * s);
+        const u32x4 ka = *(const u32x4*)(kr + 64 * (s >> 1) + ((s & 1) ? ke1 : ke0));
         sk[kq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qop[s]), sk[kq],
                                                          0, 0, 0);
       }
@@ -158,7 +279,7 @@ __global__ __launch_bounds__(NWM * 64, 2) void mla_split_kernel(MlaArgs m) {
     for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        sk[kq][r] = kb0 + kq * 16 + 4 * gi + r < ke ? sk[kq][r] * m.qscale : -INFINITY;
+        sk[kq][r] = kb0 + kq * 16 + 4 * gi + r < u.n ? sk[kq][r] * m.qscale : -INFINITY;
     float mt = fmaxf(fmaxf(fmaxf(sk[0][0], sk[0][1]), fmaxf(sk[0][2], sk[0][3])),
                      fmaxf(fmaxf(sk[1][0], sk[1][1]), fmaxf(sk[1][2], sk[1][3])));
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
@@ -190,69 +311,115 @@ __global__ __launch_bounds__(NWM * 64, 2) void mla_split_kernel(MlaArgs m) {
     const bf16x8 pa = as_bf16x8(pw);
     // O = P V: B operand = V[32 keys][16 features] via transposing LDS reads (key order matching
     // the one P's operand holds)
-    const int row1 = 4 * gi + (si >> 2);
-    const int row2 = row1 + 16;
 #pragma unroll
     for (int db = 0; db < LAT / 16; ++db) {
-      const int col = 16 * db + 4 * (si & 3);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(rows + row1 * (LROW * 8) + col));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(rows + row2 * (LROW * 8) + col));
-      const i16x8 vb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, vb), o[db],
+      const uint16_t* vp = rows + vb[db & 3] + 64 * (db >> 2);
+      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vp));
+      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vp + 16 * (CPR * 8)));
+      const i16x8 vv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, vv), o[db],
                                                       0, 0, 0);
     }
   };
 
-  issue(0, std::integral_constant<int, 0>());
-  for (int blk = 0; blk < nblk; blk += 2) {
-    __builtin_amdgcn_s_waitcnt(0);  // block blk's rows are in (and every earlier load)
-    __syncthreads();                // ... for every wavefront; buffer 1 is free again
-    if (blk + 1 < nblk) issue(blk + 1, std::integral_constant<int, 1>());
-    if (active) compute(blk, std::integral_constant<int, 0>());
-    if (blk + 1 < nblk) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (blk + 2 < nblk) issue(blk + 2, std::integral_constant<int, 0>());
-      if (active) compute(blk + 1, std::integral_constant<int, 1>());
+  // the piece of sequence bq this share holds is done: write its partial and start afresh
+  auto finish = [&](int bq) {
+    float l = lsum + __shfl_xor(lsum, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int64_t pbase = (int64_t)(c + bq) * m.H + h0;
+    if (lane < HPW) {
+      float* ml = m.part_ml + (pbase + lane) * 2;
+      ml[0] = mx;
+      ml[1] = l;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* po = m.part_o + (pbase + 4 * gi + r) * LAT + si;
+#pragma unroll
+      for (int db = 0; db < LAT / 16; ++db) po[16 * db] = o[db][r];
+    }
+#pragma unroll
+    for (int db = 0; db < LAT / 16; ++db) o[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    mx = kNegBig;
+    lsum = 0.f;
+  };
+
+  // Four stages: when block t is read, blocks t + 1 and t + 2 are in flight and t + 3 goes into
+  // the stage that held t - 1 (every wavefront is past its reads of it: they precede this
+  // barrier).
+  Cursor ic = cc;
+  issue(ic, 0);
+  if (nu > 1) {
+    advance(ic);
+    issue(ic, 1);
+  }
+  if (nu > 2) {
+    advance(ic);
+    issue(ic, 2);
+  }
+  if (active) load_q(cc.b);
+  for (int t = 0; t < nu; ++t) {
+    wait_block(min(nu - 1 - t, 2), five);
+    __syncthreads();
+    if (t + 3 < nu) {
+      advance(ic);
+      issue(ic, (t + 3) % NSTM);
+    }
+    if (active) compute(cc, t % NSTM);
+    const bool last = t + 1 == nu;
+    if (cc.j + 1 == cc.nb || last) {
+      if (active) finish(cc.b);
+      if (!last) {
+        advance(cc);
+        if (active) load_q(cc.b);
+      }
+    } else {
+      ++cc.j;
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load into LDS outstanding when the workgroup ends
-
-  if (!active) return;
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  const int64_t pbase = ((int64_t)b * m.nsplit + sp) * m.H;
-  if (lane < HPW) {
-    float* ml = m.part_ml + (pbase + h0 + lane) * 2;
-    ml[0] = mx;
-    ml[1] = lsum;
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float* po = m.part_o + (pbase + h0 + 4 * gi + r) * LAT + si;
-#pragma unroll
-    for (int db = 0; db < LAT / 16; ++db) po[16 * db] = o[db][r];
-  }
 }
 
-// out[b, h, :] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the splits that hold keys.
-__global__ __launch_bounds__(LAT) void mla_combine_kernel(MlaArgs m) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int n = min(max(m.lens[b], 0), m.Smax);
-  const int nsp = (n + SPLITM - 1) / SPLITM;
-  const int64_t base = (int64_t)b * m.nsplit * m.H + h;
+// out[b, h, :] = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p over the pieces p of sequence b;
+// 4 heads per workgroup, 8 features per lane.
+__global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs m) {
+  const int b = blockIdx.x, lane = threadIdx.x & 63;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (h >= m.H) return;
+  int U = 0, first = 0;  // the batch's blocks, and those of the sequences before b
+  for (int base = 0; base < m.B; base += 64) {
+    const int nb = seq_blocks(m, base + lane);
+    U += wave_sum(nb);
+    first += wave_sum(base + lane < b ? nb : 0);
+  }
+  const int nb = seq_blocks(m, b);
+  uint16_t* dst = m.out + ((int64_t)b * m.H + h) * LAT + 8 * lane;
+  if (nb == 0) {  // no cached row: zeros
+    *(u32x4*)dst = (u32x4){0u, 0u, 0u, 0u};
+    return;
+  }
+  const int c0 = share_of(first, U), c1 = share_of(first + nb - 1, U);
   float M = kNegBig;
-  for (int s = 0; s < nsp; ++s) M = fmaxf(M, m.part_ml[(base + (int64_t)s * m.H) * 2]);
-  float acc = 0.f, lt = 0.f;
-  for (int s = 0; s < nsp; ++s) {
-    const int64_t it = base + (int64_t)s * m.H;
+  for (int c = c0; c <= c1; ++c)
+    if (share_lo(c, U) < share_lo(c + 1, U))
+      M = fmaxf(M, m.part_ml[((int64_t)(c + b) * m.H + h) * 2]);
+  f32x4 a0 = (f32x4){0.f, 0.f, 0.f, 0.f}, a1 = a0;
+  float lt = 0.f;
+  for (int c = c0; c <= c1; ++c) {
+    if (share_lo(c, U) == share_lo(c + 1, U)) continue;
+    const int64_t it = (int64_t)(c + b) * m.H + h;
     const float wgt = fast_exp2(m.part_ml[it * 2] - M);
     lt += wgt * m.part_ml[it * 2 + 1];
-    acc += wgt * m.part_o[it * LAT + d];
+    const f32x4* po = (const f32x4*)(m.part_o + it * LAT + 8 * lane);
+    a0 += wgt * po[0];
+    a1 += wgt * po[1];
   }
-  m.out[((int64_t)b * m.H + h) * LAT + d] = f32_to_bf16(lt > 0.f ? acc / lt : 0.f);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const u32x4 v = {pack_bf16x2(a0[0] * inv, a0[1] * inv), pack_bf16x2(a0[2] * inv, a0[3] * inv),
+                   pack_bf16x2(a1[0] * inv, a1[1] * inv), pack_bf16x2(a1[2] * inv, a1[3] * inv)};
+  *(u32x4*)dst = v;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -260,8 +427,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 size_t mla_decode_workspace_bytes(int B, int H, int Smax) {
-  const int64_t nsplit = (Smax + SPLITM - 1) / SPLITM;
-  return align256((size_t)B * nsplit * H * LAT * 4) + (size_t)B * nsplit * H * 2 * 4;
+  (void)Smax;
+  const size_t slots = (size_t)kMlaWorkgroups + B;
+  return align256(slots * H * LAT * 4) + slots * H * 2 * 4;
 }
 
 hipError_t launch_mla_decode(const void* q, const void* cache, const int32_t* lens, int B, int H,
@@ -276,16 +444,16 @@ hipError_t launch_mla_decode(const void* q, const void* cache, const int32_t* le
   m.B = B;
   m.H = H;
   m.Smax = Smax;
-  m.nsplit = (Smax + SPLITM - 1) / SPLITM;
   m.qscale = scale * kLog2e;
   char* ws = (char*)workspace;
+  const size_t slots = (size_t)kMlaWorkgroups + B;
   m.part_o = (float*)ws;
-  m.part_ml = (float*)(ws + align256((size_t)B * m.nsplit * H * LAT * 4));
-  hipLaunchKernelGGL(mla_split_kernel, dim3(m.nsplit, (H + NWM * HPW - 1) / (NWM * HPW), B),
-                     dim3(NWM * 64), 0, stream, m);
+  m.part_ml = (float*)(ws + align256(slots * H * LAT * 4));
+  hipLaunchKernelGGL(mla_split_kernel, dim3(kMlaWorkgroups, (H + HPG - 1) / HPG), dim3(NWM * 64),
+                     0, stream, m);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(H, B), dim3(LAT), 0, stream, m);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(B, (H + 3) / 4), dim3(256), 0, stream, m);
   return hipGetLastError();
 }
 

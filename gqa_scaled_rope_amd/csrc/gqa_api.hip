@@ -641,6 +641,9 @@ gqa_status gqa_mla_decode(const void* q, const void* cache, const int32_t* lens,
   if (Smax < 1) return fail(GQA_E_SHAPE, "Smax must be >= 1, got %d", Smax);
   if ((int64_t)Smax * 576 * 2 > ((int64_t)1 << 40))
     return fail(GQA_E_SHAPE, "Smax is too large (%d)", Smax);
+  if ((int64_t)B * ((Smax + 31) / 32) >= ((int64_t)1 << 31))
+    return fail(GQA_E_SHAPE, "B * Smax is too large (%d x %d): the batch's 32-key blocks are "
+                "counted in 32 bits", B, Smax);
   if (!(std::isfinite(scale) && scale > 0.0))
     return fail(GQA_E_VALUE, "scale must be finite and > 0, got %g", scale);
   if (B == 0) return ok();

@@ -268,8 +268,11 @@ gqa_status gqa_attn_decode_paged(const gqa_attn_cfg* cfg, const void* q, const g
  *   H      query heads, a multiple of 16 in [16, 65535]
  *   scale  softmax scale (the caller's qk_head_dim^-0.5, times YaRN's m^2 where it applies), > 0
  *   out    device bf16 [B, H, 512], before W_uv
- *   workspace  device, >= gqa_mla_decode_workspace_bytes(B, H, Smax) bytes (split partials),
- *              256-byte aligned.
+ *   workspace  device, >= gqa_mla_decode_workspace_bytes(B, H, Smax) bytes, 256-byte aligned:
+ *              partial results of the (256 + B) pieces the batch is cut into (its blocks of 32
+ *              keys are dealt out in 256 equal shares; a share may hold pieces of several
+ *              sequences), (256 + B) * H * (512 + 2) floats.
+ * Errors: GQA_E_SHAPE also when B * ceil(Smax / 32) >= 2^31.
  * Two calls that share a workspace must be ordered on one stream. */
 size_t gqa_mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t Smax);
 gqa_status gqa_mla_decode(const void* q, const void* cache, const int32_t* lens, int32_t B,

@@ -365,8 +365,9 @@ def test_mla_validation_and_workspace():
     assert lib.gqa_mla_decode_workspace_bytes(2, 24, 100) == 0 and "multiple of 16" in g.last_error()
     assert lib.gqa_mla_decode_workspace_bytes(2, 16, 0) == 0
     n = lib.gqa_mla_decode_workspace_bytes(2, 16, 4096)
-    # per (sequence, split of 2048 keys, head) a 512-wide partial and (m, l)
-    assert n == 2 * 2 * 16 * 512 * 4 + 2 * 2 * 16 * 2 * 4
+    # per (piece slot, head) a 512-wide partial and (m, l); 256 shares + B sequences of slots
+    assert n == (256 + 2) * 16 * 512 * 4 + (256 + 2) * 16 * 2 * 4
+    assert lib.gqa_mla_decode_workspace_bytes(2, 16, 100000) == n  # independent of Smax
     call = lambda **kw: lib.gqa_mla_decode(*[kw.get(k, d) for k, d in (
         ("q", FAKE), ("c", FAKE), ("lens", FAKE), ("B", 2), ("H", 16), ("S", 4096),
         ("scale", 0.1), ("out", FAKE), ("ws", FAKE), ("nb", n), ("st", None))])
@@ -377,3 +378,4 @@ def test_mla_validation_and_workspace():
     assert call(nb=n - 1) == 5
     assert call(ws=FAKE + 16) == 5
     assert call(B=0, q=None, c=None, lens=None, out=None, ws=None, nb=0) == 0
+    assert call(B=65535, S=1 << 21) == 2 and "32 bits" in g.last_error()

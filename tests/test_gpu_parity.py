@@ -664,7 +664,10 @@ MLA = WORKLOADS["deepseek_mla_decode_bf16"]
 MLA_SCALE = oracle.yarn_softmax_scale(192, 40.0, 1.0)
 
 
-@pytest.mark.parametrize("H,Smax,B", [(16, 5000, 4), (128, 2100, 3), (64, 100, 2), (32, 4096, 1)])
+# (many short sequences: shares span several of them; 33 x <= 3 blocks: fewer blocks than shares,
+# so some shares are empty; 144 heads: a second, partly idle head group)
+@pytest.mark.parametrize("H,Smax,B", [(16, 5000, 4), (128, 2100, 3), (64, 100, 2), (32, 4096, 1),
+                                      (128, 300, 40), (16, 70, 33), (144, 700, 3)])
 def test_mla_decode_matches_oracle(H, Smax, B):
     wl = MLA.with_(B=B, Hq=H, S=Smax, lens_lo=1, lens_hi=Smax)
     say("mla decode", H, Smax, B)
