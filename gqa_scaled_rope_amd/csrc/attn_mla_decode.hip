@@ -26,10 +26,11 @@
 //                         share + sequence (unique: along the pieces both indices only grow);
 //   mla_combine_kernel    log-sum-exp merge of a sequence's pieces -> bf16.
 //
-// LDS layout of a block: row r (key) holds its 72 16-byte chunks at r * 72 + chunk, with the low
-// three chunk bits XORed by a 16-entry row table.  The table makes both LDS read patterns free of
-// bank conflicts: the K operand (16 rows, one 16-byte chunk each, per read) and the transposing V
-// read (8 rows, 32 bytes each); the DMA picks each lane's source chunk so that it lands there.
+// LDS layout of a block: row r (key) holds its 72 16-byte chunks at r * 74 + chunk.  Of the row
+// strides near 72 chunks, 74 is the one measured free of LDS bank conflicts (on gfx950, with the
+// bank-conflict counter) for both read patterns: the K operand (16 rows, one 16-byte chunk each,
+// per ds_read_b128) and the transposing V read (8 rows, 32 bytes each); 72 costs the K read 12
+// and the V read 6 extra cycles per instruction, 73 4 and 2.
 #include <algorithm>
 #include <type_traits>
 
@@ -41,8 +42,9 @@ namespace {
 constexpr int QKD = 576;                 // row width: latent 512 + rotary 64
 constexpr int LAT = 512;                 // value width
 constexpr int CPR = QKD / 8;             // 16-byte chunks per row
+constexpr int LROW = 74;                 // LDS row stride in chunks (2 of padding)
 constexpr int KB = 32;                   // keys per block
-constexpr int NDMA = KB * CPR / 64;      // 1 KB DMA instructions per block (36)
+constexpr int NDMA = KB * LROW / 64;     // 1 KB DMA instructions per block (37)
 constexpr int BUF_BYTES = NDMA * 1024;
 constexpr int NWM = 8;                   // wavefronts per workgroup
 constexpr int HPW = 16;                  // query heads per wavefront
@@ -50,16 +52,14 @@ constexpr int HPG = NWM * HPW;           // query heads per workgroup
 constexpr int NSTM = 4;                  // LDS stages
 constexpr int kMlaWorkgroups = 256;      // shares of the batch: one per compute unit
 constexpr int kMlaFlags = 0x00020000;    // raw buffer, range checked
-// chunk swizzle per row (low 4 bits of the row): 0,2,4,6,3,1,7,5, 1,3,5,7,2,0,6,4
-constexpr uint64_t kSwz = 0x4602753157136420ull;
-static_assert(NDMA == 36 && NDMA > 4 * NWM, "the DMA split below: 5 loads for waves 0-3, 4 else");
+static_assert(KB * LROW % 64 == 0 && NDMA > 4 * NWM && NDMA <= 5 * NWM,
+              "the DMA split below: five loads for the first NDMA - 4 NWM waves, four else");
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& w) { return __builtin_bit_cast(bf16x8, w); }
-__device__ __forceinline__ int swz(int r) { return (int)((kSwz >> (4 * (r & 15))) & 7); }
 
 __device__ __forceinline__ i32x4 rsrc_words(const void* base, int nrec) {
   const uint64_t p = (uint64_t)base;
@@ -135,7 +135,7 @@ __device__ __forceinline__ int share_of(int u, int U) {
 }
 
 // wait until this wavefront's loads of the block about to be read are in: `later` blocks were
-// issued after it, five loads each for waves 0-3 and four for waves 4-7
+// issued after it, five loads each (`five`) or four
 __device__ __forceinline__ void wait_block(int later, bool five) {
   if (later >= 2) {
     if (five)
@@ -208,14 +208,12 @@ __global__ __launch_bounds__(NWM * 64, 1) void mla_split_kernel(MlaArgs m) {
   const bool active = h0 < m.H;              // (H is a multiple of 16)
   const bool five = w < NDMA - 4 * NWM;      // waves issuing five loads per block
 
-  // DMA lane offsets (recomputed per block: registers are short): instruction i of the block
-  // fills LDS chunks 64 i .. 64 i + 63; chunk P holds row P / 72 and the chunk whose swizzled
-  // position is P % 72
+  // DMA lane offsets: instruction i of the block fills LDS chunks 64 i .. 64 i + 63; chunk P
+  // holds chunk P % 74 of row P / 74 (chunks 72 and 73 are padding: out of range, never read)
   auto dma_off = [&](int i) {
     const int P = 64 * i + lane;
-    const int r = P / CPR, cp = P - r * CPR;
-    const int ch = (cp & ~7) + ((cp & 7) ^ swz(r));
-    return r * (QKD * 2) + ch * 16;
+    const int r = P / LROW, c = P - r * LROW;
+    return c < CPR ? r * (QKD * 2) + c * 16 : 0x7ffffff0;
   };
   auto issue = [&](const Cursor& u, int st) {
     uint16_t* dst = g_mla + st * (BUF_BYTES / 2);
@@ -247,17 +245,10 @@ __global__ __launch_bounds__(NWM * 64, 1) void mla_split_kernel(MlaArgs m) {
   float mx = kNegBig, lsum = 0.f;
   const int gi = lane >> 4, si = lane & 15;
 
-  // LDS read positions (in bf16 elements).  K operand: row 16 kq + si, chunk 4 s + gi; the
-  // swizzle only flips the low three chunk bits, so chunk 8 t + e sits at 8 t + (e ^ swz(si)).
-  const int ke0 = 8 * (gi ^ swz(si)), ke1 = 8 * ((gi + 4) ^ swz(si));
-  const int krow = si * (CPR * 8);
-  // V operand: rows 4 gi + (si >> 2) (+ 16), bytes 32 db + 8 (si & 3), i.e. chunk
-  // 2 db + ((si >> 1) & 1) at byte 8 (si & 1); the low chunk bits are 2 (db & 3) + ((si >> 1) & 1)
-  const int vrow = 4 * gi + (si >> 2);
-  int vb[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-    vb[d] = vrow * (CPR * 8) + 8 * ((2 * d + ((si >> 1) & 1)) ^ swz(vrow)) + 4 * (si & 1);
+  // LDS read positions (in bf16 elements).  K operand: row 16 kq + si, chunk 4 s + gi.  V
+  // operand: rows 4 gi + (si >> 2) (+ 16), bytes 32 db + 8 (si & 3).
+  const int kbase = si * (LROW * 8) + 8 * gi;
+  const int vbase = (4 * gi + (si >> 2)) * (LROW * 8) + 4 * (si & 3);
 
   auto compute = [&](const Cursor& u, int st) {
     const uint16_t* rows = g_mla + st * (BUF_BYTES / 2);
@@ -267,10 +258,10 @@ __global__ __launch_bounds__(NWM * 64, 1) void mla_split_kernel(MlaArgs m) {
 #pragma unroll
     for (int kq = 0; kq < 2; ++kq) {
       sk[kq] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = rows + kq * 16 * (CPR * 8) + krow;
+      const uint16_t* kr = rows + kq * 16 * (LROW * 8) + kbase;
 #pragma unroll
       for (int s = 0; s < QKD / 32; ++s) {
-        const u32x4 ka = *(const u32x4*)(kr + 64 * (s >> 1) + ((s & 1) ? ke1 : ke0));
+        const u32x4 ka = *(const u32x4*)(kr + 32 * s);
         sk[kq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qop[s]), sk[kq],
                                                          0, 0, 0);
       }
@@ -313,11 +304,11 @@ __global__ __launch_bounds__(NWM * 64, 1) void mla_split_kernel(MlaArgs m) {
     // the one P's operand holds)
 #pragma unroll
     for (int db = 0; db < LAT / 16; ++db) {
-      const uint16_t* vp = rows + vb[db & 3] + 64 * (db >> 2);
+      const uint16_t* vp = rows + vbase + 16 * db;
       const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) i16x4*)(vp));
       const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(vp + 16 * (CPR * 8)));
+          (__attribute__((address_space(3))) i16x4*)(vp + 16 * (LROW * 8)));
       const i16x8 vv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, vv), o[db],
                                                       0, 0, 0);

@@ -41,6 +41,10 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 // Element offset of 16-byte chunk c of row r in a [BN][HD] bf16 tile.
 __device__ __forceinline__ int tile_off(int r, int c) { return r * HD + ((c ^ (r & 15)) << 3); }
+// V tiles: the transposing reads serve lanes 0-31 and 32-63 as two passes of 256 bytes over the
+// 64 four-byte banks (measured on gfx950); a pass reads a 64-byte chunk quad of each of four
+// consecutive rows, and (r & 3) << 2 puts the four quads in different quarters of the bank array.
+__device__ __forceinline__ int vtile_off(int r, int c) { return r * HD + ((c ^ ((r & 3) << 2)) << 3); }
 
 struct Smem {
   uint16_t k[2][TILE_ELEMS];
@@ -207,8 +211,8 @@ __device__ __forceinline__ void store_tile(const AttnArgs& a, int jt, TileRegs& 
   }
   *(u32x4*)(&sm.k[buf][tile_off(row, c0)]) = tr.k0;
   *(u32x4*)(&sm.k[buf][tile_off(row, c0 + 8)]) = tr.k1;
-  *(u32x4*)(&sm.v[buf][tile_off(row, c0)]) = tr.v0;
-  *(u32x4*)(&sm.v[buf][tile_off(row, c0 + 8)]) = tr.v1;
+  *(u32x4*)(&sm.v[buf][vtile_off(row, c0)]) = tr.v0;
+  *(u32x4*)(&sm.v[buf][vtile_off(row, c0 + 8)]) = tr.v1;
   if (c0 == 0) sm.kpos[buf][row] = tr.kp;
 }
 
@@ -428,8 +432,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(AttnArgs a, int nqb
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const int col = db * 32 + 16 * (gi & 1) + 4 * (s16 & 3);
-          const int off1 = row1 * HD + (((col >> 3) ^ (row1 & 15)) << 3) + (col & 7);
-          const int off2 = row2 * HD + (((col >> 3) ^ (row2 & 15)) << 3) + (col & 7);
+          const int off1 = row1 * HD + (((col >> 3) ^ ((row1 & 3) << 2)) << 3) + (col & 7);
+          const int off2 = row2 * HD + (((col >> 3) ^ ((row2 & 3) << 2)) << 3) + (col & 7);
           const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) i16x4*)(vs + off1));
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(

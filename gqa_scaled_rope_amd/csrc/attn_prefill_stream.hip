@@ -87,12 +87,13 @@ __device__ __forceinline__ u32x4 pack8(const float* x) {
 
 
 // LDS layout of a tile: row r's 16-byte chunk c sits at chunk position c ^ swz(r).  K tiles use
-// swz = r & 15 (conflict-free for the 16 rows one ds_read_b128 touches).  V tiles use a
-// permutation that also keeps the transposing reads conflict-free: each 16-lane group of
-// ds_read_b64_tr_b16 reads two adjacent chunks of four consecutive rows, and (r & 3) << 1 spreads
-// those eight 16-byte pieces over all eight bank groups.
+// swz = r & 15, measured free of bank conflicts for the operand reads (ds_read_b128, 32 rows).
+// V tiles: ds_read_b64_tr_b16 serves lanes 0-31 and 32-63 as two passes of 256 bytes over the
+// 64 four-byte banks (measured on gfx950); each pass here reads four chunks of each of four
+// consecutive rows, 256-byte rows, so the rows' 64-byte chunk quads must land in four different
+// quarters of the bank array: swz = (r & 3) << 2 moves row r's quad by r & 3 quarters.
 __device__ __forceinline__ int kswz(int r) { return r & 15; }
-__device__ __forceinline__ int vswz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+__device__ __forceinline__ int vswz(int r) { return (r & 3) << 2; }
 
 // First index j in [0, n) with kp[j] >= x for a nondecreasing kp, found by the whole wavefront:
 // each round samples 64 evenly spaced entries and keeps the one segment that contains the
