@@ -657,8 +657,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   // the second half of tile t) waits for tile t+1's loads, and once every wavefront is past it the
   // buffer of tile t-1 is free for tile t+2's loads.
   const int nsteps = 2 * n_tiles;
-  f32x16 s_cur;
-  auto step = [&](int s, auto phc) {
+  // two score sets that trade roles every step (a step reads one and fills the other), so no
+  // copy of the next step's scores has to wait for its MFMAs
+  f32x16 s_a, s_b;
+  auto step = [&](int s, auto phc, f32x16& sc, f32x16& s_next) {
     constexpr int PH = decltype(phc)::value;  // position in the 6-step buffer cycle
     constexpr int buf = PH >> 1;
     constexpr int kb = PH & 1;
@@ -671,7 +673,6 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     const int32_t klast = kpt[BN - 1];
     const bool full = (jt + BN <= j_hi) && ((int64_t)klast <= qmin) &&
                       (kfirst >= floor_max);
-    f32x16 sc = s_cur;
 
     // ---- soft-cap, mask, running max ----
     const bool unset = m == kNegBig;
@@ -721,7 +722,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     // Issued unconditionally so that it shares one basic block with the exponentials and P V
     // below (the scheduler interleaves only within a block); after the last step it reads a
     // stale buffer and its result is unused.
-    s_cur = qk(std::integral_constant<int, nbuf>(), std::integral_constant<int, nkb>());
+    s_next = qk(std::integral_constant<int, nbuf>(), std::integral_constant<int, nkb>());
 
     // ---- P = exp2(s - m); row sums of the bf16 weights the P V product uses, two per
     // v_dot2_f32_bf16 against (1, 1) ----
@@ -772,7 +773,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   commit_kpos(std::integral_constant<int, 0>());
   __syncthreads();  // staging read by every wave: buffer 1 is free for tile 1
   if (n_tiles > 1) issue_tile(j_lo + BN, std::integral_constant<int, 1>());
-  if (nsteps > 0) s_cur = qk(std::integral_constant<int, 0>(), std::integral_constant<int, 0>());
+  if (nsteps > 0) s_a = qk(std::integral_constant<int, 0>(), std::integral_constant<int, 0>());
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   using P2 = std::integral_constant<int, 2>;
@@ -780,12 +781,12 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   using P4 = std::integral_constant<int, 4>;
   using P5 = std::integral_constant<int, 5>;
   for (int s = 0; s < nsteps; s += 6) {
-    step(s, P0());
-    if (s + 1 < nsteps) step(s + 1, P1());
-    if (s + 2 < nsteps) step(s + 2, P2());
-    if (s + 3 < nsteps) step(s + 3, P3());
-    if (s + 4 < nsteps) step(s + 4, P4());
-    if (s + 5 < nsteps) step(s + 5, P5());
+    step(s, P0(), s_a, s_b);
+    if (s + 1 < nsteps) step(s + 1, P1(), s_b, s_a);
+    if (s + 2 < nsteps) step(s + 2, P2(), s_a, s_b);
+    if (s + 3 < nsteps) step(s + 3, P3(), s_b, s_a);
+    if (s + 4 < nsteps) step(s + 4, P4(), s_a, s_b);
+    if (s + 5 < nsteps) step(s + 5, P5(), s_b, s_a);
   }
 
   const float ltot = lsum + swap_halves(lsum);
