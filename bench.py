@@ -139,7 +139,7 @@ def _prefill_setup(wl, torch, g):
                 out=out, table_len=table_len, kcache=kcache)
 
 
-def run_prefill(wl, steps, warmup, torch, g):
+def run_prefill(wl, steps, warmup, torch, g, graph=True):
     x = _prefill_setup(wl, torch, g)
     spec = _rope_spec(g, wl)
     stream = torch.cuda.current_stream()
@@ -162,14 +162,42 @@ def run_prefill(wl, steps, warmup, torch, g):
     for _ in range(warmup):
         launches()
     torch.cuda.synchronize()
+    step_fn = launches
+    if graph:
+        # the step's three launches captured once as a HIP graph and replayed (no memset or
+        # allocation is recorded: every buffer exists before the capture); the replayed output
+        # must match the eager one bit for bit
+        eager = x["out"].clone()
+        hg = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            x["out"].zero_()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(hg, stream=cap):
+                launches()
+        stream.wait_stream(cap)
+        for _ in range(3):
+            x["out"].zero_()
+            hg.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(x["out"], eager):
+                raise RuntimeError("graph replay differs from the eager step")
+        x["graph"] = hg
+        step_fn = hg.replay
+    # the step: only the two bracketing events (an event between kernels adds a few us of
+    # queue work of its own, so the per-launch times come from a separate pass below)
     t0, t1 = E(), E()
-    evs = [[E() for _ in range(4)] for _ in range(steps)]
     t0.record(stream)
     for i in range(steps):
-        launches(evs[i])
+        step_fn()
     t1.record(stream)
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
+    evs = [[E() for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        launches(evs[i])
+    torch.cuda.synchronize()
     parts = {name: sorted(e[k].elapsed_time(e[k + 1]) for e in evs)
              for k, name in enumerate(("rope_tables", "prep_keys", "attention"))}
     stats = {name: (sum(v) / len(v), v[len(v) // 2]) for name, v in parts.items()}
@@ -375,6 +403,8 @@ def main(argv=None):
     ap.add_argument("--decode-workload", default="llama31_decode_bf16")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the step's kernels one by one instead of replaying a HIP graph")
     ap.add_argument("--mla-workload", default="deepseek_mla_decode_bf16",
                     help="latent-attention decode workload timed after the decode ('' to skip)")
     ap.add_argument("--paged-block", type=int, default=16, metavar="N",
@@ -409,7 +439,7 @@ def main(argv=None):
     g.library()
     wl = WORKLOADS[args.workload]
     log(f"[bench] prefill workload {wl.name}: warmup {args.warmup}, steps {args.steps}")
-    x, step_ms, stats = run_prefill(wl, args.steps, args.warmup, torch, g)
+    x, step_ms, stats = run_prefill(wl, args.steps, args.warmup, torch, g, graph=not args.no_graph)
     kern_ms, kern_med = stats["attention"]
     flops = prefill_flops(wl)
     value = flops / (step_ms * 1e-3) / 1e12
@@ -426,7 +456,8 @@ def main(argv=None):
                    "rope": wl.rope_kind, "theta": wl.theta, "qk_norm": wl.qk_norm,
                    "window": wl.window, "softcap": wl.softcap, "n_cached": wl.n_cached,
                    "chunk": wl.chunk, "chunk_lookback": wl.chunk_lookback, "sinks": wl.sinks,
-                   "parallelism": "none (1 GPU)"},
+                   "parallelism": "none (1 GPU)",
+                   "launch": "eager" if args.no_graph else "HIP graph of the step's 3 kernels"},
         "roofline": {"bound": "mfma", "kernel": "prefill_stream_kernel",
                      "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
