@@ -319,11 +319,6 @@ template <int BUF>
 __device__ __forceinline__ uint16_t* vbuf() { return BUF == 0 ? g_v0 : BUF == 1 ? g_v1 : g_v2; }
 template <int BUF>
 __device__ __forceinline__ int32_t* pbuf() { return BUF == 0 ? g_p0 : BUF == 1 ? g_p1 : g_p2; }
-// Before tile 1 is loaded, the K and V areas of buffers 1 and 2 stage the workgroup's prepared
-// queries: rows 64k .. 64k + 63 in area k (16-byte chunk c of row r at chunk c ^ (r & 15)).
-__device__ __forceinline__ uint16_t* qstage(int k) {
-  return k == 0 ? g_k1 : k == 1 ? g_v1 : k == 2 ? g_k2 : g_v2;
-}
 
 struct StreamArgs {
   AttnArgs a;
@@ -472,113 +467,125 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
                         : a.has_floor() ? (int32_t)max<int64_t>(key_floor(a, qp), INT32_MIN)
                                         : INT32_MIN;
 
-  // ---- query prep, shared by the workgroup: 16 lanes per query row, 8 features per lane (32 rows
-  // per pass, 8 passes in two batches whose loads all go out before their arithmetic: rows and
-  // positions, then the table entries at those positions).  Each row is RMS-normed, rotated at
-  // its position and scaled into log2 units, then stored as bf16 in the staging area; rows past
-  // the end are stored as zeros.  The row-local exchanges (norm sum, rotation partner) are DPP
-  // moves ----
+  // ---- query prep, per wavefront and in registers: lane (ql, hg) loads, for its row, exactly the
+  // features its MFMA operands hold -- 16 s + 8 hg .. + 7 for s = 0..7 -- RMS-norms the row (the
+  // other 64 features are in lane ql + 32), rotates it at its position and scales it into log2
+  // units.  With half-split rotation at R = 32, 64 or 128 a feature's partner (R/2 further on)
+  // lies R/32 operand chunks further in the same lane; at R = 16 it is in lane l ^ 32.
+  // Interleaved pairs are adjacent.  No LDS and no barrier: the waves prep independently, in two
+  // memory round trips (rows, gains and the position; then the table entries at the position).
+  bf16x8 qop[8];
   {
-    const int grp = tid >> 4, c = tid & 15;
-    const uint16_t* qw = (const uint16_t*)a.qw;
-    const int P = a.R >> 4;
+    const uint16_t* qrow = (const uint16_t*)a.q + (int64_t)b * a.q_b + (int64_t)qi * a.q_i +
+                           (int64_t)qh * a.q_h + 8 * hg;
+    u32x4 xw[8], ww[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) xw[s] = ld16(qrow + 16 * s);
+    if (NORM) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) ww[s] = ld16((const uint16_t*)a.qw + 16 * s + 8 * hg);
+    }
+    const int P = a.R >> 4;  // half-split: partner distance in 8-feature chunks
     const int halfp = a.R >> 1;
-    const bool rot = 8 * c < a.R;
-    const bool first = 8 * c < halfp;
-    const int p0 = ROT == 1 ? (!rot ? 0 : (first ? 8 * c : 8 * c - halfp)) : (rot ? 4 * c : 0);
-    const float qscale = a.scale * kLog2e;
-    constexpr int NP = ROWS / 64;  // passes per batch
-    float wv[8];
-    if (NORM) unpack8(ld16(qw + 8 * c), wv);
+    const int64_t tp = min<int64_t>(max<int64_t>(qp, 0), a.table_len - 1);
+    const float* crow = a.cos_t + tp * halfp;
+    const float* srow = a.sin_t + tp * halfp;
+    // table entries: half-split -- for each first-half chunk c = 2 s + hg < P (so s < 4), its 8
+    // pairs (at R = 16 both lanes load pairs 0..7); interleaved -- for each rotated chunk, its 4
+    f32x4 tc[8][2], ts[8][2];
+    if (ROT == 1) {
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-    u32x4 xw[NP];
-    int32_t pw[NP];
-    bool vw[NP];
+      for (int s = 0; s < 4; ++s) {
+        const int cch = 2 * s + hg;
+        const bool ld = P == 1 ? s == 0 : cch < P;
+        const int pb = P == 1 ? 0 : 8 * cch;
+        if (ld) {
+          tc[s][0] = *(const f32x4*)(crow + pb);
+          tc[s][1] = *(const f32x4*)(crow + pb + 4);
+          ts[s][0] = *(const f32x4*)(srow + pb);
+          ts[s][1] = *(const f32x4*)(srow + pb + 4);
+        }
+      }
+    } else if (ROT == 2) {
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      // a valid flattened row index is below L*G < 2^31 (checked on the host): 32-bit division
-      const int64_t f = f0 + 32 * (NP * hb + j) + grp;
-      vw[j] = f < nrows;
-      const uint32_t fv = vw[j] ? (uint32_t)f : 0u;
-      const int ri = (int)(fv / (uint32_t)G);
-      const int rh = g * G + (int)(fv - (uint32_t)ri * (uint32_t)G);
-      xw[j] = ld16((const uint16_t*)a.q + (int64_t)b * a.q_b + (int64_t)ri * a.q_i +
-                   (int64_t)rh * a.q_h + 8 * c);
-      pw[j] = qpos_b[ri];
-    }
-    f32x4 tc[NP][2], ts[NP][2];
-    if (ROT) {
-#pragma unroll
-      for (int j = 0; j < NP; ++j) {
-        const int64_t tp = min<int64_t>(max<int64_t>(pw[j], 0), a.table_len - 1);
-        const float* cr = a.cos_t + tp * halfp + p0;
-        const float* sr = a.sin_t + tp * halfp + p0;
-        tc[j][0] = *(const f32x4*)cr;
-        ts[j][0] = *(const f32x4*)sr;
-        if (ROT == 1) {
-          tc[j][1] = *(const f32x4*)(cr + 4);
-          ts[j][1] = *(const f32x4*)(sr + 4);
+      for (int s = 0; s < 8; ++s) {
+        const int cch = 2 * s + hg;
+        if (8 * cch < a.R) {
+          tc[s][0] = *(const f32x4*)(crow + 4 * cch);
+          ts[s][0] = *(const f32x4*)(srow + 4 * cch);
         }
       }
     }
+    float x[8][8];
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      float x[8];
-      unpack8(xw[j], x);
-      if (NORM) {
-        float ss = 0.f;
+    for (int s = 0; s < 8; ++s) unpack8(xw[s], x[s]);
+    if (NORM) {
+      float ss = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-        ss = row16_sum(ss);
-        const float rs = rsqrtf(ss * (1.0f / HD) + a.eps);
+      for (int s = 0; s < 8; ++s)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] *= rs * wv[e];
+        for (int e = 0; e < 8; ++e) ss += x[s][e] * x[s][e];
+      ss += swap_halves(ss);
+      const float rs = rsqrtf(ss * (1.0f / HD) + a.eps);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        float wv[8];
+        unpack8(ww[s], wv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[s][e] *= rs * wv[e];
       }
-      if (ROT == 1) {
-        float y[8];
-        if (P == 1) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = dpp_mov<kDppXor1>(x[e]);
-        } else if (P == 2) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = dpp_mov<kDppXor2>(x[e]);
-        } else if (P == 4) {
-          const bool up = (c & 4) != 0;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float l = dpp_mov<kDppShl4>(x[e]), rgt = dpp_mov<kDppShr4>(x[e]);
-            y[e] = up ? rgt : l;
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = dpp_mov<kDppRor8>(x[e]);
-        }
+    }
+    if (ROT == 1) {
+      if (P == 1) {
+        // chunk 0 (lane hg = 0, first half) and chunk 1 (lane hg = 1, second half) pair up
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float cs = tc[j][e >> 2][e & 3], sn = ts[j][e >> 2][e & 3];
-          const float r = first ? (x[e] * cs - y[e] * sn) : (y[e] * sn + x[e] * cs);
-          x[e] = rot ? r : x[e];
+          const float y = swap_halves(x[0][e]);
+          const float cs = tc[0][e >> 2][e & 3], sn = ts[0][e >> 2][e & 3];
+          x[0][e] = hg == 0 ? x[0][e] * cs - y * sn : y * sn + x[0][e] * cs;
         }
-      } else if (ROT == 2) {
+      } else {
+        const int hs = P >> 1;  // partner distance in this lane's chunk index: 1, 2 or 4
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float cs = tc[j][0][e], sn = ts[j][0][e];
-          const float u = x[2 * e], v = x[2 * e + 1];
-          x[2 * e] = rot ? u * cs - v * sn : u;
-          x[2 * e + 1] = rot ? u * sn + v * cs : v;
+        for (int s = 0; s < 4; ++s) {
+          if (2 * s + hg < P) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float cs = tc[s][e >> 2][e & 3], sn = ts[s][e >> 2][e & 3];
+              const float lo = x[s][e];
+              // (the partner chunk is picked without dynamic register indexing)
+              const float hi = hs == 1 ? x[s + 1][e] : hs == 2 ? x[s + 2][e] : x[s + 4][e];
+              x[s][e] = lo * cs - hi * sn;
+              const float nhi = hi * cs + lo * sn;
+              if (hs == 1) x[s + 1][e] = nhi;
+              else if (hs == 2) x[s + 2][e] = nhi;
+              else x[s + 4][e] = nhi;
+            }
+          }
         }
       }
+    } else if (ROT == 2) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = vw[j] ? x[e] * qscale : 0.f;
-      const int row = 32 * (NP * hb + j) + grp;  // 0 .. 255
-      const int rr = row & 63;
-      *(u32x4*)(qstage(row >> 6) + rr * HD + ((c ^ (rr & 15)) << 3)) = pack8(x);
+      for (int s = 0; s < 8; ++s) {
+        if (8 * (2 * s + hg) < a.R) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float cs = tc[s][0][e], sn = ts[s][0][e];
+            const float u = x[s][2 * e], v = x[s][2 * e + 1];
+            x[s][2 * e] = u * cs - v * sn;
+            x[s][2 * e + 1] = u * sn + v * cs;
+          }
+        }
+      }
     }
+    const float qscale = a.scale * kLog2e;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[s][e] = qvalid ? x[s][e] * qscale : 0.f;
+      qop[s] = as_bf16x8(pack8(x[s]));
     }
   }
-  __syncthreads();  // staging complete
-  bf16x8 qop[8];  // read from the staging area just before the loop
 
   // ---- band: first key past the newest query, first key the oldest query may see ----
   // (a guess is right when the key before it is below the target and the key at it is not; if
@@ -762,16 +769,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   };
 
   if (a.has_floor() && n_tiles > 0) issue_tile(j_lo, std::integral_constant<int, 0>());
-  // this lane's query operands from the staging rows (chunk 2s + hg of row 32w + ql)
-  {
-    const int rr = ((w & 1) << 5) + ql;
-    const uint16_t* st = qstage(w >> 1) + rr * HD;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qop[s] = as_bf16x8(*(const u32x4*)(st + (((2 * s + hg) ^ (rr & 15)) << 3)));
-  }
   __builtin_amdgcn_s_waitcnt(0);  // also retires the early first-tile loads when n_tiles == 0
   commit_kpos(std::integral_constant<int, 0>());
-  __syncthreads();  // staging read by every wave: buffer 1 is free for tile 1
+  __syncthreads();  // the first tile and its key positions are visible to every wave
   if (n_tiles > 1) issue_tile(j_lo + BN, std::integral_constant<int, 1>());
   if (nsteps > 0) s_a = qk(std::integral_constant<int, 0>(), std::integral_constant<int, 0>());
   using P0 = std::integral_constant<int, 0>;
