@@ -4,13 +4,13 @@
 // Two launches:
 //  1. rows_prep_kernel: every NEW key row (index >= n_cached) is RMS-normed and rotated once
 //     ([Models] "What differs": q/k norm then rotation; [Guide] section 3.2 and section 4) and
-//     written, rounded to bf16, to the workspace; the workspace also holds the last 63 cached rows
+//     written, rounded to bf16, to the workspace; the workspace also holds the last 31 cached rows
 //     (copied as stored) so that every key tile reads a single source.  Other cached rows are
 //     used in place.  This is the cache-append step of the page's flow (rotate,
 //     then cache.update) and costs one read and one write of the new keys, instead of redoing the
 //     norm and rotation each time a key tile is revisited by another query block.
 //  2. prefill_stream_kernel: the attention proper.  Same tiling and math as the fused kernel
-//     (8 wavefronts x 32 query rows of one KV head, S^T = K Q^T and O^T = V^T P^T on
+//     (4 wavefronts x 32 query rows of one KV head, 32-key tiles, S^T = K Q^T and O^T = V^T P^T on
 //     v_mfma_f32_32x32x16_bf16, online softmax in log2 units with lazy rescaling), but K and V
 //     tiles travel from HBM straight into LDS with buffer_load ... lds: no VGPR staging, no LDS
 //     store instructions, 32-bit offsets from a buffer descriptor, and the descriptor's range check
@@ -25,11 +25,13 @@ namespace gqa {
 namespace {
 
 constexpr int HD = 128;
-constexpr int NW = 8;
+constexpr int NW = 4;
 constexpr int NT = NW * 64;
 constexpr int ROWS = NW * 32;
-constexpr int BN = 64;
+constexpr int BN = 32;
 constexpr int TILE_ELEMS = BN * HD;
+constexpr int kTileRounds = BN / (4 * NW);  // 1 KB loads per wave per K (or V) tile
+static_assert(BN % (4 * NW) == 0 && BN <= 64, "tile loader and key-position loader layout");
 constexpr float kRescaleThreshold = 8.0f;
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit dwords, range checked
 
@@ -327,7 +329,9 @@ struct StreamArgs {
 };
 
 template <int ROT, bool NORM, bool CAP>
-__global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, int nqb) {
+// Two workgroups per CU (3 x 16 KB tiles of LDS and up to 256 VGPRs each): one's query prep and
+// first tiles overlap the other's loop, and each barrier holds only the four waves of one group.
+__global__ __launch_bounds__(NT, 2) void prefill_stream_kernel(StreamArgs sa, int nqb) {
   const AttnArgs& a = sa.a;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -404,14 +408,14 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
 
   uint32_t kp_pend = 0;
   bool kp_pend_ok = false;
-  // Tile loader: wave w, round i fills LDS rows 4*(w + 8i) .. +3 (1 KB); lane -> row 4(w+8i) +
-  // lane/16, LDS chunk lane%16, which holds source chunk (lane%16) ^ (row & 15).
+  // Tile loader: wave w, round i fills LDS rows 4*(w + NW i) .. +3 (1 KB); lane -> row
+  // 4(w + NW i) + lane/16, LDS chunk lane%16, which holds source chunk (lane%16) ^ swz(row).
   // Lane constants of the tile loader (offset of the lane's 16 bytes within a tile); a tile adds
   // jt rows.  Rows at or past S fall outside the descriptors' ranges and read as zero.
-  int lk[2], lv[2];
+  int lk[kTileRounds], lv[kTileRounds];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 4 * (w + 8 * i) + (lane >> 4);
+  for (int i = 0; i < kTileRounds; ++i) {
+    const int r = 4 * (w + NW * i) + (lane >> 4);
     lk[i] = r * row_bytes + (((lane & 15) ^ kswz(r)) << 4);
     lv[i] = r * row_bytes + (((lane & 15) ^ vswz(r)) << 4);
   }
@@ -422,9 +426,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     const i32x4 rks = from_k ? rk : rw;
     const int kb0 = from_k ? tb : (jt - w0) * row_bytes;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      lds_void* kdst = (lds_void*)(kbuf<buf>() + 4 * (w + 8 * i) * HD);
-      lds_void* vdst = (lds_void*)(vbuf<buf>() + 4 * (w + 8 * i) * HD);
+    for (int i = 0; i < kTileRounds; ++i) {
+      lds_void* kdst = (lds_void*)(kbuf<buf>() + 4 * (w + NW * i) * HD);
+      lds_void* vdst = (lds_void*)(vbuf<buf>() + 4 * (w + NW * i) * HD);
       tile_dma16(rv, vdst, lv[i] + tb);
       tile_dma16(rks, kdst, lk[i] + kb0);
     }
@@ -433,12 +437,12 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     // position test alone masks the ragged tail
     if (w == 0) {
       kp_pend = __builtin_amdgcn_raw_buffer_load_b32(rp, (jt + lane) * 4, 0, 0);
-      kp_pend_ok = jt + lane < a.S;
+      kp_pend_ok = lane < BN && jt + lane < a.S;
     }
   };
   auto commit_kpos = [&](auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    if (w == 0) pbuf<buf>()[lane] = kp_pend_ok ? (int32_t)kp_pend : INT32_MAX;
+    if (w == 0 && lane < BN) pbuf<buf>()[lane] = kp_pend_ok ? (int32_t)kp_pend : INT32_MAX;
   };
 
   // Without a window or chunks the first tile starts at key 0: start its loads before the query
@@ -610,10 +614,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   const float cap2 = a.softcap * kLog2e;
   const float inv_cap2 = CAP ? 1.0f / cap2 : 0.f;
 
-  // per-lane LDS read offsets (elements).  K: row ql (+32 for the second half), chunk 2s + hg.
-  // V^T (transposing reads): rows 4*hgv + s16/4 (+8 for items 4..7) of each 16-key group,
-  // columns db*32 + 16*(gi&1) + 4*(s16&3); both swizzles only see the row's low 4 bits, which
-  // the 16- and 32-key group offsets leave unchanged.
+  // per-lane LDS read offsets (elements).  K: row ql, chunk 2s + hg.  V^T (transposing reads):
+  // rows 4*hgv + s16/4 (+8 for items 4..7) of each 16-key group, columns db*32 + 16*(gi&1) +
+  // 4*(s16&3); both swizzles only see the row's low 4 bits, which the 16-key group offset leaves
+  // unchanged.
   const int gi = lane >> 4, s16 = lane & 15;
   const int hgv = gi >> 1;
   int koff[8];
@@ -635,11 +639,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   // wait for this row's position before any other load is issued, later it costs registers)
   const int32_t qp32 = qvalid ? (int32_t)qp : INT32_MIN;
 
-  // S^T - m_eff for the 32 keys of half kb of a buffered tile
-  auto qk = [&](auto bufc, auto kbc) {
+  // S^T - m_eff for the 32 keys of a buffered tile
+  auto qk = [&](auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    constexpr int kb = decltype(kbc)::value;
-    const uint16_t* ks = kbuf<buf>() + kb * 32 * HD;
+    const uint16_t* ks = kbuf<buf>();
     u32x4 kop[8];
 #pragma unroll
     for (int st = 0; st < 8; ++st) kop[st] = *(const u32x4*)(ks + koff[st]);
@@ -655,25 +658,22 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     return acc;
   };
 
-  // One step = one 32-key half of a tile, software-pipelined: the step's own S^T was computed by
-  // the previous step; here the mask and running max come first, then the NEXT step's S^T MFMAs
-  // are issued, then this step's exponentials and P V.  In program order the next S^T MFMAs
-  // therefore sit beside this step's exponentials, and this step's P V MFMAs beside the next
-  // step's mask and max, so the matrix unit and the vector ALU work at the same time.
-  // Tiles live in NBUF = 3 buffers: the barrier before the first S^T of tile t+1 (issued during
-  // the second half of tile t) waits for tile t+1's loads, and once every wavefront is past it the
-  // buffer of tile t-1 is free for tile t+2's loads.
-  const int nsteps = 2 * n_tiles;
+  // One step = one 32-key tile, software-pipelined: the step's own S^T was computed by the
+  // previous step; here the mask and running max come first, then the NEXT tile's S^T MFMAs are
+  // issued, then this step's exponentials and P V.  In program order the next S^T MFMAs therefore
+  // sit beside this step's exponentials, and this step's P V MFMAs beside the next step's mask and
+  // max, so the matrix unit and the vector ALU work at the same time.
+  // Tiles live in NBUF = 3 buffers: the barrier before the S^T of tile t+1 waits for tile t+1's
+  // loads, and once every wavefront is past it the buffer of tile t-1 is free for tile t+2's.
+  const int nsteps = n_tiles;
   // two score sets that trade roles every step (a step reads one and fills the other), so no
   // copy of the next step's scores has to wait for its MFMAs
   f32x16 s_a, s_b;
   auto step = [&](int s, auto phc, f32x16& sc, f32x16& s_next) {
-    constexpr int PH = decltype(phc)::value;  // position in the 6-step buffer cycle
-    constexpr int buf = PH >> 1;
-    constexpr int kb = PH & 1;
-    constexpr int nbuf = kb ? (buf + 1) % NBUF : buf;
-    constexpr int nkb = kb ^ 1;
-    const int t = s >> 1;
+    constexpr int PH = decltype(phc)::value;  // position in the 6-step cycle (buffers x score sets)
+    constexpr int buf = PH % NBUF;
+    constexpr int nbuf = (buf + 1) % NBUF;
+    const int t = s;
     const int jt = j_lo + t * BN;
     const int32_t* kpt = pbuf<buf>();
     const int32_t kfirst = kpt[0];
@@ -695,7 +695,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     if (!full) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int32_t kp = kpt[kb * 32 + 8 * (r >> 2) + 4 * hg + (r & 3)];
+        const int32_t kp = kpt[8 * (r >> 2) + 4 * hg + (r & 3)];
         if (!(kp <= qp32 && kp >= qlo32)) sc[r] = -INFINITY;
       }
     }
@@ -719,8 +719,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
       for (int r = 0; r < 16; ++r) sc[r] -= delta;
     }
 
-    // ---- the next step's S^T (first crossing into the next tile when kb == 1) ----
-    if (kb == 1 && s + 1 < nsteps) {
+    // ---- the next tile's S^T, after the crossing into it ----
+    if (s + 1 < nsteps) {
       __builtin_amdgcn_s_waitcnt(0);
       commit_kpos(std::integral_constant<int, nbuf>());
       __syncthreads();
@@ -729,7 +729,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     // Issued unconditionally so that it shares one basic block with the exponentials and P V
     // below (the scheduler interleaves only within a block); after the last step it reads a
     // stale buffer and its result is unused.
-    s_next = qk(std::integral_constant<int, nbuf>(), std::integral_constant<int, nkb>());
+    s_next = qk(std::integral_constant<int, nbuf>());
 
     // ---- P = exp2(s - m); row sums of the bf16 weights the P V product uses, two per
     // v_dot2_f32_bf16 against (1, 1) ----
@@ -757,7 +757,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const int base = (kb * 32 + 16 * u) * HD;
+        const int base = 16 * u * HD;
         const i16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(vs + base + voff[0][db]));
         const i16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -773,7 +773,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   commit_kpos(std::integral_constant<int, 0>());
   __syncthreads();  // the first tile and its key positions are visible to every wave
   if (n_tiles > 1) issue_tile(j_lo + BN, std::integral_constant<int, 1>());
-  if (nsteps > 0) s_a = qk(std::integral_constant<int, 0>(), std::integral_constant<int, 0>());
+  if (nsteps > 0) s_a = qk(std::integral_constant<int, 0>());
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   using P2 = std::integral_constant<int, 2>;

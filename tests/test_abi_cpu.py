@@ -98,8 +98,8 @@ def test_prefill_rejects_bad_sizes_and_pointers():
     assert _prefill(c, ws=FAKE + 16, ws_bytes=1 << 20) == 5
     cr = _cfg(rotary_dim=128, cos_table=FAKE, sin_table=FAKE, table_len=8)
     need = lib.gqa_prefill_workspace_bytes(ctypes.byref(cr), 2, 300, 100)
-    # new keys plus the last 63 cached rows (so that a key tile reads one source), bf16
-    assert need == 2 * (200 + 63) * 8 * 128 * 2
+    # new keys plus the last 31 cached rows (so that a 32-key tile reads one source), bf16
+    assert need == 2 * (200 + 31) * 8 * 128 * 2
     assert _prefill(cr, B=2, L=300, S=300, n_cached=100, ws=FAKE, ws_bytes=need - 2) == 5
     assert lib.gqa_prefill_workspace_bytes(ctypes.byref(cr), 2, 300, 300) == 0  # all cached
     assert lib.gqa_prefill_workspace_bytes(ctypes.byref(_cfg()), 2, 300, 0) == 0  # nothing to prep
