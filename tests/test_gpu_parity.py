@@ -204,6 +204,25 @@ def test_prefill_per_sequence_positions(policy):
     check(gpu_prefill(wl, x), ref_prefill(wl, x))
 
 
+@pytest.mark.parametrize("window,chunk,n_cached", [(0, 0, 0), (37, 0, 0), (100, 0, 150),
+                                                  (0, 48, 0), (0, 40, 120)])
+def test_prefill_gapped_key_positions(window, chunk, n_cached, policy):
+    # nondecreasing key positions with gaps and repeats (the queries sit at the new keys'
+    # positions): the band edges cannot be inferred from the first key's position, so the kernel
+    # has to search for them
+    wl = BASE.with_(qk_norm=False, window=window, chunk=chunk, n_cached=n_cached,
+                    L=300 - n_cached, S=300)
+    say("gapped key positions", window, chunk, n_cached, "policy", policy)
+    x = prefill_inputs(wl, seed=13)
+    rng = np.random.default_rng(13)
+    for b in range(wl.B):
+        kp = (np.cumsum(rng.integers(0, 4, wl.S)) + 5 * b).astype(np.int32)
+        x["key_positions"][b] = kp
+        x["positions"][b] = kp[n_cached:]
+    assert (np.diff(x["key_positions"], axis=1) == 0).any()
+    check(gpu_prefill(wl, x), ref_prefill(wl, x))
+
+
 def test_prefill_shared_positions_stride0():
     wl = BASE.with_(qk_norm=False, window=64)
     x = prefill_inputs(wl, seed=10)
