@@ -445,9 +445,6 @@ __global__ __launch_bounds__(NT, 2) void prefill_stream_kernel(StreamArgs sa, in
     if (w == 0 && lane < BN) pbuf<buf>()[lane] = kp_pend_ok ? (int32_t)kp_pend : INT32_MAX;
   };
 
-  // Without a window or chunks the first tile starts at key 0: start its loads before the query
-  // prep.
-  if (!a.has_floor()) issue_tile(0, std::integral_constant<int, 0>());
 
   // ---- band guesses: with consecutive key positions the band edges are known from the query
   // positions; the two keys around each guess are loaded now (clamped indices) and checked below
@@ -464,6 +461,13 @@ __global__ __launch_bounds__(NT, 2) void prefill_stream_kernel(StreamArgs sa, in
   const int32_t floor_max = (int32_t)max<int64_t>(key_floor(a, qmax), INT32_MIN);
   const int g_hi = (int)min<int64_t>(max<int64_t>(x_hi - kp0, 0), a.S);
   const int g_lo = (int)min<int64_t>(max<int64_t>(x_lo - kp0, 0), a.S);
+  // The first tile's loads go out now -- at key 0 without a window or chunks, else at the guessed
+  // band start (loaded again below if the guess is wrong) -- after the waits for the position
+  // loads above (a wait for those placed behind the tile's loads would wait for the tile too) and
+  // beside the band and query-prep loads below.
+  const int j_first = a.has_floor() ? g_lo : 0;
+  __builtin_amdgcn_sched_barrier(0);
+  issue_tile(j_first, std::integral_constant<int, 0>());
   const int32_t hi_l = kpos_b[max(g_hi - 1, 0)], hi_r = kpos_b[min(g_hi, a.S - 1)];
   const int32_t lo_l = kpos_b[max(g_lo - 1, 0)], lo_r = kpos_b[min(g_lo, a.S - 1)];
   // smallest key position the row may see (window, chunks); INT32_MAX for rows past the end
@@ -768,7 +772,10 @@ __global__ __launch_bounds__(NT, 2) void prefill_stream_kernel(StreamArgs sa, in
       }
   };
 
-  if (a.has_floor() && n_tiles > 0) issue_tile(j_lo, std::integral_constant<int, 0>());
+  if (j_lo != j_first && n_tiles > 0) {
+    __builtin_amdgcn_s_waitcnt(0);  // the guessed tile's loads land before the right tile's
+    issue_tile(j_lo, std::integral_constant<int, 0>());
+  }
   __builtin_amdgcn_s_waitcnt(0);  // also retires the early first-tile loads when n_tiles == 0
   commit_kpos(std::integral_constant<int, 0>());
   __syncthreads();  // the first tile and its key positions are visible to every wave
