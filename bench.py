@@ -79,15 +79,17 @@ def decode_bytes(wl, lens):
             + 2 * wl.B * wl.Hq * wl.D * eb + 4 * wl.B)
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter runs (profiles/traffic.json:
-    FETCH_SIZE and WRITE_SIZE scaled by a known-size copy), or None when the kernel's source has
-    changed since the counters were taken."""
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter runs
+    (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE scaled by a known-size copy), or None when
+    the counters were taken on another workload or the kernel's source has changed since."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)["kernels"][kernel]
+        if rec.get("workload") != workload:
+            return None
         with open(os.path.join(ROOT, rec["source"]), "rb") as f:
             if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
                 return None
@@ -461,7 +463,7 @@ def main(argv=None):
         "roofline": {"bound": "mfma", "kernel": "prefill_stream_kernel",
                      "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("prefill_stream_kernel"),
+                     "traffic": measured_traffic("prefill_stream_kernel", wl.name),
                      "kernel_ms_mean": round(kern_ms, 4),
                      "kernel_ms_median": round(kern_med, 4), "algorithmic_flop": flops},
         "step_parts_ms": {k: round(v[0], 4) for k, v in stats.items()},
@@ -487,7 +489,7 @@ def main(argv=None):
                                       "decode_combine_kernel (one gqa_attn_decode call)",
                             "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(gbs / HBM_PEAK_GBS, 4),
-                            "traffic": measured_traffic("decode_split_kernel"),
+                            "traffic": measured_traffic("decode_split_kernel", dwl.name),
                             "kernel_ms_mean": round(dms, 4), "kernel_ms_median": round(dmed, 4)}}
         if not args.no_cpu_baseline:
             dec["cpu_baseline"] = cpu_baseline_decode(dwl, dx, torch)
@@ -519,7 +521,7 @@ def main(argv=None):
                          "kernel": "mla_split_kernel + mla_combine_kernel (one gqa_mla_decode call)",
                          "achieved": round(mgbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(mgbs / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic("mla_split_kernel"),
+                         "traffic": measured_traffic("mla_split_kernel", mwl.name),
                          "mfma_tflops": round(mtf, 1),
                          "mfma_frac": round(mtf / MFMA_BF16_PEAK_TFLOPS, 4)}}
     print(json.dumps(line), flush=True)

@@ -243,6 +243,19 @@ def test_decode_byte_model_matches_page(golden):
         assert row["layers"] * per_layer * 32768 / 2 ** 30 == pytest.approx(row["GiB_for_32k_tokens"])
 
 
+def test_counter_traffic_only_for_its_workload():
+    # the HBM byte counters were taken on one workload per kernel: a bench line for another
+    # workload reports no traffic rather than those bytes
+    import bench
+    import json
+    with open(os.path.join(os.path.dirname(bench.__file__), "profiles", "traffic.json")) as f:
+        kernels = json.load(f)["kernels"]
+    for kernel, rec in kernels.items():
+        assert bench.measured_traffic(kernel, rec["workload"] + "_other") is None
+        got = bench.measured_traffic(kernel, rec["workload"])
+        assert got is None or got == int(rec["hbm_bytes_per_launch"])
+
+
 def test_prefill_flop_model():
     # allowed (query, key) pairs per (b, h) for the workloads, counted by brute force over
     # positions at a reduced size and by the closed form used in the bench
