@@ -58,6 +58,14 @@ def policy(request):
     PATH["path"] = "stream"
 
 
+@pytest.fixture(params=["mfma", "generic"])
+def dpolicy(request):
+    """Decode kernel path: the MFMA split-KV kernels, or generic (one wave per row, fp32 math)."""
+    g.set_kernel_policy(1 if request.param == "generic" else 0)
+    yield request.param
+    g.set_kernel_policy(0)
+
+
 def mask_kw(wl):
     """Sinks and chunking of a workload, as oracle keyword arguments."""
     return dict(sinks=draw_sinks(wl), chunk=wl.chunk, chunk_lookback=wl.chunk_lookback)
@@ -304,9 +312,8 @@ DEC_VARIANTS = {
 
 
 @pytest.mark.parametrize("name", list(DEC_VARIANTS))
-def test_decode_variants(name, policy):
-    if policy == "fused":
-        pytest.skip("decode has no fused/stream distinction")
+def test_decode_variants(name, dpolicy):
+    policy = dpolicy
     wl = DEC_VARIANTS[name]
     say("decode variant", name, "policy", policy)
     lens, q, qw = decode_lens_q(wl, seed=21)
@@ -550,9 +557,8 @@ def test_prefill_rope_schedules(name, wkw, policy):
 
 
 @pytest.mark.parametrize("name", ["yarn_mscale", "longrope_long"])
-def test_decode_rope_schedules(name, policy):
-    if policy == "fused":
-        pytest.skip("decode has no fused/stream distinction")
+def test_decode_rope_schedules(name, dpolicy):
+    policy = dpolicy
     wl = DEC.with_(rope_kind="default", theta=1e4, qk_norm=True)
     say("decode schedule", name, "policy", policy)
     lens, q, qw = decode_lens_q(wl, seed=23)
