@@ -38,8 +38,8 @@ namespace {
 constexpr int HD = 128;
 constexpr int DWAVES = 4;
 constexpr int DT = DWAVES * 64;
-constexpr int SPLIT = 1024;
-constexpr int SUB = SPLIT / DWAVES;  // keys per wavefront
+constexpr int SPLIT = 1024;         // keys per split of a short walk; long walks take 2 SPLIT
+constexpr int kLongWalk = 8192;     // walks longer than this many keys use the long splits
 constexpr int KBLK = 32;             // keys per block
 constexpr int MAXG = 16;
 constexpr int kPlanMax = 2048;       // sequences per launch of the split kernel
@@ -231,6 +231,14 @@ __device__ __forceinline__ void load_block_paged(const DecodeArgs& da, int b, in
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Keys per split of a sequence whose walk covers `range` keys.  Long walks take 2048-key splits
+// (fewer items, so less per-item work and fewer partials to merge); short ones keep 1024, so that
+// a batch of short walks still spreads over every workgroup.  The split and combine kernels both
+// use it; the partials keep a stride of ceil(S / SPLIT) splits per (sequence, KV head).
+__device__ __forceinline__ int split_keys(int range) {
+  return range > kLongWalk ? 2 * SPLIT : SPLIT;
+}
+
 template <bool CAP, bool PAGED>
 __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs da) {
   __shared__ SplitSmem sm;
@@ -244,7 +252,8 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
     const int n = min(max(a.lens[i], 0), a.S);
     const int start = walk_start(a, n, PAGED);
     sm.len[i] = n;
-    sm.plan[i] = ((n - start + SPLIT - 1) / SPLIT) * Hkv;
+    const int sz = split_keys(n - start);
+    sm.plan[i] = ((n - start + sz - 1) / sz) * Hkv;
   }
   __syncthreads();
   {
@@ -298,10 +307,11 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
     it.sp = r - it.g * nsp;
     const int start = walk_start(a, n, PAGED);
     it.klo = first_key(a, n);
-    const int ks = start + it.sp * SPLIT;
-    const int ke = min(ks + SPLIT, n);
-    it.ws = ks + w * SUB;
-    it.we = min(it.ws + SUB, ke);
+    const int sz = split_keys(n - start), sub = sz / DWAVES;  // keys per split, per wavefront
+    const int ks = start + it.sp * sz;
+    const int ke = min(ks + sz, n);
+    it.ws = ks + w * sub;
+    it.we = min(it.ws + sub, ke);
     it.nblk = it.we > it.ws ? (it.we - it.ws + KBLK - 1) / KBLK : 0;
     return it;
   };
@@ -521,7 +531,8 @@ __global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs da) {
   const int G = a.G, g = h / G, hs = h % G;
   const int n = min(max(a.lens[b], 0), a.S);
   const int start = walk_start(a, n, da.table != nullptr);
-  const int nsp = (n - start + SPLIT - 1) / SPLIT;
+  const int sz = split_keys(n - start);
+  const int nsp = (n - start + sz - 1) / sz;
   const int64_t item0 = (((int64_t)b * a.Hkv + g) * da.nsplit) * G + hs;
   const float* ml = da.part_ml;
   if (d < 64) {
