@@ -38,8 +38,8 @@ namespace {
 constexpr int HD = 128;
 constexpr int DWAVES = 4;
 constexpr int DT = DWAVES * 64;
-constexpr int SPLIT = 1024;         // keys per split of a short walk; long walks take 2 SPLIT
-constexpr int kLongWalk = 8192;     // walks longer than this many keys use the long splits
+constexpr int SPLIT = 1024;         // keys per split; with enough work, 2 SPLIT (see split_keys)
+constexpr int kLongItems = 8;       // items per resident workgroup that call for the long splits
 constexpr int KBLK = 32;             // keys per block
 constexpr int MAXG = 16;
 constexpr int kPlanMax = 2048;       // sequences per launch of the split kernel
@@ -58,6 +58,8 @@ struct DecodeArgs {
   float* part_ml;     // [B, Hkv, nsplit, G, 2] running max (log2 units) and sum
   uint16_t* qprep;    // [B, Hq, D] prepared queries (bf16, log2 units)
   int32_t nsplit;     // splits per (b, g) allotted in the workspace
+  int32_t plan_seqs;  // sequences per launch of the split kernel (the launches' plan sets)
+  int32_t resident;   // split workgroups resident on the device
   // paged cache (table non-null): a.k, a.v are pools [num_blocks, Hkv, 2^log2bs, D]; slot j of
   // sequence b is row j % bs of block table[b * max_blocks + j / bs]
   const int32_t* table;
@@ -231,12 +233,17 @@ __device__ __forceinline__ void load_block_paged(const DecodeArgs& da, int b, in
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Keys per split of a sequence whose walk covers `range` keys.  Long walks take 2048-key splits
-// (fewer items, so less per-item work and fewer partials to merge); short ones keep 1024, so that
-// a batch of short walks still spreads over every workgroup.  The split and combine kernels both
-// use it; the partials keep a stride of ceil(S / SPLIT) splits per (sequence, KV head).
-__device__ __forceinline__ int split_keys(int range) {
-  return range > kLongWalk ? 2 * SPLIT : SPLIT;
+// Keys per split of a walk of `range` keys.  When a launch's sequences hold at least kLongItems
+// items (at SPLIT keys) per resident workgroup, walks longer than SPLIT take 2 SPLIT keys per
+// item (fewer items, so less per-item work and fewer partials to merge); otherwise, or for short
+// walks, SPLIT, so that a batch of short walks still spreads over every workgroup.  The split
+// and combine kernels decide alike from the same sequences; the partials keep a stride of
+// ceil(S / SPLIT) splits per (sequence, KV head).
+__device__ __forceinline__ int split_keys(int range, bool longs) {
+  return longs && range > SPLIT ? 2 * SPLIT : SPLIT;
+}
+__device__ __forceinline__ bool use_long_splits(int64_t short_items, int resident) {
+  return short_items >= (int64_t)kLongItems * resident;
 }
 
 template <bool CAP, bool PAGED>
@@ -252,11 +259,11 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
     const int n = min(max(a.lens[i], 0), a.S);
     const int start = walk_start(a, n, PAGED);
     sm.len[i] = n;
-    const int sz = split_keys(n - start);
-    sm.plan[i] = ((n - start + sz - 1) / sz) * Hkv;
+    sm.plan[i] = ((n - start + SPLIT - 1) / SPLIT) * Hkv;
   }
   __syncthreads();
-  {
+  // exclusive prefix of sm.plan[0 .. B) in place, the total in sm.plan[B]
+  auto scan_plan = [&]() {
     const int per = (B + DT - 1) / DT;
     const int i0 = min(tid * per, B), i1 = min(i0 + per, B);
     int loc = 0;
@@ -278,6 +285,20 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
     }
     if (tid == 0) sm.plan[B] = sm.wsum[0] + sm.wsum[1] + sm.wsum[2] + sm.wsum[3];
     __syncthreads();
+  };
+  scan_plan();
+  const bool longs =
+      use_long_splits(__builtin_amdgcn_readfirstlane(sm.plan[B]), da.resident);
+  if (longs) {  // plan again with the long splits (uniform: every wave read the same total)
+    __syncthreads();
+    for (int i = tid; i < B; i += DT) {
+      const int n = sm.len[i];
+      const int start = walk_start(a, n, PAGED);
+      const int sz = split_keys(n - start, true);
+      sm.plan[i] = ((n - start + sz - 1) / sz) * Hkv;
+    }
+    __syncthreads();
+    scan_plan();
   }
   const int total = __builtin_amdgcn_readfirstlane(sm.plan[B]);
   if ((int)blockIdx.x >= total) return;
@@ -307,7 +328,7 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
     it.sp = r - it.g * nsp;
     const int start = walk_start(a, n, PAGED);
     it.klo = first_key(a, n);
-    const int sz = split_keys(n - start), sub = sz / DWAVES;  // keys per split, per wavefront
+    const int sz = split_keys(n - start, longs), sub = sz / DWAVES;  // keys per split, per wave
     const int ks = start + it.sp * sz;
     const int ke = min(ks + sz, n);
     it.ws = ks + w * sub;
@@ -531,7 +552,20 @@ __global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs da) {
   const int G = a.G, g = h / G, hs = h % G;
   const int n = min(max(a.lens[b], 0), a.S);
   const int start = walk_start(a, n, da.table != nullptr);
-  const int sz = split_keys(n - start);
+  // the split kernel's choice of split size, from the same sequences: those of b's launch
+  const int c0 = b / da.plan_seqs * da.plan_seqs, c1 = min(c0 + da.plan_seqs, a.B);
+  int64_t cnt = 0;
+  for (int i = c0 + d; i < c1; i += HD) {
+    const int ni = min(max(a.lens[i], 0), a.S);
+    cnt += (int64_t)((ni - walk_start(a, ni, da.table != nullptr) + SPLIT - 1) / SPLIT) * a.Hkv;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+  __shared__ int64_t cnt_w[HD / 64];
+  if ((d & 63) == 0) cnt_w[d >> 6] = cnt;
+  __syncthreads();
+  const bool longs = use_long_splits(cnt_w[0] + cnt_w[1], da.resident);
+  const int sz = split_keys(n - start, longs);
   const int nsp = (n - start + sz - 1) / sz;
   const int64_t item0 = (((int64_t)b * a.Hkv + g) * da.nsplit) * G + hs;
   const float* ml = da.part_ml;
@@ -649,6 +683,8 @@ hipError_t launch_decode_mfma(const AttnArgs& a, void* workspace, hipStream_t st
   const int64_t per_seq = (int64_t)a.Hkv * d.nsplit;
   const int chunk = (int)std::min<int64_t>(kPlanMax, std::max<int64_t>(1, INT32_MAX / per_seq));
   const int resident = cu_count() * kWgPerCu;
+  d.plan_seqs = chunk;
+  d.resident = resident;
   for (int b0 = 0; b0 < a.B; b0 += chunk) {
     const int nb = std::min(chunk, a.B - b0);
     DecodeArgs c = d;
