@@ -21,8 +21,8 @@ __all__ = [
     "rope_attention_factor", "rope_softmax_scale",
     "attn_prefill", "attn_decode", "decode_workspace_bytes", "PagedKV", "paged_append",
     "paged_decode_workspace_bytes", "attn_decode_paged", "mla_decode_workspace_bytes",
-    "mla_decode", "prefill_workspace_bytes", "prep_keys", "last_error", "set_kernel_policy",
-    "LIB_PATH", "EXPORTS",
+    "mla_decode", "prefill_workspace_bytes", "prep_keys", "last_error", "KERNELS",
+    "hip_runtimes_mapped", "LIB_PATH", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_rope.so")
@@ -30,6 +30,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_rope
 GQA_F32, GQA_BF16 = 0, 1
 ROPE_KINDS = {"default": 0, "linear": 1, "llama3": 2, "yarn": 3, "longrope": 4}
 ROT_STYLES = {"half": 0, "interleaved": 1}
+# gqa_attn_cfg.kernel (gqa_kernel_select): per-call kernel choice, "auto" in production
+KERNELS = {"auto": 0, "generic": 1, "decode_short": 2, "decode_long": 3}
 STATUS = {0: "GQA_OK", 1: "GQA_E_NULL", 2: "GQA_E_SHAPE", 3: "GQA_E_DTYPE",
           4: "GQA_E_UNSUPPORTED", 5: "GQA_E_WORKSPACE", 6: "GQA_E_HIP", 7: "GQA_E_VALUE"}
 
@@ -62,7 +64,8 @@ class _AttnCfg(ctypes.Structure):
                 ("eps", ctypes.c_double), ("q_norm_w", ctypes.c_void_p),
                 ("k_norm_w", ctypes.c_void_p), ("scale", ctypes.c_double),
                 ("softcap", ctypes.c_double), ("sinks", ctypes.c_void_p),
-                ("chunk_size", ctypes.c_int32), ("chunk_lookback", ctypes.c_int32)]
+                ("chunk_size", ctypes.c_int32), ("chunk_lookback", ctypes.c_int32),
+                ("kernel", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class _PagedKV(ctypes.Structure):
@@ -97,7 +100,6 @@ EXPORTS = {
                                      _I32, _I32, _P, _P, _SZ, _P]),
     "gqa_mla_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "gqa_mla_decode": (_I32, [_P, _P, _P, _I32, _I32, _I32, ctypes.c_double, _P, _P, _SZ, _P]),
-    "gqa_set_kernel_policy": (_I32, [_I32]),
     "gqa_last_error": (ctypes.c_char_p, []),
     "gqa_version": (ctypes.c_char_p, []),
 }
@@ -105,8 +107,31 @@ EXPORTS = {
 _lib = None
 
 
+def hip_runtimes_mapped(maps_text=None):
+    """Distinct HIP runtime files (libamdhip64) mapped into this process, read from
+    /proc/self/maps (or from the given text)."""
+    if maps_text is None:
+        try:
+            with open("/proc/self/maps") as f:
+                maps_text = f.read()
+        except OSError:
+            return set()
+    found = set()
+    for line in maps_text.splitlines():
+        parts = line.split(None, 5)
+        if len(parts) == 6 and os.path.basename(parts[5]).startswith("libamdhip64.so"):
+            path = parts[5].strip()
+            try:
+                path = os.path.realpath(path)
+            except OSError:
+                pass
+            found.add(path)
+    return found
+
+
 def library():
-    """Load libgqa_rope.so (built in-tree by __graft_entry__.build()); raise if it is missing."""
+    """Load libgqa_rope.so (built in-tree by __graft_entry__.build()); raise if it is missing, or
+    if loading it left two HIP runtimes in the process."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
@@ -114,9 +139,15 @@ def library():
                                f"g; g.build()'` (hipcc, gfx950)")
         # torch ships its own HIP runtime (same soname as ROCm's).  Loading torch first makes the
         # library resolve to that runtime, so torch's streams and allocations are valid in it; the
-        # other order would bring a second HIP runtime into the process.
+        # other order would bring a second HIP runtime into the process, in which torch's streams
+        # are invalid and the first call crashes or fails.  That state is detected and refused.
         import torch  # noqa: F401
         lib = ctypes.CDLL(LIB_PATH)
+        runtimes = hip_runtimes_mapped()
+        if len(runtimes) > 1:
+            raise RuntimeError("two HIP runtimes are mapped into this process ("
+                               + ", ".join(sorted(runtimes)) + "): import torch before anything "
+                               "that loads libamdhip64, so that libgqa_rope binds to torch's")
         for name, (res, args) in EXPORTS.items():
             fn = getattr(lib, name)
             fn.restype = res
@@ -132,11 +163,6 @@ def last_error() -> str:
 def _check(status):
     if status != 0:
         raise GQAError(status, last_error())
-
-
-def set_kernel_policy(policy: int):
-    """0: MFMA kernels where they apply (default); 1: generic kernels for everything."""
-    _check(library().gqa_set_kernel_policy(int(policy)))
 
 
 # ------------------------------------------------------------------------------------------------
@@ -164,7 +190,7 @@ class RopeSpec:
 
     def c_struct(self):
         if self.kind not in ROPE_KINDS:
-            raise GQAError(4, f"RoPE type {self.kind!r} is not implemented")
+            raise GQAError(4, f"unknown rope kind {self.kind!r}; known: {', '.join(ROPE_KINDS)}")
 
         def table(v):
             return None if v is None else (ctypes.c_double * len(v))(*[float(x) for x in v])
@@ -271,6 +297,7 @@ class AttnConfig:
     sinks: Optional[object] = None      # device tensor [num_q_heads] fp32: learned sink logits
     chunk_size: int = 0                 # chunked attention: chunk length in positions (0 = off)
     chunk_lookback: int = 0             # chunks before the query's own that stay visible
+    kernel: str = "auto"                # per-call kernel choice (KERNELS); "auto" in production
 
     @property
     def torch_dtype(self):
@@ -298,6 +325,8 @@ class AttnConfig:
                 raise GQAError(1, "q_norm_w and k_norm_w are required when qk_norm is set")
             qw = _need(self.q_norm_w, "q_norm_w", (self.head_dim,), self.torch_dtype).value
             kw = _need(self.k_norm_w, "k_norm_w", (self.head_dim,), self.torch_dtype).value
+        if self.kernel not in KERNELS:
+            raise GQAError(7, f"kernel must be one of {sorted(KERNELS)}, got {self.kernel!r}")
         sk = None
         if self.sinks is not None:
             sk = _need(self.sinks, "sinks", (self.num_q_heads,), torch.float32).value
@@ -305,7 +334,7 @@ class AttnConfig:
                         self.num_q_heads, self.num_kv_heads, self.rotary_dim,
                         ROT_STYLES[self.rot_style], pc, ps, tl, int(bool(self.qk_norm)), self.eps,
                         qw, kw, self.scale, self.softcap, sk, int(self.chunk_size),
-                        int(self.chunk_lookback))
+                        int(self.chunk_lookback), KERNELS[self.kernel], 0)
 
 
 def prep_keys(cfg: AttnConfig, k, key_positions, n_cached=0, k_out=None, stream=None):

@@ -57,9 +57,12 @@ struct DecodeArgs {
   float* part_o;      // [B, Hkv, nsplit, G, D] unnormalised partial outputs
   float* part_ml;     // [B, Hkv, nsplit, G, 2] running max (log2 units) and sum
   uint16_t* qprep;    // [B, Hq, D] prepared queries (bf16, log2 units)
+  int32_t* split_long;  // [launches] 1 when that split launch took the long splits; written by
+                        // the launch's workgroup 0, read by the combine kernel
   int32_t nsplit;     // splits per (b, g) allotted in the workspace
   int32_t plan_seqs;  // sequences per launch of the split kernel (the launches' plan sets)
   int32_t resident;   // split workgroups resident on the device
+  int32_t split_mode; // SplitMode: 0 chosen from the launch's sequences, 1 short, 2 long
   // paged cache (table non-null): a.k, a.v are pools [num_blocks, Hkv, 2^log2bs, D]; slot j of
   // sequence b is row j % bs of block table[b * max_blocks + j / bs]
   const int32_t* table;
@@ -288,7 +291,10 @@ __global__ __launch_bounds__(DT, kWgPerCu) void decode_split_kernel(DecodeArgs d
   };
   scan_plan();
   const bool longs =
-      use_long_splits(__builtin_amdgcn_readfirstlane(sm.plan[B]), da.resident);
+      da.split_mode == 2 ||
+      (da.split_mode == 0 && use_long_splits(__builtin_amdgcn_readfirstlane(sm.plan[B]), da.resident));
+  // the combine kernel takes the launch's choice from here (every workgroup decided alike)
+  if (blockIdx.x == 0 && tid == 0) da.split_long[0] = longs ? 1 : 0;
   if (longs) {  // plan again with the long splits (uniform: every wave read the same total)
     __syncthreads();
     for (int i = tid; i < B; i += DT) {
@@ -552,19 +558,8 @@ __global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs da) {
   const int G = a.G, g = h / G, hs = h % G;
   const int n = min(max(a.lens[b], 0), a.S);
   const int start = walk_start(a, n, da.table != nullptr);
-  // the split kernel's choice of split size, from the same sequences: those of b's launch
-  const int c0 = b / da.plan_seqs * da.plan_seqs, c1 = min(c0 + da.plan_seqs, a.B);
-  int64_t cnt = 0;
-  for (int i = c0 + d; i < c1; i += HD) {
-    const int ni = min(max(a.lens[i], 0), a.S);
-    cnt += (int64_t)((ni - walk_start(a, ni, da.table != nullptr) + SPLIT - 1) / SPLIT) * a.Hkv;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
-  __shared__ int64_t cnt_w[HD / 64];
-  if ((d & 63) == 0) cnt_w[d >> 6] = cnt;
-  __syncthreads();
-  const bool longs = use_long_splits(cnt_w[0] + cnt_w[1], da.resident);
+  // the split size that b's split launch chose
+  const bool longs = da.split_long[b / da.plan_seqs] != 0;
   const int sz = split_keys(n - start, longs);
   const int nsp = (n - start + sz - 1) / sz;
   const int64_t item0 = (((int64_t)b * a.Hkv + g) * da.nsplit) * G + hs;
@@ -632,6 +627,30 @@ int cu_count() {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Sequences per split launch: at most kPlanMax, and few enough that item ids fit in int32.
+int plan_seqs(int Hkv, int64_t nsplit) {
+  const int64_t per_seq = (int64_t)Hkv * nsplit;
+  return (int)std::min<int64_t>(kPlanMax, std::max<int64_t>(1, INT32_MAX / per_seq));
+}
+
+// Workspace: partial outputs | partial (max, sum) | prepared queries | one split flag per launch.
+struct DecodeWs {
+  size_t o, ml, q, flags, total;
+};
+DecodeWs decode_ws_layout(int B, int Hkv, int G, int Smax) {
+  const int64_t nsplit = (Smax + SPLIT - 1) / SPLIT;
+  const int64_t items = (int64_t)B * Hkv * nsplit * G;
+  const int64_t per_launch = plan_seqs(Hkv, nsplit);
+  const int64_t launches = (B + per_launch - 1) / per_launch;
+  DecodeWs w;
+  w.o = 0;
+  w.ml = align256((size_t)items * HD * sizeof(float));
+  w.q = w.ml + align256((size_t)items * 2 * sizeof(float));
+  w.flags = w.q + align256((size_t)B * Hkv * G * HD * sizeof(uint16_t));
+  w.total = w.flags + (size_t)std::max<int64_t>(launches, 1) * sizeof(int32_t);
+  return w;
+}
+
 }  // namespace
 
 int decode_split_keys() { return SPLIT; }
@@ -643,14 +662,12 @@ bool decode_mfma_supported(const AttnArgs& a) {
 }
 
 size_t decode_mfma_workspace_bytes(int B, int Hkv, int G, int D, int Smax) {
-  const int64_t nsplit = (Smax + SPLIT - 1) / SPLIT;
-  const int64_t items = (int64_t)B * Hkv * nsplit * G;
-  return align256((size_t)items * D * sizeof(float)) + align256((size_t)items * 2 * sizeof(float)) +
-         (size_t)B * Hkv * G * D * sizeof(uint16_t);
+  (void)D;  // head_dim is 128 on this path
+  return decode_ws_layout(B, Hkv, G, Smax).total;
 }
 
 hipError_t launch_decode_mfma(const AttnArgs& a, void* workspace, hipStream_t stream,
-                              const PagedKV* paged) {
+                              const PagedKV* paged, SplitMode mode) {
   if (a.B == 0) return hipSuccess;
   DecodeArgs d;
   d.a = a;
@@ -659,12 +676,13 @@ hipError_t launch_decode_mfma(const AttnArgs& a, void* workspace, hipStream_t st
   d.log2bs = paged ? paged->log2bs : 0;
   d.num_blocks = paged ? paged->num_blocks : 0;
   d.nsplit = (a.S + SPLIT - 1) / SPLIT;
-  const int64_t items = (int64_t)a.B * a.Hkv * d.nsplit * a.G;
+  d.split_mode = (int)mode;
+  const DecodeWs wl = decode_ws_layout(a.B, a.Hkv, a.G, a.S);
   char* ws = (char*)workspace;
-  d.part_o = (float*)ws;
-  d.part_ml = (float*)(ws + align256((size_t)items * HD * sizeof(float)));
-  d.qprep = (uint16_t*)(ws + align256((size_t)items * HD * sizeof(float)) +
-                        align256((size_t)items * 2 * sizeof(float)));
+  d.part_o = (float*)(ws + wl.o);
+  d.part_ml = (float*)(ws + wl.ml);
+  d.qprep = (uint16_t*)(ws + wl.q);
+  d.split_long = (int32_t*)(ws + wl.flags);
 
   const int rot = a.R == 0 ? 0 : (a.style == 0 ? 1 : 2);
   const bool norm = a.qk_norm != 0;
@@ -681,7 +699,7 @@ hipError_t launch_decode_mfma(const AttnArgs& a, void* workspace, hipStream_t st
 
   // The split kernel plans at most kPlanMax sequences per launch (and keeps item ids in int32).
   const int64_t per_seq = (int64_t)a.Hkv * d.nsplit;
-  const int chunk = (int)std::min<int64_t>(kPlanMax, std::max<int64_t>(1, INT32_MAX / per_seq));
+  const int chunk = plan_seqs(a.Hkv, d.nsplit);
   const int resident = cu_count() * kWgPerCu;
   d.plan_seqs = chunk;
   d.resident = resident;
@@ -695,6 +713,7 @@ hipError_t launch_decode_mfma(const AttnArgs& a, void* workspace, hipStream_t st
     c.part_o = d.part_o + (int64_t)b0 * per_seq * a.G * HD;
     c.part_ml = d.part_ml + (int64_t)b0 * per_seq * a.G * 2;
     c.qprep = d.qprep + (int64_t)b0 * a.Hq * HD;
+    c.split_long = d.split_long + b0 / chunk;
     const int nwg = (int)std::min<int64_t>((int64_t)nb * per_seq, resident);
     if (d.table) {
       c.a.k = a.k;  // the pools are shared by all sequences

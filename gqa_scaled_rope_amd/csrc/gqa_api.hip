@@ -103,7 +103,8 @@ gqa_status check_rope(const gqa_rope_params* rp) {
       break;
     }
     default:
-      return fail(GQA_E_UNSUPPORTED, "RoPE type %d is not implemented", rp->kind);
+      return fail(GQA_E_UNSUPPORTED, "unknown rope kind %d (0 default, 1 linear, 2 llama3, 3 yarn, "
+                  "4 longrope)", rp->kind);
   }
   if (rp->reserved != 0) return fail(GQA_E_VALUE, "rope params reserved field must be 0");
   return ok();
@@ -127,24 +128,28 @@ double attention_factor_host(const gqa_rope_params* rp) {
 void inv_freq_host(const gqa_rope_params* rp, double* out) {
   const int R = rp->rotary_dim;
   const double two_pi = 6.283185307179586476925286766559;
-  // yarn: the (fractional) pair index that turns r times over the original context solves
-  // original * theta^(-2x/R) = 2 pi r; the ramp runs from the beta_fast pair to the beta_slow one.
-  double ramp_lo = 0.0, ramp_w = 1.0;
+  // yarn: pair index i turns original * theta^(-2i/R) / (2 pi) times over the original context,
+  // fewer as i grows.  The ramp starts at the last index still turning beta_fast times and ends at
+  // the first one turning at most beta_slow times (walked index by index over 0 .. R-1), or, with
+  // yarn_no_truncate, at the fractional indices where the turn count equals each beta.
+  double ramp_a = 0.0, ramp_b = 0.0;
   if (rp->kind == GQA_ROPE_YARN) {
-    const double old = rp->original_max_pos;
-    auto pair_turning = [&](double r) {
-      return R * std::log(old / (r * two_pi)) / (2.0 * std::log(rp->theta));
-    };
-    double lo = pair_turning(rp->beta_fast != 0.0 ? rp->beta_fast : 32.0);
-    double hi = pair_turning(rp->beta_slow != 0.0 ? rp->beta_slow : 1.0);
+    const double orig = rp->original_max_pos;
+    const double fast = rp->beta_fast != 0.0 ? rp->beta_fast : 32.0;
+    const double slow = rp->beta_slow != 0.0 ? rp->beta_slow : 1.0;
+    auto turns_at = [&](double i) { return orig * std::pow(rp->theta, -2.0 * i / R) / two_pi; };
     if (!rp->yarn_no_truncate) {
-      lo = std::floor(lo);
-      hi = std::ceil(hi);
+      int a = 0;
+      while (a + 1 <= R - 1 && turns_at(a + 1) >= fast) ++a;
+      int b = 0;
+      while (b < R - 1 && turns_at(b) > slow) ++b;
+      ramp_a = a;
+      ramp_b = b;
+    } else {
+      const double per_index = 2.0 * std::log(rp->theta) / R;  // ln(turns) drop per index
+      ramp_a = std::max(std::log(turns_at(0) / fast) / per_index, 0.0);
+      ramp_b = std::min(std::log(turns_at(0) / slow) / per_index, (double)(R - 1));
     }
-    lo = std::max(lo, 0.0);
-    hi = std::min(hi, (double)(R - 1));
-    ramp_lo = lo;
-    ramp_w = hi != lo ? hi - lo : 0.001;
   }
   const double* table = nullptr;
   if (rp->kind == GQA_ROPE_LONGROPE)
@@ -167,16 +172,17 @@ void inv_freq_host(const gqa_rope_params* rp, double* out) {
         f = (1.0 - s) * base / rp->factor + s * base;
       }
     } else if (rp->kind == GQA_ROPE_YARN) {
-      const double w = std::min(std::max((i - ramp_lo) / ramp_w, 0.0), 1.0);  // 1: divided
-      f = base / rp->factor * w + base * (1.0 - w);
+      // weight of the divided frequency: 0 up to the ramp's start, 1 from its end; where the two
+      // ends meet, a step just after them
+      const double w = ramp_b > ramp_a ? std::min(std::max((i - ramp_a) / (ramp_b - ramp_a), 0.0), 1.0)
+                                       : (i > ramp_a ? 1.0 : 0.0);
+      f = base * (1.0 - w) + (base / rp->factor) * w;
     } else if (rp->kind == GQA_ROPE_LONGROPE) {
       f = base / table[i];
     }
     out[i] = f;
   }
 }
-
-int g_policy = 0;  // 0 auto, 1 generic kernels only
 
 gqa_status check_cfg(const gqa_attn_cfg* c) {
   if (!c) return fail(GQA_E_NULL, "cfg pointer is null");
@@ -220,6 +226,9 @@ gqa_status check_cfg(const gqa_attn_cfg* c) {
   if (c->chunk_size < 0 || c->chunk_lookback < 0)
     return fail(GQA_E_SHAPE, "chunk_size and chunk_lookback must be >= 0, got %d, %d",
                 c->chunk_size, c->chunk_lookback);
+  if (c->kernel < GQA_KERNEL_AUTO || c->kernel > GQA_KERNEL_DECODE_LONG)
+    return fail(GQA_E_VALUE, "kernel must be a gqa_kernel_select value in [0, 3], got %d", c->kernel);
+  if (c->reserved != 0) return fail(GQA_E_VALUE, "cfg reserved field must be 0");
   return ok();
 }
 
@@ -252,13 +261,6 @@ extern "C" {
 const char* gqa_last_error(void) { return g_err.c_str(); }
 
 const char* gqa_version(void) { return "gqa_rope 0.1.0 (gfx950)"; }
-
-// Kernel policy for tests: 0 = automatic (MFMA kernels where they apply), 1 = generic kernels.
-gqa_status gqa_set_kernel_policy(int32_t policy) {
-  if (policy != 0 && policy != 1) return fail(GQA_E_VALUE, "policy must be 0 or 1, got %d", policy);
-  g_policy = policy;
-  return ok();
-}
 
 gqa_status gqa_rope_inv_freq(const gqa_rope_params* rope, double* inv_freq_out) {
   gqa_status st = check_rope(rope);
@@ -332,7 +334,8 @@ static bool prefill_stream_applies(const gqa_attn_cfg* cfg, const gqa::AttnArgs&
   static const int32_t dummy = 0;
   t.qpos = &dummy;
   t.kpos = &dummy;
-  return cfg->dtype == GQA_BF16 && g_policy == 0 && a.S > 0 && gqa::prefill_stream_supported(t);
+  return cfg->dtype == GQA_BF16 && cfg->kernel != GQA_KERNEL_GENERIC && a.S > 0 &&
+         gqa::prefill_stream_supported(t);
 }
 
 size_t gqa_prefill_workspace_bytes(const gqa_attn_cfg* cfg, int32_t B, int32_t S, int32_t n_cached) {
@@ -395,7 +398,7 @@ gqa_status gqa_attn_prefill(const gqa_attn_cfg* cfg, const void* q, const void* 
       return fail(GQA_E_WORKSPACE, "prefill workspace needs %zu bytes, got %zu", need,
                   workspace_bytes);
   }
-  if (bf16 && g_policy == 0 && S > 0 && gqa::prefill_mfma_supported(a))
+  if (bf16 && cfg->kernel != GQA_KERNEL_GENERIC && S > 0 && gqa::prefill_mfma_supported(a))
     return hip_status(gqa::launch_prefill_mfma(a, stream), "prefill (fused) launch");
   return hip_status(gqa::launch_attn_generic(a, bf16, stream), "prefill (generic) launch");
 }
@@ -423,9 +426,17 @@ gqa_status gqa_prep_keys(const gqa_attn_cfg* cfg, const void* k, const int32_t* 
   return hip_status(gqa::launch_prep_keys(a, k_out, stream), "prep_keys launch");
 }
 
+// Decode split-size choice of a call: automatic, or forced by the kernel selector.
+static gqa::SplitMode decode_split_mode(const gqa_attn_cfg* cfg) {
+  return cfg->kernel == GQA_KERNEL_DECODE_SHORT  ? gqa::SplitMode::kShort
+         : cfg->kernel == GQA_KERNEL_DECODE_LONG ? gqa::SplitMode::kLong
+                                                 : gqa::SplitMode::kAuto;
+}
+
 static bool decode_uses_mfma(const gqa_attn_cfg* cfg) {
   gqa::AttnArgs a = base_args(cfg);
-  return cfg->dtype == GQA_BF16 && g_policy == 0 && gqa::decode_mfma_supported(a);
+  return cfg->dtype == GQA_BF16 && cfg->kernel != GQA_KERNEL_GENERIC &&
+         gqa::decode_mfma_supported(a);
 }
 
 size_t gqa_decode_workspace_bytes(const gqa_attn_cfg* cfg, int32_t B, int32_t Smax) {
@@ -485,7 +496,8 @@ gqa_status gqa_attn_decode(const gqa_attn_cfg* cfg, const void* q, const void* k
                   workspace_bytes, workspace ? "" : " (null)");
     if (((uintptr_t)workspace & 255u) != 0)
       return fail(GQA_E_WORKSPACE, "workspace must be 256-byte aligned");
-    return hip_status(gqa::launch_decode_mfma(a, workspace, stream), "decode (mfma) launch");
+    return hip_status(gqa::launch_decode_mfma(a, workspace, stream, nullptr, decode_split_mode(cfg)),
+                      "decode (mfma) launch");
   }
   return hip_status(gqa::launch_attn_generic(a, cfg->dtype == GQA_BF16, stream),
                     "decode (generic) launch");
@@ -619,7 +631,8 @@ gqa_status gqa_attn_decode_paged(const gqa_attn_cfg* cfg, const void* q, const g
   a.L = 1;
   a.n_cached = Smax;
   a.window = window;
-  return hip_status(gqa::launch_decode_mfma(a, workspace, stream, &pk), "paged decode launch");
+  return hip_status(gqa::launch_decode_mfma(a, workspace, stream, &pk, decode_split_mode(cfg)),
+                    "paged decode launch");
 }
 
 size_t gqa_mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t Smax) {

@@ -44,10 +44,13 @@ struct PagedKV {
 // bf16 split-KV decode for head_dim 128 (query preparation, split kernel, combine kernel); the
 // workspace holds the split partials and the prepared queries.  With `paged`, a.k and a.v are
 // the pools and a.S = max_blocks * block size.
+// Split size of the decode walks: chosen per launch from the batch (kAuto), or fixed at 1024
+// keys (kShort) or 2048 keys for walks longer than 1024 (kLong).
+enum class SplitMode { kAuto = 0, kShort = 1, kLong = 2 };
 bool decode_mfma_supported(const AttnArgs& a);
 size_t decode_mfma_workspace_bytes(int B, int Hkv, int G, int D, int Smax);
 hipError_t launch_decode_mfma(const AttnArgs& a, void* workspace, hipStream_t stream,
-                              const PagedKV* paged = nullptr);
+                              const PagedKV* paged = nullptr, SplitMode mode = SplitMode::kAuto);
 
 // cache.update into a paged pool: rows i < a.L of a.k (normed and rotated at a.kpos, as the key
 // preparation does) and of a.v (copied) go to slots start[b] + i.

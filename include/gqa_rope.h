@@ -123,7 +123,27 @@ typedef struct gqa_attn_cfg {
    * chunk_size 0: no chunking.  Both >= 0. */
   int32_t chunk_size;
   int32_t chunk_lookback;
+  /* Kernel selection for this call (gqa_kernel_select); production callers leave it 0.  Every
+   * choice computes the same result up to rounding order. */
+  int32_t kernel;
+  int32_t reserved;           /* must be 0 */
 } gqa_attn_cfg;
+
+/* Values of gqa_attn_cfg.kernel.  The choice is per call: the library holds no selection state.
+ *   GQA_KERNEL_AUTO          bf16 problems run on the MFMA kernels wherever their shape is
+ *                            covered, everything else on the generic kernel
+ *   GQA_KERNEL_GENERIC       every problem on the generic kernel (one wavefront per query row and
+ *                            head, fp32 arithmetic): a second implementation to compare against
+ *   GQA_KERNEL_DECODE_SHORT  decode on the MFMA kernels with 1024-key splits for every walk
+ *   GQA_KERNEL_DECODE_LONG   decode on the MFMA kernels with 2048-key splits for every walk
+ *                            longer than 1024 keys (AUTO picks between the two by the batch's
+ *                            size); for prefill calls the last two act as AUTO */
+typedef enum gqa_kernel_select {
+  GQA_KERNEL_AUTO = 0,
+  GQA_KERNEL_GENERIC = 1,
+  GQA_KERNEL_DECODE_SHORT = 2,
+  GQA_KERNEL_DECODE_LONG = 3
+} gqa_kernel_select;
 
 /* Build cos/sin tables for positions 0 .. table_len-1 ([Models] "Scaled RoPE", rope_tables):
  * cos_out[p*(R/2) + i] = a * cos(p * inv_freq[i]), sin_out likewise, with a the attention factor
@@ -279,12 +299,11 @@ gqa_status gqa_mla_decode(const void* q, const void* cache, const int32_t* lens,
                           int32_t H, int32_t Smax, double scale, void* out, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
-/* Kernel selection, for tests and comparisons: 0 (default) = bf16 problems run on the MFMA
- * kernels wherever their shape is covered; 1 = every problem runs on the generic kernel (one
- * wavefront per query row and head, fp32 arithmetic).  Process-wide; not thread-safe. */
-gqa_status gqa_set_kernel_policy(int32_t policy);
-
-/* Message for the last non-OK status returned on this thread ("" if none). */
+/* Message for the last non-OK status returned on this thread ("" if none).  The error style
+ * follows the pages: a rope type outside the known set is rejected by name ([Models] "Scaled
+ * RoPE", rope_inv_freq); each refusal message names what failed ([Ster] "Refusals"); and a
+ * request this build cannot serve is refused before any work, never served by a fallback ([Ster]
+ * "Device choice").  Messages here name the offending argument and its accepted range. */
 const char* gqa_last_error(void);
 
 /* Library version string. */

@@ -76,25 +76,35 @@ def rope_inv_freq(rotary_dim, theta, kind="default", factor=1.0, low_freq_factor
     if rotary_dim < 0 or rotary_dim % 2:
         raise ValueError(f"rotary_dim must be even and >= 0, got {rotary_dim}")
     if kind not in ROPE_KINDS:
-        raise ValueError(f"RoPE type {kind!r} is not implemented")
+        raise ValueError(f"unknown rope scaling kind {kind!r}; known kinds: {', '.join(ROPE_KINDS)}")
     half = rotary_dim // 2
     out = np.empty(half, dtype=np.float64)
     if kind == "yarn":
+        # Rotation counts: pair i makes turns[i] = original * theta^(-2i/d) / (2 pi) full turns
+        # over the original context, fewer the higher i.  The ramp's index range is 0 .. d-1.
+        fast = float(beta_fast) if beta_fast else 32.0
+        slow = float(beta_slow) if beta_slow else 1.0
         old = float(original_max_position_embeddings)
-
-        def pair_turning(rotations):
-            return rotary_dim * math.log(old / (rotations * 2.0 * math.pi)) / (2.0 * math.log(theta))
-
-        lo = pair_turning(float(beta_fast or 32.0))
-        hi = pair_turning(float(beta_slow or 1.0))
+        idx = np.arange(rotary_dim, dtype=np.float64)
+        turns = old * float(theta) ** (-2.0 * idx / rotary_dim) / (2.0 * math.pi)
         if truncate:
-            lo, hi = math.floor(lo), math.ceil(hi)
-        lo, hi = max(lo, 0), min(hi, rotary_dim - 1)
-        width = (hi - lo) or 0.001
+            # whole-index ends: the last index that still turns `fast` times, the first that
+            # turns no more than `slow` times
+            start = max(int(np.count_nonzero(turns >= fast)) - 1, 0)
+            stop = min(int(np.count_nonzero(turns > slow)), rotary_dim - 1)
+        else:
+            # fractional ends: the index at which the turn count equals fast (resp. slow)
+            turns0 = old / (2.0 * math.pi)
+            start = max(0.5 * rotary_dim * math.log(turns0 / fast) / math.log(theta), 0.0)
+            stop = min(0.5 * rotary_dim * math.log(turns0 / slow) / math.log(theta),
+                       rotary_dim - 1.0)
         for i in range(half):
             base = float(theta) ** (-2.0 * i / rotary_dim)
-            interp = min(max((i - lo) / width, 0.0), 1.0)   # 0: kept, 1: divided by factor
-            out[i] = base / factor * interp + base * (1.0 - interp)
+            if stop > start:    # share of the frequency that is divided by the factor
+                share = min(max((i - start) / (stop - start), 0.0), 1.0)
+            else:               # the two ends meet: a step after the first one
+                share = 1.0 if i > start else 0.0
+            out[i] = base * (1.0 - share) + base / factor * share
         return out
     if kind == "longrope":
         old = float(original_max_position_embeddings)

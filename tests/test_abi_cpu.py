@@ -37,7 +37,8 @@ def test_version():
 def _cfg(**kw):
     base = dict(dtype=1, head_dim=128, num_q_heads=32, num_kv_heads=8, rotary_dim=0, rot_style=0,
                 cos_table=None, sin_table=None, table_len=0, qk_norm=0, eps=1e-6, q_norm_w=None,
-                k_norm_w=None, scale=0.0, softcap=0.0, sinks=None, chunk_size=0, chunk_lookback=0)
+                k_norm_w=None, scale=0.0, softcap=0.0, sinks=None, chunk_size=0, chunk_lookback=0,
+                kernel=0, reserved=0)
     base.update(kw)
     c = g._AttnCfg()
     for k, v in base.items():
@@ -73,6 +74,9 @@ def _prefill(c, B=1, L=4, S=4, n_cached=0, window=0, q=FAKE, k=FAKE, v=FAKE, pos
     (dict(sinks=FAKE + 2), 7, "sinks"),
     (dict(chunk_size=-1), 2, "chunk_size"),
     (dict(chunk_size=64, chunk_lookback=-1), 2, "chunk_lookback"),
+    (dict(kernel=4), 7, "kernel"),
+    (dict(kernel=-1), 7, "kernel"),
+    (dict(reserved=1), 7, "reserved"),
 ])
 def test_prefill_rejects_bad_cfg(kw, status, msg):
     st = _prefill(_cfg(**kw))
@@ -111,10 +115,16 @@ def test_decode_validation_and_workspace():
     c = _cfg()
     need = lib.gqa_decode_workspace_bytes(ctypes.byref(c), 64, 32768)
     # split partials, B * Hkv * ceil(Smax/1024) * G * (D + 2) floats, each part 256-aligned,
-    # then the prepared queries, B * Hq * D bf16
+    # then the prepared queries, B * Hq * D bf16 (256-aligned), then one int32 per split launch
+    # (the split size it chose, for the combine kernel)
     items = 64 * 8 * 32 * 4
     align = lambda x: (x + 255) // 256 * 256
-    assert need == align(items * 128 * 4) + align(items * 2 * 4) + 64 * 32 * 128 * 2
+    assert need == align(items * 128 * 4) + align(items * 2 * 4) + align(64 * 32 * 128 * 2) + 4
+    # more than 2048 sequences take several split launches: one flag each
+    need3 = lib.gqa_decode_workspace_bytes(ctypes.byref(c), 4100, 64)
+    items3 = 4100 * 8 * 1 * 4
+    assert need3 == (align(items3 * 128 * 4) + align(items3 * 2 * 4) + align(4100 * 32 * 128 * 2)
+                     + 3 * 4)
     st = lib.gqa_attn_decode(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 64, 32768, 0, FAKE, None,
                              0, None)
     assert st == 5 and "workspace" in g.last_error()
@@ -144,7 +154,7 @@ def test_rope_param_validation():
     p = g.RopeSpec(64).c_struct()
     p.kind = 9
     assert lib.gqa_rope_tables(ctypes.byref(p), 16, FAKE, FAKE, None) == 4
-    assert "not implemented" in g.last_error()
+    assert "unknown rope kind" in g.last_error()
     p = g.RopeSpec(64).c_struct()
     assert lib.gqa_rope_tables(ctypes.byref(p), 0, FAKE, FAKE, None) == 2
     with pytest.raises(g.GQAError):
@@ -225,10 +235,38 @@ def test_host_attention_factor_and_softmax_scale_match_oracle(kind, factor, extr
         g.rope_softmax_scale(spec, 0)
 
 
-def test_policy_switch_validates():
+def test_kernel_choice_is_per_call():
+    # the library exports no selection state: the choice travels in each call's cfg
+    assert not any("policy" in name for name in g.EXPORTS)
     with pytest.raises(g.GQAError):
-        g.set_kernel_policy(7)
-    g.set_kernel_policy(0)
+        g.AttnConfig("bf16", 128, 32, 8, kernel="fastest").c_struct()
+    for name, val in g.KERNELS.items():
+        assert g.AttnConfig("bf16", 128, 32, 8, kernel=name).c_struct().kernel == val
+    # a generic-kernel call needs no decode workspace; the forced split sizes use the MFMA one
+    c = _cfg()
+    need = lib.gqa_decode_workspace_bytes(ctypes.byref(c), 4, 4096)
+    assert need > 0
+    assert lib.gqa_decode_workspace_bytes(ctypes.byref(_cfg(kernel=1)), 4, 4096) == 0
+    assert lib.gqa_decode_workspace_bytes(ctypes.byref(_cfg(kernel=2)), 4, 4096) == need
+    assert lib.gqa_decode_workspace_bytes(ctypes.byref(_cfg(kernel=3)), 4, 4096) == need
+    # prefill: the generic kernel needs no key-preparation workspace
+    cr = dict(rotary_dim=128, cos_table=FAKE, sin_table=FAKE, table_len=8)
+    assert lib.gqa_prefill_workspace_bytes(ctypes.byref(_cfg(**cr)), 2, 300, 100) > 0
+    assert lib.gqa_prefill_workspace_bytes(ctypes.byref(_cfg(kernel=1, **cr)), 2, 300, 100) == 0
+
+
+def test_second_hip_runtime_is_detected():
+    # two different libamdhip64 files mapped into one process is the state in which torch's
+    # streams are invalid for the library; the loader refuses it
+    one = ("7f00-7f10 r-xp 00000000 08:01 11 /opt/x/torch/lib/libamdhip64.so\n"
+           "7f10-7f20 r--p 00010000 08:01 11 /opt/x/torch/lib/libamdhip64.so\n"
+           "7f30-7f40 r-xp 00000000 08:01 12 /usr/lib/libc.so.6\n")
+    two = one + "7f50-7f60 r-xp 00000000 08:01 13 /opt/rocm/lib/libamdhip64.so.7.2.0\n"
+    assert len(g.hip_runtimes_mapped(one)) == 1
+    assert len(g.hip_runtimes_mapped(two)) == 2
+    assert len(g.hip_runtimes_mapped("")) == 0
+    # this process (torch imported first, library loaded) holds at most one
+    assert len(g.hip_runtimes_mapped()) <= 1
 
 
 def test_decode_byte_model_matches_page(golden):

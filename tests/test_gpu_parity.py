@@ -44,26 +44,36 @@ def spec(wl):
                       wl.high_freq_factor, wl.original_max_pos)
 
 
-PATH = {"path": "stream"}
+# The kernel path a test runs, carried into every config the helpers build (cfg.kernel is a
+# per-call field; the library holds no selection state).
+PATH = {"path": "stream", "kernel": "auto"}
+
+
+def cfg_of(*args, **kw):
+    """AttnConfig with the current test's kernel choice."""
+    kw.setdefault("kernel", PATH["kernel"])
+    return g.AttnConfig(*args, **kw)
 
 
 @pytest.fixture(params=["stream", "fused", "generic"])
 def policy(request):
     """Kernel path: stream (key-prep pass + streaming MFMA kernel), fused (MFMA kernel that
     preps keys on the fly, no workspace), generic (one wave per row, fp32 math)."""
-    g.set_kernel_policy(1 if request.param == "generic" else 0)
+    PATH["kernel"] = "generic" if request.param == "generic" else "auto"
     PATH["path"] = request.param
     yield request.param
-    g.set_kernel_policy(0)
+    PATH["kernel"] = "auto"
     PATH["path"] = "stream"
 
 
-@pytest.fixture(params=["mfma", "generic"])
+@pytest.fixture(params=["mfma", "mfma_long", "generic"])
 def dpolicy(request):
-    """Decode kernel path: the MFMA split-KV kernels, or generic (one wave per row, fp32 math)."""
-    g.set_kernel_policy(1 if request.param == "generic" else 0)
+    """Decode kernel path: the MFMA split-KV kernels (split size chosen from the batch, or 2048
+    keys forced), or generic (one wave per row, fp32 math)."""
+    PATH["kernel"] = {"mfma": "auto", "mfma_long": "decode_long", "generic": "generic"}[
+        request.param]
     yield request.param
-    g.set_kernel_policy(0)
+    PATH["kernel"] = "auto"
 
 
 def mask_kw(wl):
@@ -82,7 +92,7 @@ def gpu_prefill(wl, x, table_len=None, shared_pos=False):
     dt = tdt(wl)
     tl = table_len or int(max(x["positions"].max(), x["key_positions"].max())) + 1
     cos, sin = g.rope_tables(spec(wl), tl) if wl.rotary_dim else (None, None)
-    cfg = g.AttnConfig(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
+    cfg = cfg_of(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
                        wl.qk_norm, wl.eps,
                        dev(x["q_norm_w"], dt) if wl.qk_norm else None,
                        dev(x["k_norm_w"], dt) if wl.qk_norm else None, 0.0, wl.softcap,
@@ -285,7 +295,7 @@ def test_mask_probe_bitexact(window, n_cached, shift, chunk, lookback, policy):
 def gpu_decode(wl, q, kc, vc, lens, qw=None):
     dt = tdt(wl)
     cos, sin = g.rope_tables(spec(wl), kc.shape[2]) if wl.rotary_dim else (None, None)
-    cfg = g.AttnConfig(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
+    cfg = cfg_of(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
                        wl.qk_norm, wl.eps, dev(qw, dt) if wl.qk_norm else None,
                        dev(qw, dt) if wl.qk_norm else None, 0.0, wl.softcap, **cfg_extra(wl))
     out = g.attn_decode(cfg, dev(q, dt), dev(kc, dt), dev(vc, dt), dev(lens, torch.int32),
@@ -345,7 +355,7 @@ def test_decode_equals_last_prefill_row():
     dwl = wl.with_(qk_norm=True)
     dt = torch.bfloat16
     cos, sin = g.rope_tables(spec(wl), wl.S)
-    cfg = g.AttnConfig("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin, True,
+    cfg = cfg_of("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin, True,
                        wl.eps, dev(x["q_norm_w"]), dev(x["k_norm_w"]))
     dec = g.attn_decode(cfg, dev(x["q"][:, -1]), dev(kc), dev(vc), dev(lens, torch.int32), 0)
     torch.cuda.synchronize()
@@ -394,7 +404,7 @@ def test_full_size_decode_sampled(name):
     say("full size decode", wl.name)
     x = decode_device_inputs(wl)
     cos, sin = g.rope_tables(spec(wl), wl.S)
-    cfg = g.AttnConfig("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
+    cfg = cfg_of("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
                        **cfg_extra(wl))
     out = g.attn_decode(cfg, x["q"], x["k"], x["v"], x["lens"], wl.window)
     torch.cuda.synchronize()
@@ -411,6 +421,75 @@ def test_full_size_decode_sampled(name):
         check(got[b][None], ref[None], head_axis=1)
 
 
+def test_decode_several_split_launches():
+    # more than 2048 sequences: the split kernel runs in two launches sharing one combine.  With
+    # 2100 sequences of 1025-2100 keys the first launch (2048 sequences) holds enough work for the
+    # 2048-key splits and the second (52) does not, so the two launches choose differently and the
+    # combine must take each sequence's choice from its own launch.
+    wl = WORKLOADS["llama31_decode_bf16"].with_(B=2100, S=2100, Hq=8, Hkv=2, lens_lo=1025,
+                                                 lens_hi=2100, seed=61)
+    say("decode, two split launches", wl.B, wl.S)
+    x = decode_device_inputs(wl)
+    cos, sin = g.rope_tables(spec(wl), wl.S)
+    cfg = cfg_of("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin)
+    out = g.attn_decode(cfg, x["q"], x["k"], x["v"], x["lens"], 0)
+    torch.cuda.synchronize()
+    lens = x["lens"].cpu().numpy()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    inv = inv_freq(wl)
+    for b in sorted({0, 1, 1000, 2046, 2047, 2048, 2049, 2099, int(np.argmin(lens[2048:])) + 2048,
+                     int(np.argmax(lens[2048:])) + 2048, int(np.argmax(lens[:2048]))}):
+        n = int(lens[b])
+        ref = oracle.attn_decode_one(x["q"][b].float().cpu().numpy(),
+                                     x["k"][b, :, :n].float().cpu().numpy(),
+                                     x["v"][b, :, :n].float().cpu().numpy(), n, inv_freq=inv)
+        check(got[b][None], ref[None], head_axis=1)
+    # every split size gives the same result up to rounding
+    for k in ("decode_short", "decode_long"):
+        cfg_k = cfg_of("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin, kernel=k)
+        other = g.attn_decode(cfg_k, x["q"], x["k"], x["v"], x["lens"], 0)
+        torch.cuda.synchronize()
+        diff = np.abs(other.float().cpu().numpy() - got)
+        assert diff.max() <= 2e-2, (k, diff.max())
+
+
+@pytest.mark.parametrize("path", ["stream", "fused"])
+def test_full_size_window_edge_probe_bitexact(path):
+    # [Models] "Sliding windows": a query at position p sees keys p-4095 .. p at window 4096.  At
+    # the Mistral-style size one key more or less moves an output by ~1/4096, below the bf16
+    # tolerance, so the edges are probed exactly: q = 0 gives every allowed key weight exactly 1/n,
+    # and one-hot values over a key block make output column d nonzero iff key blk+d is allowed.
+    wl = WORKLOADS["mistral_swa_prefill_bf16"]
+    say("full-size window edge probe", path)
+    B, L, Hq, Hkv, D = wl.B, wl.L, wl.Hq, wl.Hkv, wl.D
+    from synth import device_normal
+    q = torch.zeros((B, L, Hq, D), dtype=torch.bfloat16, device="cuda")
+    k = device_normal((B, L, Hkv, D), 3 * 10 + 2, "bf16")
+    pos = torch.arange(L, dtype=torch.int32, device="cuda")
+    cos, sin = g.rope_tables(spec(wl), L)
+    cfg = cfg_of("bf16", D, Hq, Hkv, wl.rotary_dim, wl.style, cos, sin)
+    rows = [0, 1, 4094, 4095, 4096, 4097, 4160, 6000, 8191]
+    for blk in (0, 4032, 8064):
+        v = torch.zeros((B, L, Hkv, D), dtype=torch.bfloat16, device="cuda")
+        idx = torch.arange(D, device="cuda")
+        v[:, blk + idx, :, idx] = 1.0
+        out = g.attn_prefill(cfg, q, k, v, pos, pos, 0, wl.window,
+                             workspace=None if path == "fused" else "auto")
+        torch.cuda.synchronize()
+        got = out[:, rows].float().cpu().numpy()            # [B, rows, Hq, D]
+        for ri, i in enumerate(rows):
+            kp = blk + np.arange(D)
+            allowed = (kp <= i) & (i - kp <= wl.window - 1)
+            n = min(i, wl.window - 1) + 1                   # keys the row sees in all
+            for b in range(B):
+                nz = got[b, ri] != 0                        # [Hq, D]
+                assert (nz == allowed[None, :]).all(), (blk, i, b)
+                if allowed.any():
+                    vals = got[b, ri][:, allowed]
+                    np.testing.assert_allclose(vals, 1.0 / n, rtol=2 ** -8)
+
+
 @pytest.mark.parametrize("name", ["qknorm_half128", "interleaved64_cap_chunk", "half32_partial",
                                   "norope"])
 def test_prep_keys_then_cached_prefill(name):
@@ -422,7 +501,7 @@ def test_prep_keys_then_cached_prefill(name):
     dt = torch.bfloat16
     tl = int(x["key_positions"].max()) + 1
     cos, sin = g.rope_tables(spec(wl), tl) if wl.rotary_dim else (None, None)
-    cfg = g.AttnConfig("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin, wl.qk_norm,
+    cfg = cfg_of("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin, wl.qk_norm,
                        wl.eps, dev(x["q_norm_w"]) if wl.qk_norm else None,
                        dev(x["k_norm_w"]) if wl.qk_norm else None, 0.0, wl.softcap)
     k = dev(x["k"])
@@ -534,7 +613,7 @@ def test_prefill_rope_schedules(name, wkw, policy):
     spec_ = sched_spec(name, wl.rotary_dim, wl.S)
     cos, sin = g.rope_tables(spec_, wl.S)
     scale = g.rope_softmax_scale(spec_, wl.D)
-    cfg = g.AttnConfig("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin, wl.qk_norm,
+    cfg = cfg_of("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin, wl.qk_norm,
                        wl.eps, dev(x["q_norm_w"]) if wl.qk_norm else None,
                        dev(x["k_norm_w"]) if wl.qk_norm else None, scale, wl.softcap)
     out = g.attn_prefill(cfg, dev(x["q"]), dev(x["k"]), dev(x["v"]),
@@ -572,7 +651,7 @@ def test_decode_rope_schedules(name, dpolicy):
     spec_ = sched_spec(name, wl.rotary_dim, wl.S)
     cos, sin = g.rope_tables(spec_, wl.S)
     scale = g.rope_softmax_scale(spec_, wl.D)
-    cfg = g.AttnConfig("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin, True,
+    cfg = cfg_of("bf16", wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin, True,
                        wl.eps, dev(qw), dev(qw), scale, wl.softcap)
     out = g.attn_decode(cfg, dev(q), dev(kc), dev(vc), dev(lens, torch.int32), wl.window)
     torch.cuda.synchronize()
@@ -611,7 +690,7 @@ def test_paged_append_matches_oracle(bs, L, R, style, norm):
     wl = BASE.with_(Hq=4, Hkv=Hkv, rotary_dim=R, style=style, theta=1e4, qk_norm=norm)
     tl = int(kpos.max()) + 1
     cos, sin = g.rope_tables(spec(wl), tl) if R else (None, None)
-    cfg = g.AttnConfig("bf16", D, 4, Hkv, R, style, cos, sin, norm, wl.eps,
+    cfg = cfg_of("bf16", D, 4, Hkv, R, style, cos, sin, norm, wl.eps,
                        dev(kw) if norm else None, dev(kw) if norm else None)
     kv = _paged_kv(kp, vp, table)
     g.paged_append(cfg, kv, dev(k_new), dev(v_new), dev(kpos, torch.int32),
@@ -641,11 +720,12 @@ PAGED_DEC = {
 }
 
 
+@pytest.mark.parametrize("split", ["auto", "decode_long"])
 @pytest.mark.parametrize("name", list(PAGED_DEC))
-def test_paged_decode_matches_oracle(name):
+def test_paged_decode_matches_oracle(name, split):
     bs, kw = PAGED_DEC[name]
     wl = DEC.with_(**kw)
-    say("paged decode", name)
+    say("paged decode", name, split)
     lens, q, qw = decode_lens_q(wl, seed=29)
     lens[0], lens[1] = 1, wl.S
     max_blocks = (wl.S + bs - 1) // bs
@@ -665,9 +745,9 @@ def test_paged_decode_matches_oracle(name):
                 if (i + 1) * bs <= first or i * bs >= n:
                     gpu_table[b, i] = nan_blk
     cos, sin = g.rope_tables(spec(wl), wl.S)
-    cfg = g.AttnConfig(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
+    cfg = cfg_of(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
                        wl.qk_norm, wl.eps, dev(qw) if wl.qk_norm else None,
-                       dev(qw) if wl.qk_norm else None, 0.0, wl.softcap, **cfg_extra(wl))
+                       dev(qw) if wl.qk_norm else None, 0.0, wl.softcap, **cfg_extra(wl), kernel=split)
     out = g.attn_decode_paged(cfg, dev(q), _paged_kv(kp, vp, gpu_table), dev(lens, torch.int32),
                               wl.window)
     torch.cuda.synchronize()
