@@ -1,17 +1,23 @@
 """Benchmark of the rotary grouped-query attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --only NAME [--steps K] [--warmup W]      (one workload, for the profiler)
 
 One step = one pass of the whole hot path over one batch of synthetic input, inputs resident in
 HBM: the rotary tables (gqa_rope_tables), the key preparation that norms and rotates the new keys
 into the K cache (gqa_prep_keys), and the attention over the cache (gqa_attn_prefill with every
-key used as stored), three launches timed separately with HIP events.  The default workload is the Qwen3-style prefill (B=4, L=S=2048, Hq=32, Hkv=8, D=128,
-per-head q/k RMSNorm, full causal).  The split-KV decode workload (64 sequences, cache lengths
-U[1024, 32768], llama3 rope) is timed in the same run and reported under "decode".
+key used as stored), replayed as one HIP graph.  The headline workload is the largest prefill
+that fits one GPU, the Mistral-style sliding-window prefill (B=2, L=S=8192, Hq=32, Hkv=8, D=128,
+window 4096).  Every other workload of the scope is timed in the same run and reported under
+"configs" with its own roofline and CPU baseline: the tiny fp32 causal prefill (latency only),
+the Qwen3-style prefill, the chunked prefill in both layer kinds (window 4096, full) and the
+Llama-3.1-style split-KV decode; the paged-pool decode and the latent-attention decode follow
+under "extras".
 
 Prints ONE JSON line on stdout (progress goes to stderr).  FLOPs count only allowed
 (query, key) pairs, 4 * D per pair per head; decode bytes are the K and V rows each sequence
-actually reads plus q, out and lens.
+actually reads plus q, out and lens.  Kernel times come from HIP events recorded on the stream
+the kernels are launched on, around K back-to-back launches of the timed call.
 """
 from __future__ import annotations
 
@@ -26,6 +32,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3           # MI355X fp32 vector
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
 METRIC = "prefill attn TFLOP/s (% MFMA peak); decode KV GB/s (% HBM peak)"
 
@@ -82,19 +89,17 @@ def decode_bytes(wl, lens):
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` on `workload` from the committed counter runs
     (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE scaled by a known-size copy), or None when
-    the counters were taken on another workload or the kernel's source has changed since."""
+    no counters were taken on that workload or the kernel's source has changed since."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
-            rec = json.load(f)["kernels"][kernel]
-        if rec.get("workload") != workload:
-            return None
+            rec = json.load(f)["kernels"][kernel][workload]
         with open(os.path.join(ROOT, rec["source"]), "rb") as f:
             if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
                 return None
         return int(rec["hbm_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+    except (OSError, KeyError, ValueError, TypeError):
         return None
 
 
@@ -141,34 +146,57 @@ def _prefill_setup(wl, torch, g):
                 out=out, table_len=table_len, kcache=kcache)
 
 
+def _time_calls(fn, n, torch):
+    """Average ms of n back-to-back calls of fn, from HIP events on the current stream (the
+    stream every library call here is launched on)."""
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(n):
+        fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / n
+
+
 def run_prefill(wl, steps, warmup, torch, g, graph=True):
+    """The prefill step (tables, key preparation, attention) of workload wl: returns the inputs
+    and outputs, the step time (ms, as replayed) and the time of each call alone (ms, n calls of
+    that call back to back).  fp32 problems have no key-preparation pass (the attention call
+    prepares the keys itself)."""
     x = _prefill_setup(wl, torch, g)
     spec = _rope_spec(g, wl)
     stream = torch.cuda.current_stream()
-    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    bf16 = wl.dtype == "bf16"
 
-    def launches(ev=None):
-        if ev:
-            ev[0].record(stream)
+    def tables():
         g.rope_tables(spec, x["table_len"], x["cos"], x["sin"])
-        if ev:
-            ev[1].record(stream)
+
+    def prep():
         g.prep_keys(x["cfg"], x["k"], x["kpos"], wl.n_cached, k_out=x["kcache"])
-        if ev:
-            ev[2].record(stream)
-        g.attn_prefill(x["cfg"], x["q"], x["kcache"], x["v"], x["pos"], x["kpos"], wl.S,
-                       wl.window, x["out"], workspace=None)
-        if ev:
-            ev[3].record(stream)
+
+    def attention():
+        if bf16:
+            g.attn_prefill(x["cfg"], x["q"], x["kcache"], x["v"], x["pos"], x["kpos"], wl.S,
+                           wl.window, x["out"], workspace=None)
+        else:
+            g.attn_prefill(x["cfg"], x["q"], x["k"], x["v"], x["pos"], x["kpos"], wl.n_cached,
+                           wl.window, x["out"], workspace=None)
+
+    def launches():
+        tables()
+        if bf16:
+            prep()
+        attention()
 
     for _ in range(warmup):
         launches()
     torch.cuda.synchronize()
     step_fn = launches
     if graph:
-        # the step's three launches captured once as a HIP graph and replayed (no memset or
-        # allocation is recorded: every buffer exists before the capture); the replayed output
-        # must match the eager one bit for bit
+        # the step's launches captured once as a HIP graph and replayed (no memset or allocation
+        # is recorded: every buffer exists before the capture); the replayed output must match
+        # the eager one bit for bit
         eager = x["out"].clone()
         hg = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
@@ -187,23 +215,62 @@ def run_prefill(wl, steps, warmup, torch, g, graph=True):
                 raise RuntimeError("graph replay differs from the eager step")
         x["graph"] = hg
         step_fn = hg.replay
-    # the step: only the two bracketing events (an event between kernels adds a few us of
-    # queue work of its own, so the per-launch times come from a separate pass below)
-    t0, t1 = E(), E()
-    t0.record(stream)
-    for i in range(steps):
-        step_fn()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    step_ms = t0.elapsed_time(t1) / steps
-    evs = [[E() for _ in range(4)] for _ in range(steps)]
-    for i in range(steps):
-        launches(evs[i])
-    torch.cuda.synchronize()
-    parts = {name: sorted(e[k].elapsed_time(e[k + 1]) for e in evs)
-             for k, name in enumerate(("rope_tables", "prep_keys", "attention"))}
-    stats = {name: (sum(v) / len(v), v[len(v) // 2]) for name, v in parts.items()}
-    return x, step_ms, stats
+    step_ms = _time_calls(step_fn, steps, torch)
+    # each call alone, back to back (the attention call reads the cache the step left)
+    parts = {"rope_tables": _time_calls(tables, steps, torch)}
+    if bf16:
+        parts["prep_keys"] = _time_calls(prep, steps, torch)
+    parts["attention"] = _time_calls(attention, steps, torch)
+    return x, step_ms, parts
+
+
+def prefill_record(wl, steps, warmup, torch, g, graph, cpu, budget_s):
+    """Bench record of one prefill workload: step throughput, the attention kernel's roofline and,
+    unless cpu is False, the oracle's rate on a bounded sample with parity on the timed outputs."""
+    x, step_ms, parts = run_prefill(wl, steps, warmup, torch, g, graph=graph)
+    flops = prefill_flops(wl)
+    kern_ms = parts["attention"]
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    value = flops / (step_ms * 1e-3) / 1e12
+    bf16 = wl.dtype == "bf16"
+    log(f"[bench] {wl.name}: step {step_ms:.4f} ms ("
+        + ", ".join(f"{k} {v:.4f}" for k, v in parts.items())
+        + f") -> step {value:.1f}, attention {achieved:.1f} TFLOP/s")
+    if bf16:
+        roof = {"bound": "mfma", "kernel": "prefill_stream_kernel", "achieved": round(achieved, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic("prefill_stream_kernel", wl.name),
+                "kernel_ms_mean": round(kern_ms, 4), "algorithmic_flop": flops}
+    else:
+        # 16 query rows: far too small to load any unit of the chip; reported against the fp32
+        # vector peak for completeness, no roofline claim
+        roof = {"bound": "alu", "kernel": "attn_generic_kernel", "achieved": round(achieved, 6),
+                "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP32_PEAK_TFLOPS, 8), "traffic": None,
+                "kernel_ms_mean": round(kern_ms, 5), "algorithmic_flop": flops,
+                "note": "latency-bound (16 query rows); no roofline claim"}
+    rec = {"workload": wl.name, "value": round(value, 4 if bf16 else 8), "unit": "TFLOP/s",
+           "ms_per_step": round(step_ms, 5), "dtype": wl.dtype,
+           "step_parts_ms": {k: round(v, 5) for k, v in parts.items()},
+           "config": _config(wl), "roofline": roof}
+    if not bf16:
+        rec["latency_us"] = round(step_ms * 1e3, 2)
+    if cpu:
+        rec["cpu_baseline"] = cpu_baseline_prefill(wl, x, torch, budget_s)
+        log(f"[bench] {wl.name}: cpu baseline {rec['cpu_baseline']['value']:.4g} TFLOP/s, parity "
+            f"{rec['cpu_baseline']['parity_ok']}")
+    del x
+    torch.cuda.empty_cache()
+    return rec
+
+
+def _config(wl):
+    return {"workload": wl.name, "B": wl.B, "L": wl.L, "S": wl.S, "Hq": wl.Hq, "Hkv": wl.Hkv,
+            "head_dim": wl.D, "rotary_dim": wl.rotary_dim, "rot_style": wl.style,
+            "rope": wl.rope_kind, "theta": wl.theta, "qk_norm": wl.qk_norm, "window": wl.window,
+            "softcap": wl.softcap, "n_cached": wl.n_cached, "chunk": wl.chunk,
+            "chunk_lookback": wl.chunk_lookback, "sinks": wl.sinks}
 
 
 def run_decode(wl, steps, warmup, torch, g):
@@ -216,20 +283,38 @@ def run_decode(wl, steps, warmup, torch, g):
                        **_mask_cfg(wl, torch))
     ws = torch.empty(g.decode_workspace_bytes(cfg, wl.B, wl.S), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(x["q"])
-    stream = torch.cuda.current_stream()
+
+    def call():
+        g.attn_decode(cfg, x["q"], x["k"], x["v"], x["lens"], wl.window, out, ws)
+
     for _ in range(warmup):
-        g.attn_decode(cfg, x["q"], x["k"], x["v"], x["lens"], wl.window, out, ws)
+        call()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for i in range(steps):
-        evs[i][0].record(stream)
-        g.attn_decode(cfg, x["q"], x["k"], x["v"], x["lens"], wl.window, out, ws)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    ms = _time_calls(call, steps, torch)
     x.update(cfg=cfg, out=out, cos=cos, sin=sin)
-    return x, sum(ms) / len(ms), ms[len(ms) // 2]
+    return x, ms
+
+
+def decode_record(wl, steps, warmup, torch, g, cpu, budget_s):
+    dx, dms = run_decode(wl, steps, warmup, torch, g)
+    lens = dx["lens"].cpu().tolist()
+    nbytes = decode_bytes(wl, lens)
+    gbs = nbytes / (dms * 1e-3) / 1e9
+    log(f"[bench] {wl.name}: {dms:.4f} ms per call -> {gbs:.0f} GB/s")
+    rec = {"workload": wl.name, "value": round(gbs, 1), "unit": "GB/s", "ms_per_call": round(dms, 4),
+           "algorithmic_bytes": nbytes, "dtype": wl.dtype, "config": _config(wl),
+           "roofline": {"bound": "hbm",
+                        "kernel": "decode_prep_q_kernel + decode_split_kernel + "
+                                  "decode_combine_kernel (one gqa_attn_decode call)",
+                        "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic("decode_split_kernel", wl.name),
+                        "kernel_ms_mean": round(dms, 4)}}
+    if cpu:
+        rec["cpu_baseline"] = cpu_baseline_decode(wl, dx, torch, budget_s)
+        log(f"[bench] {wl.name}: cpu baseline {rec['cpu_baseline']['value']:.4g} GB/s, parity "
+            f"{rec['cpu_baseline']['parity_ok']}")
+    return rec, dx, nbytes
 
 
 def run_decode_paged(wl, dx, block_size, steps, warmup, torch, g):
@@ -252,21 +337,16 @@ def run_decode_paged(wl, dx, block_size, steps, warmup, torch, g):
     cfg = dx["cfg"]
     ws = torch.empty(g.paged_decode_workspace_bytes(cfg, kv, B), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(dx["q"])
-    stream = torch.cuda.current_stream()
+    def call():
+        g.attn_decode_paged(cfg, dx["q"], kv, dx["lens"], wl.window, out, ws)
+
     for _ in range(warmup):
-        g.attn_decode_paged(cfg, dx["q"], kv, dx["lens"], wl.window, out, ws)
+        call()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for i in range(steps):
-        evs[i][0].record(stream)
-        g.attn_decode_paged(cfg, dx["q"], kv, dx["lens"], wl.window, out, ws)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    ms = _time_calls(call, steps, torch)
     same = bool(torch.equal(out, dx["out"]))
     del kv, ws
-    return sum(ms) / len(ms), ms[len(ms) // 2], same
+    return ms, same
 
 
 MLA_ROW_BYTES = 576 * 2
@@ -293,23 +373,17 @@ def run_mla(wl, steps, warmup, torch, g):
     ws = torch.empty(g.mla_decode_workspace_bytes(wl.B, wl.Hq, wl.S), dtype=torch.uint8,
                      device="cuda")
     out = torch.empty((wl.B, wl.Hq, 512), dtype=torch.bfloat16, device="cuda")
-    stream = torch.cuda.current_stream()
+    def call():
+        g.mla_decode(q, cache, dl, scale, out, ws)
+
     for _ in range(warmup):
-        g.mla_decode(q, cache, dl, scale, out, ws)
+        call()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for i in range(steps):
-        evs[i][0].record(stream)
-        g.mla_decode(q, cache, dl, scale, out, ws)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    ms = _time_calls(call, steps, torch)
     keys = int(lens.sum())
     nbytes = keys * MLA_ROW_BYTES + wl.B * wl.Hq * (576 + 512) * 2 + 4 * wl.B
     flops = keys * wl.Hq * MLA_FLOP_PER_KEY_HEAD
-    return dict(lens=lens, q=q, cache=cache, out=out, scale=scale), sum(ms) / len(ms), \
-        ms[len(ms) // 2], nbytes, flops
+    return dict(lens=lens, q=q, cache=cache, out=out, scale=scale), ms, nbytes, flops
 
 
 def cpu_baseline_prefill(wl, x, torch, budget_s=15.0):
@@ -339,14 +413,15 @@ def cpu_baseline_prefill(wl, x, torch, budget_s=15.0):
         got = x["out"][b:b + 1].float().cpu().numpy()
         err = np.abs(got - ref)
         maxerr = max(maxerr, float(err.max()))
-        ok &= bool(np.all(err <= 2e-2 + 2e-2 * np.abs(ref)))
+        tol = 1e-4 if wl.dtype == "f32" else 2e-2 + 2e-2 * np.abs(ref)
+        ok &= bool(np.all(err <= tol))
         nseq += 1
         if t_total >= budget_s:
             break
     flops = 4 * nseq * wl.Hq * wl.D * allowed_pairs(wl.L, wl.S, wl.window, wl.n_cached,
                                                     wl.chunk, wl.chunk_lookback)
     return dict(value=flops / t_total / 1e12, unit="TFLOP/s", cores=_blas_threads(),
-                kind="oracle",
+                host_cpu_count=os.cpu_count(), kind="oracle",
                 sample=f"{nseq} of {wl.B} sequences of {wl.name}, all rows and heads "
                        f"({flops / 1e9:.1f} GFLOP in {t_total:.1f} s)",
                 parity_ok=ok, max_abs_err=maxerr)
@@ -381,7 +456,8 @@ def cpu_baseline_decode(wl, x, torch, budget_s=15.0):
         nseq += 1
         if t_total >= budget_s:
             break
-    return dict(value=nbytes / t_total / 1e9, unit="GB/s", cores=_blas_threads(), kind="oracle",
+    return dict(value=nbytes / t_total / 1e9, unit="GB/s", cores=_blas_threads(),
+                host_cpu_count=os.cpu_count(), kind="oracle",
                 sample=f"{nseq} of {wl.B} sequences of {wl.name} ({nbytes / 1e6:.0f} MB of K/V "
                        f"in {t_total:.1f} s)", parity_ok=ok, max_abs_err=maxerr)
 
@@ -396,22 +472,51 @@ def _blas_threads():
         return os.cpu_count() or 1
 
 
+CONFIGS = ("tiny_causal_f32", "qwen3_prefill_bf16", "chunked_prefill_bf16_w4096",
+           "chunked_prefill_bf16_full")
+DECODE_CONFIG = "llama31_decode_bf16"
+
+
+def run_only(name, steps, warmup, torch, g):
+    """One workload's timed loop, eager launches, for a profiler run (no CPU baseline)."""
+    from synth import WORKLOADS
+    wl = WORKLOADS[name]
+    if wl.name == "deepseek_mla_decode_bf16":
+        _, ms, nbytes, _ = run_mla(wl, steps, warmup, torch, g)
+        rec = {"workload": name, "ms_per_call": ms, "GB/s": nbytes / (ms * 1e-3) / 1e9}
+    elif wl.kind == "decode":
+        dx, ms = run_decode(wl, steps, warmup, torch, g)
+        nbytes = decode_bytes(wl, dx["lens"].cpu().tolist())
+        rec = {"workload": name, "ms_per_call": ms, "GB/s": nbytes / (ms * 1e-3) / 1e9}
+    else:
+        _, step_ms, parts = run_prefill(wl, steps, warmup, torch, g, graph=False)
+        rec = {"workload": name, "ms_per_step": step_ms, "parts_ms": parts,
+               "attention_TFLOP/s": prefill_flops(wl) / (parts["attention"] * 1e-3) / 1e12}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_prefill_bf16")
-    ap.add_argument("--decode-workload", default="llama31_decode_bf16")
-    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--workload", default="mistral_swa_prefill_bf16",
+                    help="headline prefill workload")
+    ap.add_argument("--configs", default=",".join(CONFIGS + (DECODE_CONFIG,)),
+                    help="comma-separated workloads timed beside the headline ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle time on the headline's sample (sub-records get half)")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the step's kernels one by one instead of replaying a HIP graph")
     ap.add_argument("--mla-workload", default="deepseek_mla_decode_bf16",
-                    help="latent-attention decode workload timed after the decode ('' to skip)")
+                    help="latent-attention decode workload timed as an extra ('' to skip)")
     ap.add_argument("--paged-block", type=int, default=16, metavar="N",
                     help="also time the decode workload through a paged pool of N-slot blocks "
                          "(0: skip)")
+    ap.add_argument("--only", default="", metavar="NAME",
+                    help="run only this workload's timed loop (eager) and print its times")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (three times), the "
                          "known-size reference for scaling HBM byte counters")
@@ -439,84 +544,61 @@ def main(argv=None):
     from synth import WORKLOADS
 
     g.library()
+    if args.only:
+        return run_only(args.only, args.steps, args.warmup, torch, g)
+    cpu = not args.no_cpu_baseline
+    graph = not args.no_graph
     wl = WORKLOADS[args.workload]
-    log(f"[bench] prefill workload {wl.name}: warmup {args.warmup}, steps {args.steps}")
-    x, step_ms, stats = run_prefill(wl, args.steps, args.warmup, torch, g, graph=not args.no_graph)
-    kern_ms, kern_med = stats["attention"]
-    flops = prefill_flops(wl)
-    value = flops / (step_ms * 1e-3) / 1e12
-    achieved = flops / (kern_ms * 1e-3) / 1e12
-    log(f"[bench] step {step_ms:.3f} ms (tables {stats['rope_tables'][0]:.4f}, prep_keys "
-        f"{stats['prep_keys'][0]:.4f}, attention {kern_ms:.4f}) -> attention {achieved:.1f} TFLOP/s")
+    log(f"[bench] headline prefill workload {wl.name}: warmup {args.warmup}, steps {args.steps}")
+    head = prefill_record(wl, args.steps, args.warmup, torch, g, graph, cpu, args.cpu_budget)
     line = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "metric": METRIC, "value": head["value"], "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic (seeded N(0,1) draws, device-generated)",
-        "config": {"workload": wl.name, "B": wl.B, "L": wl.L, "S": wl.S, "Hq": wl.Hq,
-                   "Hkv": wl.Hkv, "head_dim": wl.D, "rotary_dim": wl.rotary_dim,
-                   "rope": wl.rope_kind, "theta": wl.theta, "qk_norm": wl.qk_norm,
-                   "window": wl.window, "softcap": wl.softcap, "n_cached": wl.n_cached,
-                   "chunk": wl.chunk, "chunk_lookback": wl.chunk_lookback, "sinks": wl.sinks,
-                   "parallelism": "none (1 GPU)",
-                   "launch": "eager" if args.no_graph else "HIP graph of the step's 3 kernels"},
-        "roofline": {"bound": "mfma", "kernel": "prefill_stream_kernel",
-                     "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("prefill_stream_kernel", wl.name),
-                     "kernel_ms_mean": round(kern_ms, 4),
-                     "kernel_ms_median": round(kern_med, 4), "algorithmic_flop": flops},
-        "step_parts_ms": {k: round(v[0], 4) for k, v in stats.items()},
+        "config": {**head["config"], "parallelism": "none (1 GPU)",
+                   "launch": "eager" if args.no_graph else "HIP graph of the step's kernels"},
+        "roofline": head["roofline"],
+        "step_parts_ms": head["step_parts_ms"],
     }
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle) on a bounded sample ...")
-        line["cpu_baseline"] = cpu_baseline_prefill(wl, x, torch)
-        log(f"[bench] cpu baseline {line['cpu_baseline']['value']:.4f} TFLOP/s")
-    del x
-    torch.cuda.empty_cache()
-    if not args.no_decode:
-        dwl = WORKLOADS[args.decode_workload]
-        log(f"[bench] decode workload {dwl.name}")
-        dx, dms, dmed = run_decode(dwl, args.steps, args.warmup, torch, g)
-        lens = dx["lens"].cpu().tolist()
-        nbytes = decode_bytes(dwl, lens)
-        gbs = nbytes / (dms * 1e-3) / 1e9
-        log(f"[bench] decode {dms:.3f} ms -> {gbs:.0f} GB/s")
-        dec = {"workload": dwl.name, "value": round(gbs, 1), "unit": "GB/s",
-               "ms_per_call": round(dms, 4), "algorithmic_bytes": nbytes,
-               "roofline": {"bound": "hbm",
-                            "kernel": "decode_prep_q_kernel + decode_split_kernel + "
-                                      "decode_combine_kernel (one gqa_attn_decode call)",
-                            "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": round(gbs / HBM_PEAK_GBS, 4),
-                            "traffic": measured_traffic("decode_split_kernel", dwl.name),
-                            "kernel_ms_mean": round(dms, 4), "kernel_ms_median": round(dmed, 4)}}
-        if not args.no_cpu_baseline:
-            dec["cpu_baseline"] = cpu_baseline_decode(dwl, dx, torch)
-        if args.paged_block:
-            pms, pmed, same = run_decode_paged(dwl, dx, args.paged_block, args.steps, args.warmup,
-                                               torch, g)
-            pgbs = nbytes / (pms * 1e-3) / 1e9
-            log(f"[bench] paged decode (blocks of {args.paged_block}) {pms:.3f} ms -> "
-                f"{pgbs:.0f} GB/s, bit-identical to the contiguous cache: {same}")
-            dec["paged"] = {"block_size": args.paged_block, "value": round(pgbs, 1), "unit": "GB/s",
-                            "ms_per_call": round(pms, 4), "ms_median": round(pmed, 4),
-                            "frac": round(pgbs / HBM_PEAK_GBS, 4),
-                            "identical_to_contiguous": same}
-        line["decode"] = dec
-        del dx
-        torch.cuda.empty_cache()
+    if cpu:
+        line["cpu_baseline"] = head["cpu_baseline"]
+    configs = {}
+    dx = None
+    for name in filter(None, args.configs.split(",")):
+        cwl = WORKLOADS[name]
+        log(f"[bench] config {name}")
+        if cwl.kind == "decode":
+            rec, dx, nbytes = decode_record(cwl, args.steps, args.warmup, torch, g, cpu,
+                                            args.cpu_budget / 2)
+            if args.paged_block:
+                pms, same = run_decode_paged(cwl, dx, args.paged_block, args.steps, args.warmup,
+                                             torch, g)
+                pgbs = nbytes / (pms * 1e-3) / 1e9
+                log(f"[bench] paged decode (blocks of {args.paged_block}) {pms:.3f} ms -> "
+                    f"{pgbs:.0f} GB/s, bit-identical to the contiguous cache: {same}")
+                rec["paged"] = {"block_size": args.paged_block, "value": round(pgbs, 1),
+                                "unit": "GB/s", "ms_per_call": round(pms, 4),
+                                "frac": round(pgbs / HBM_PEAK_GBS, 4),
+                                "identical_to_contiguous": same}
+            del dx
+            torch.cuda.empty_cache()
+        else:
+            rec = prefill_record(cwl, args.steps, args.warmup, torch, g, graph, cpu,
+                                 args.cpu_budget / 2)
+        configs[name] = rec
+    line["configs"] = configs
+    extras = {}
     if args.mla_workload:
         mwl = WORKLOADS[args.mla_workload]
         log(f"[bench] latent-attention decode workload {mwl.name}")
-        mx, mms, mmed, mbytes, mflops = run_mla(mwl, args.steps, args.warmup, torch, g)
+        mx, mms, mbytes, mflops = run_mla(mwl, args.steps, args.warmup, torch, g)
         mgbs = mbytes / (mms * 1e-3) / 1e9
         mtf = mflops / (mms * 1e-3) / 1e12
         log(f"[bench] latent-attention decode {mms:.3f} ms -> {mgbs:.0f} GB/s, {mtf:.1f} TFLOP/s")
-        line["mla_decode"] = {
+        extras["mla_decode"] = {
             "workload": mwl.name, "value": round(mgbs, 1), "unit": "GB/s",
-            "ms_per_call": round(mms, 4), "ms_median": round(mmed, 4),
-            "algorithmic_bytes": mbytes, "algorithmic_flop": mflops,
+            "ms_per_call": round(mms, 4), "algorithmic_bytes": mbytes, "algorithmic_flop": mflops,
             "roofline": {"bound": "hbm",
                          "kernel": "mla_split_kernel + mla_combine_kernel (one gqa_mla_decode call)",
                          "achieved": round(mgbs, 1), "peak": HBM_PEAK_GBS,
@@ -524,6 +606,8 @@ def main(argv=None):
                          "traffic": measured_traffic("mla_split_kernel", mwl.name),
                          "mfma_tflops": round(mtf, 1),
                          "mfma_frac": round(mtf / MFMA_BF16_PEAK_TFLOPS, 4)}}
+        del mx
+    line["extras"] = extras
     print(json.dumps(line), flush=True)
     return 0
 

@@ -282,16 +282,19 @@ def test_decode_byte_model_matches_page(golden):
 
 
 def test_counter_traffic_only_for_its_workload():
-    # the HBM byte counters were taken on one workload per kernel: a bench line for another
-    # workload reports no traffic rather than those bytes
+    # the HBM byte counters are kept per (kernel, workload): a bench line for a workload without
+    # counters reports no traffic rather than another workload's bytes
     import bench
     import json
     with open(os.path.join(os.path.dirname(bench.__file__), "profiles", "traffic.json")) as f:
         kernels = json.load(f)["kernels"]
-    for kernel, rec in kernels.items():
-        assert bench.measured_traffic(kernel, rec["workload"] + "_other") is None
-        got = bench.measured_traffic(kernel, rec["workload"])
-        assert got is None or got == int(rec["hbm_bytes_per_launch"])
+    assert kernels
+    for kernel, per_workload in kernels.items():
+        for workload, rec in per_workload.items():
+            assert bench.measured_traffic(kernel, workload + "_other") is None
+            got = bench.measured_traffic(kernel, workload)
+            # None once the kernel's source has changed since the counters were taken
+            assert got is None or got == int(rec["hbm_bytes_per_launch"])
 
 
 def test_prefill_flop_model():

@@ -798,7 +798,7 @@ def test_mla_decode_matches_oracle(H, Smax, B):
 def test_full_size_mla_decode_sampled():
     # the bench's DeepSeek-V3-shaped batch and launch, sampled sequences checked by the oracle
     import bench
-    mx, _, _, _, _ = bench.run_mla(MLA, 1, 0, torch, g)
+    mx, _, _, _ = bench.run_mla(MLA, 1, 0, torch, g)
     lens = mx["lens"]
     got = mx["out"].float().cpu().numpy()
     assert np.isfinite(got).all()
