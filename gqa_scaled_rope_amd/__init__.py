@@ -22,7 +22,8 @@ __all__ = [
     "attn_prefill", "attn_decode", "decode_workspace_bytes", "PagedKV", "paged_append",
     "paged_decode_workspace_bytes", "attn_decode_paged", "mla_decode_workspace_bytes",
     "mla_decode", "prefill_workspace_bytes", "prep_keys", "last_error", "KERNELS",
-    "hip_runtimes_mapped", "LIB_PATH", "EXPORTS",
+    "hip_runtimes_mapped", "attn_decode_noalloc", "DECODE_NOALLOC_MAX_BYTES", "LIB_PATH",
+    "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_rope.so")
@@ -92,6 +93,8 @@ EXPORTS = {
     "gqa_decode_workspace_bytes": (_SZ, [ctypes.POINTER(_AttnCfg), _I32, _I32]),
     "gqa_attn_decode": (_I32, [ctypes.POINTER(_AttnCfg), _P, _P, _P, _P, _I32, _I32, _I32, _P, _P,
                                _SZ, _P]),
+    "gqa_attn_decode_noalloc": (_I32, [ctypes.POINTER(_AttnCfg), _P, _P, _P, _P, _I32, _I32,
+                                       _I32, _P, _P]),
     "gqa_paged_append": (_I32, [ctypes.POINTER(_AttnCfg), ctypes.POINTER(_PagedKV), _P, _P, _P,
                                 _I64, _P, _I32, _I32, _P]),
     "gqa_paged_decode_workspace_bytes": (_SZ, [ctypes.POINTER(_AttnCfg), ctypes.POINTER(_PagedKV),
@@ -438,6 +441,31 @@ def attn_decode(cfg: AttnConfig, q, kcache, vcache, lens, window=0, out=None, wo
     c = cfg.c_struct()
     _check(library().gqa_attn_decode(ctypes.byref(c), pq, pk, pv, pl, B, Smax, int(window), po, pw,
                                      nbytes, _stream(stream)))
+    return out
+
+
+DECODE_NOALLOC_MAX_BYTES = 64 << 20   # GQA_DECODE_NOALLOC_MAX_BYTES
+
+
+def attn_decode_noalloc(cfg: AttnConfig, q, kcache, vcache, lens, window=0, out=None,
+                        stream=None):
+    """attn_decode whose split partials live in the library's fixed per-GPU scratch (no device
+    allocation by the library; `out` is allocated here only when not given).  Calls that overlap
+    on one GPU race."""
+    torch = _torch()
+    B = q.shape[0]
+    Smax = kcache.shape[2]
+    dt = cfg.torch_dtype
+    pq = _need(q, "q", (B, cfg.num_q_heads, cfg.head_dim), dt)
+    pk = _need(kcache, "kcache", (B, cfg.num_kv_heads, Smax, cfg.head_dim), dt)
+    pv = _need(vcache, "vcache", (B, cfg.num_kv_heads, Smax, cfg.head_dim), dt)
+    pl = _need(lens, "lens", (B,), torch.int32)
+    if out is None:
+        out = torch.empty_like(q)
+    po = _need(out, "out", tuple(q.shape), dt)
+    c = cfg.c_struct()
+    _check(library().gqa_attn_decode_noalloc(ctypes.byref(c), pq, pk, pv, pl, B, Smax, int(window),
+                                             po, _stream(stream)))
     return out
 
 

@@ -29,6 +29,7 @@
 // unconditional (ranges that must not be touched are cut off by buffer descriptors), so the
 // compiler's wait counts are exact and no wait ever covers the stores.
 #include <algorithm>
+#include <mutex>
 
 #include "launch.hpp"
 
@@ -664,6 +665,35 @@ bool decode_mfma_supported(const AttnArgs& a) {
 size_t decode_mfma_workspace_bytes(int B, int Hkv, int G, int D, int Smax) {
   (void)D;  // head_dim is 128 on this path
   return decode_ws_layout(B, Hkv, G, Smax).total;
+}
+
+// ---- fixed scratch for the entry point that allocates nothing ---------------------------------
+// One array per GPU, in this module's device memory for as long as the process runs.  Host code
+// never uses the array's name as an address (on the host it is only a stand-in for the symbol):
+// each device's address comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address reaches kernels.
+namespace {
+__device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_mfma(const AttnArgs& a, void* workspace, hipStream_t stream,

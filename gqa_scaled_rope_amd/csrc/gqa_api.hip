@@ -9,6 +9,9 @@
 #include "gqa_rope.h"
 #include "launch.hpp"
 
+static_assert(GQA_DECODE_NOALLOC_MAX_BYTES == gqa::kDecodeScratchBytes,
+              "the header states the scratch size the library holds");
+
 namespace {
 
 thread_local std::string g_err;
@@ -451,10 +454,12 @@ size_t gqa_decode_workspace_bytes(const gqa_attn_cfg* cfg, int32_t B, int32_t Sm
                                           Smax);
 }
 
-gqa_status gqa_attn_decode(const gqa_attn_cfg* cfg, const void* q, const void* kcache,
-                           const void* vcache, const int32_t* lens, int32_t B, int32_t Smax,
-                           int32_t window, void* out, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
+// gqa_attn_decode, with the split partials either in the caller's workspace or, for the entry
+// point that allocates nothing (noalloc), in the library's fixed per-GPU scratch array.
+static gqa_status decode_impl(const gqa_attn_cfg* cfg, const void* q, const void* kcache,
+                              const void* vcache, const int32_t* lens, int32_t B, int32_t Smax,
+                              int32_t window, void* out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, bool noalloc) {
   gqa_status st = check_cfg(cfg);
   if (st != GQA_OK) return st;
   if (B < 0 || Smax < 1) return fail(GQA_E_SHAPE, "B must be >= 0 and Smax >= 1, got %d, %d", B, Smax);
@@ -491,6 +496,16 @@ gqa_status gqa_attn_decode(const gqa_attn_cfg* cfg, const void* q, const void* k
   if (decode_uses_mfma(cfg)) {
     const size_t need =
         gqa::decode_mfma_workspace_bytes(B, a.Hkv, a.G, cfg->head_dim, Smax);
+    if (noalloc) {
+      if (need > GQA_DECODE_NOALLOC_MAX_BYTES)
+        return fail(GQA_E_WORKSPACE, "decode of B=%d sequences with Smax=%d needs %zu bytes of "
+                    "scratch, more than the %zu of the no-allocation entry point; call "
+                    "gqa_attn_decode with a workspace", B, Smax, need,
+                    (size_t)GQA_DECODE_NOALLOC_MAX_BYTES);
+      hipError_t e = gqa::decode_scratch(&workspace);
+      if (e != hipSuccess) return hip_status(e, "decode scratch address");
+      workspace_bytes = GQA_DECODE_NOALLOC_MAX_BYTES;
+    }
     if (!workspace || workspace_bytes < need)
       return fail(GQA_E_WORKSPACE, "decode needs a workspace of %zu bytes, got %zu%s", need,
                   workspace_bytes, workspace ? "" : " (null)");
@@ -501,6 +516,20 @@ gqa_status gqa_attn_decode(const gqa_attn_cfg* cfg, const void* q, const void* k
   }
   return hip_status(gqa::launch_attn_generic(a, cfg->dtype == GQA_BF16, stream),
                     "decode (generic) launch");
+}
+
+gqa_status gqa_attn_decode(const gqa_attn_cfg* cfg, const void* q, const void* kcache,
+                           const void* vcache, const int32_t* lens, int32_t B, int32_t Smax,
+                           int32_t window, void* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  return decode_impl(cfg, q, kcache, vcache, lens, B, Smax, window, out, workspace,
+                     workspace_bytes, stream, false);
+}
+
+gqa_status gqa_attn_decode_noalloc(const gqa_attn_cfg* cfg, const void* q, const void* kcache,
+                                   const void* vcache, const int32_t* lens, int32_t B,
+                                   int32_t Smax, int32_t window, void* out, hipStream_t stream) {
+  return decode_impl(cfg, q, kcache, vcache, lens, B, Smax, window, out, nullptr, 0, stream, true);
 }
 
 static gqa_status check_paged(const gqa_attn_cfg* cfg, const gqa_paged_kv* kv, gqa::PagedKV* out) {

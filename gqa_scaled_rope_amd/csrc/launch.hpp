@@ -52,6 +52,11 @@ size_t decode_mfma_workspace_bytes(int B, int Hkv, int G, int D, int Smax);
 hipError_t launch_decode_mfma(const AttnArgs& a, void* workspace, hipStream_t stream,
                               const PagedKV* paged = nullptr, SplitMode mode = SplitMode::kAuto);
 
+// Decode scratch that needs no allocation: the address of this GPU's fixed array of
+// kDecodeScratchBytes (taken once per device, with the device current).  Calls on one GPU share it.
+constexpr size_t kDecodeScratchBytes = (size_t)64 << 20;
+hipError_t decode_scratch(void** ptr);
+
 // cache.update into a paged pool: rows i < a.L of a.k (normed and rotated at a.kpos, as the key
 // preparation does) and of a.v (copied) go to slots start[b] + i.
 hipError_t launch_paged_append(const AttnArgs& a, const PagedKV& kv, void* k_pool, void* v_pool,

@@ -230,6 +230,21 @@ gqa_status gqa_attn_decode(const gqa_attn_cfg* cfg, const void* q, const void* k
                            int32_t window, void* out, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* gqa_attn_decode for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments (less the workspace),
+ * layouts, errors and result as gqa_attn_decode; the split partials live in a fixed array of
+ * GQA_DECODE_NOALLOC_MAX_BYTES inside the library instead, one per GPU, which that GPU holds from
+ * the first call (or library load) until the process ends.  The call allocates nothing.  Sizes
+ * whose gqa_decode_workspace_bytes(cfg, B, Smax) exceed the limit return GQA_E_WORKSPACE (the
+ * Llama-3.1-style batch of 64 sequences of up to 32768 keys, Hkv 8, G 4 needs ~34 MiB).  Every
+ * call on one GPU shares that GPU's array and leaves its last contents there (nothing in it has
+ * to start at zero): calls that overlap on one GPU -- unordered streams, or several host threads
+ * -- race and give wrong results, so order them on one stream. */
+#define GQA_DECODE_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+gqa_status gqa_attn_decode_noalloc(const gqa_attn_cfg* cfg, const void* q, const void* kcache,
+                                   const void* vcache, const int32_t* lens, int32_t B,
+                                   int32_t Smax, int32_t window, void* out, hipStream_t stream);
+
 /* Paged KV pool (the block manager's layout behind cache.update: [Models] "What differs" (the
  * cache.update call), "Sliding windows" (blocks that leave every window can be recycled) and the
  * multi-head latent attention section's paged pool; [Guide] section 3.3 for what the cache holds).

@@ -235,6 +235,22 @@ def test_host_attention_factor_and_softmax_scale_match_oracle(kind, factor, extr
         g.rope_softmax_scale(spec, 0)
 
 
+def test_noalloc_decode_validates_before_touching_the_gpu():
+    # sizes whose partials exceed the fixed scratch are refused on the host, as are the ordinary
+    # argument errors of gqa_attn_decode
+    c = _cfg()
+    assert lib.gqa_decode_workspace_bytes(ctypes.byref(c), 64, 65536) > g.DECODE_NOALLOC_MAX_BYTES
+    st = lib.gqa_attn_decode_noalloc(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 64, 65536, 0, FAKE,
+                                     None)
+    assert st == 5 and "no-allocation" in g.last_error()
+    st = lib.gqa_attn_decode_noalloc(ctypes.byref(c), FAKE, FAKE, FAKE, None, 2, 16, 0, FAKE, None)
+    assert st == 1 and "lens" in g.last_error()
+    assert lib.gqa_attn_decode_noalloc(ctypes.byref(c), None, None, None, None, 0, 16, 0, None,
+                                       None) == 0
+    assert lib.gqa_attn_decode_noalloc(ctypes.byref(_cfg(kernel=9)), FAKE, FAKE, FAKE, FAKE, 1, 16,
+                                       0, FAKE, None) == 7
+
+
 def test_kernel_choice_is_per_call():
     # the library exports no selection state: the choice travels in each call's cfg
     assert not any("policy" in name for name in g.EXPORTS)
