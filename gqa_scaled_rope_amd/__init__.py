@@ -32,7 +32,8 @@ GQA_F32, GQA_BF16 = 0, 1
 ROPE_KINDS = {"default": 0, "linear": 1, "llama3": 2, "yarn": 3, "longrope": 4}
 ROT_STYLES = {"half": 0, "interleaved": 1}
 # gqa_attn_cfg.kernel (gqa_kernel_select): per-call kernel choice, "auto" in production
-KERNELS = {"auto": 0, "generic": 1, "decode_short": 2, "decode_long": 3}
+KERNELS = {"auto": 0, "generic": 1, "decode_short": 2, "decode_long": 3, "prefill_long": 4,
+           "prefill_short": 5}
 STATUS = {0: "GQA_OK", 1: "GQA_E_NULL", 2: "GQA_E_SHAPE", 3: "GQA_E_DTYPE",
           4: "GQA_E_UNSUPPORTED", 5: "GQA_E_WORKSPACE", 6: "GQA_E_HIP", 7: "GQA_E_VALUE"}
 

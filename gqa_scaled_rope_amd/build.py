@@ -27,13 +27,20 @@ FLAGS = [
 ]
 
 
+# Per-file code-generation options: no NaN is assumed in the prefill stream kernel, so row maxima
+# need no quieting instruction (infinities are kept: masked scores are -inf).
+FILE_FLAGS = {
+    "attn_prefill_stream.hip": ["-fno-honor-nans"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src):
     obj = os.path.join(OBJ, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -9,115 +9,31 @@
 //     used in place.  This is the cache-append step of the page's flow (rotate,
 //     then cache.update) and costs one read and one write of the new keys, instead of redoing the
 //     norm and rotation each time a key tile is revisited by another query block.
-//  2. prefill_stream_kernel: the attention proper.  Same tiling and math as the fused kernel
-//     (4 wavefronts x 32 query rows of one KV head, 32-key tiles, S^T = K Q^T and O^T = V^T P^T on
-//     v_mfma_f32_32x32x16_bf16, online softmax in log2 units with lazy rescaling), but K and V
+//  2. prefill_stream_kernel: the attention proper.  The same math as the fused kernel (32-key
+//     tiles, S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16, online softmax in log2
+//     units with lazy rescaling), on 8 wavefronts x 32 query rows of one KV head in two groups
+//     that alternate matrix and softmax phases; K and V
 //     tiles travel from HBM straight into LDS with buffer_load ... lds: no VGPR staging, no LDS
 //     store instructions, 32-bit offsets from a buffer descriptor, and the descriptor's range check
 //     returns zeros past the last key, which handles the ragged tail.  Each wave instruction fills
 //     1 KB of LDS in lane order; choosing the source chunk per lane produces the XOR-swizzled
 //     layout the MFMA operand reads want.
+#include <algorithm>
 #include <type_traits>
 
-#include "launch.hpp"
+#include "stream_tiles.hpp"
 
 namespace gqa {
 namespace {
 
-constexpr int HD = 128;
-constexpr int NW = 4;
+using namespace stream;
+
+constexpr int NW = 8;                 // wavefronts per workgroup, two per SIMD
 constexpr int NT = NW * 64;
-constexpr int ROWS = NW * 32;
-constexpr int BN = 32;
-constexpr int TILE_ELEMS = BN * HD;
+constexpr int WROWS = 32;             // query rows per wavefront
+constexpr int ROWS = NW * WROWS;      // 256 query rows per workgroup
 constexpr int kTileRounds = BN / (4 * NW);  // 1 KB loads per wave per K (or V) tile
 static_assert(BN % (4 * NW) == 0 && BN <= 64, "tile loader and key-position loader layout");
-constexpr float kRescaleThreshold = 8.0f;
-constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit dwords, range checked
-
-constexpr int kXcds = 8;               // MI355X: 8 accelerator complex dies, one L2 each
-
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor as four words (base, stride 0, num_records, flags) for tile_dma16.
-__device__ __forceinline__ i32x4 rsrc_words(const void* base, int nrec) {
-  const uint64_t p = (uint64_t)base;
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xffffu));
-  r[2] = __builtin_amdgcn_readfirstlane(nrec);
-  r[3] = kBufFlags;
-  return r;
-}
-
-// One HBM -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds: lane l's bytes land at
-// dst + 16 l).  Written as assembly on purpose: the compiler's wait-count pass cannot tell these
-// asynchronous LDS writes apart from the reads of the other tile buffers and would make the
-// next LDS read wait for every tile load just issued, which removes the prefetch.  Correctness
-// rests on the explicit full wait before each barrier that hands a buffer to its readers; the
-// compiler's own memory waits stay correct because loads retire in issue order.
-// The five wait states before the load cover the m0 write (one needed) and a descriptor word
-// written by a VALU instruction just before (five needed before a memory instruction reads it);
-// the compiler does not look inside the statement for either hazard.
-__device__ __forceinline__ void tile_dma16(i32x4 rsrc, const lds_void* dst, int voff) {
-  uint32_t saved;  // m0 is the LDS address operand; it is restored for the compiler
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 4\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane((int)(uintptr_t)dst)), "v"(voff), "s"(rsrc));
-}
-
-__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *(const u32x4*)p; }
-__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& w) { return __builtin_bit_cast(bf16x8, w); }
-
-__device__ __forceinline__ void unpack8(const u32x4& w, float* x) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[2 * e] = bf16lo(w[e]);
-    x[2 * e + 1] = bf16hi(w[e]);
-  }
-}
-__device__ __forceinline__ u32x4 pack8(const float* x) {
-  u32x4 w;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
-  return w;
-}
-
-
-// LDS layout of a tile: row r's 16-byte chunk c sits at chunk position c ^ swz(r).  K tiles use
-// swz = r & 15, measured free of bank conflicts for the operand reads (ds_read_b128, 32 rows).
-// V tiles: ds_read_b64_tr_b16 serves lanes 0-31 and 32-63 as two passes of 256 bytes over the
-// 64 four-byte banks (measured on gfx950); each pass here reads four chunks of each of four
-// consecutive rows, 256-byte rows, so the rows' 64-byte chunk quads must land in four different
-// quarters of the bank array: swz = (r & 3) << 2 moves row r's quad by r & 3 quarters.
-__device__ __forceinline__ int kswz(int r) { return r & 15; }
-__device__ __forceinline__ int vswz(int r) { return (r & 3) << 2; }
-
-// First index j in [0, n) with kp[j] >= x for a nondecreasing kp, found by the whole wavefront:
-// each round samples 64 evenly spaced entries and keeps the one segment that contains the
-// boundary, so n keys take ceil(log64 n) dependent loads instead of log2 n.
-__device__ __forceinline__ int wave_lower_bound(const int32_t* kp, int n, int64_t x) {
-  const int lane = threadIdx.x & 63;
-  int lo = 0, hi = n;  // answer in [lo, hi]
-  while (hi > lo) {
-    const int stride = (hi - lo + 63) >> 6;
-    const int idx = lo + lane * stride;
-    const bool below = idx < hi && (int64_t)kp[idx] < x;
-    const int cnt = __popcll(__ballot(below));
-    if (cnt == 0) {
-      hi = lo;
-    } else {
-      const int nlo = lo + (cnt - 1) * stride + 1;
-      hi = min(lo + cnt * stride, hi);
-      lo = nlo;
-    }
-  }
-  return lo;
-}
 
 // ---------------------------------------------------------------------------------------------
 // 1. key preparation: 16 lanes per key row (8 features each), 16 rows per 256-thread block
@@ -300,41 +216,79 @@ __global__ __launch_bounds__(256) void rows_prep_kernel(AttnArgs a, RowJob jb) {
 // ---------------------------------------------------------------------------------------------
 // 2. attention over prepared keys
 // ---------------------------------------------------------------------------------------------
-// Triple-buffered K/V/key-position tiles.  Each buffer is its own LDS object and the step loop
-// is unrolled over the buffer cycle, so every access names its buffer at compile time: the
-// compiler can then see that reads of the current tiles never alias the asynchronous HBM->LDS
-// loads of a later one and does not make them wait for those loads.
-constexpr int NBUF = 3;
-__shared__ __attribute__((aligned(16))) uint16_t g_k0[TILE_ELEMS];
-__shared__ __attribute__((aligned(16))) uint16_t g_k1[TILE_ELEMS];
-__shared__ __attribute__((aligned(16))) uint16_t g_k2[TILE_ELEMS];
-__shared__ __attribute__((aligned(16))) uint16_t g_v0[TILE_ELEMS];
-__shared__ __attribute__((aligned(16))) uint16_t g_v1[TILE_ELEMS];
-__shared__ __attribute__((aligned(16))) uint16_t g_v2[TILE_ELEMS];
-__shared__ __attribute__((aligned(16))) int32_t g_p0[BN];
-__shared__ __attribute__((aligned(16))) int32_t g_p1[BN];
-__shared__ __attribute__((aligned(16))) int32_t g_p2[BN];
-
-template <int BUF>
-__device__ __forceinline__ uint16_t* kbuf() { return BUF == 0 ? g_k0 : BUF == 1 ? g_k1 : g_k2; }
-template <int BUF>
-__device__ __forceinline__ uint16_t* vbuf() { return BUF == 0 ? g_v0 : BUF == 1 ? g_v1 : g_v2; }
-template <int BUF>
-__device__ __forceinline__ int32_t* pbuf() { return BUF == 0 ? g_p0 : BUF == 1 ? g_p1 : g_p2; }
-
-struct StreamArgs {
-  AttnArgs a;
-  const uint16_t* kprep;   // [B, S - w0, Hkv, D] keys from row w0 = max(n_cached - (BN-1), 0) on,
-                           // new ones prepared (null if nothing needs preparing)
+// A workgroup is eight wavefronts of 32 query rows (256 rows of one KV head), one workgroup per
+// CU, so each SIMD holds two wavefronts: w and w + 4 (waves are dealt to the SIMDs in turn).  On
+// gfx950 a wavefront's own vector instructions do not overlap its 32x32x16 MFMAs (each MFMA
+// holds the wavefront for about 28 of its 32 cycles), but another wavefront's do.  So the two
+// wavefronts of a SIMD take turns: while one issues its matrix phase the other runs its
+// softmax phase, and a workgroup barrier after every phase swaps them.  Per 32-key tile t a
+// wavefront runs
+//   matrix phase M(t):   S(t+1) = K(t+1) Q^T and O^T += V(t)^T P(t)^T (16 MFMAs, K and V read
+//                        from LDS)
+//   softmax phase V(t):  mask (edge tiles only), row max, rare rescale, exp2, bf16 P(t+1), row
+//                        sums
+// group 0 (waves 0-3) in the order M(0) V(0) M(1) V(1) ..., group 1 (waves 4-7) one phase later:
+// [idle] M(0) V(0) M(1) ...  Scores arrive relative to the row's running reference m (log2 units):
+// the first MFMA of each S^T chain starts from a template holding -m, and m moves only when a
+// score exceeds it by more than kRescaleThreshold (exact, rare), when O, the sum, the scores and
+// the template are corrected.
+//
+// K, V and key positions travel HBM -> LDS by buffer_load ... lds through eight buffers; tile
+// t+7 is issued (by every wavefront, 1/8 of the tile each) at the start of the softmax phase that
+// follows M(t), about six tiles before its keys are needed.  Tiles past the band are issued with an
+// out-of-range offset (no memory access, zeros written), so every wavefront issues the same
+// number of loads per tile and fixed vmcnt waits retire exactly the tiles that must have landed.
+constexpr int NBUF = 8;
+constexpr int kDmaPerTile = 2 * kTileRounds + 1; // per wavefront: K, V and the key positions
+constexpr uint32_t kNullOfs = 0x7FFFF000u;       // a buffer offset past every descriptor's range
+// The K tiles come first, so that every K operand read reaches its buffer with a constant offset
+// below 64 KB from one per-lane address; the V reads get their own per-lane base 64 KB on.
+// Key positions: wave 0 loads the tile's; the other wavefronts' loads (out of range, same count)
+// write zeros into their own rows, never into the one that is read.  144 KB in all.
+struct StreamLds {
+  uint16_t k[NBUF][TILE_ELEMS];
+  uint16_t v[NBUF][TILE_ELEMS];
+  int32_t kp[NBUF][NW][64];
 };
+__shared__ __attribute__((aligned(16))) StreamLds g_lds;
 
-template <int ROT, bool NORM, bool CAP>
-// Two workgroups per CU (3 x 16 KB tiles of LDS and up to 256 VGPRs each): one's query prep and
-// first tiles overlap the other's loop, and each barrier holds only the four waves of one group.
-__global__ __launch_bounds__(NT, 2) void prefill_stream_kernel(StreamArgs sa, int nqb) {
+
+// One HBM -> LDS copy of 4 bytes per lane (buffer_load_dword ... lds: lane l's dword lands at
+// dst + 4 l).  Same hazards as tile_dma16.
+__device__ __forceinline__ void tile_dma4(i32x4 rsrc, const lds_void* dst, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 4\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(rsrc));
+}
+
+// Workgroup barrier ordering LDS accesses only (the fences wait for this wavefront's LDS
+// operations, not for its buffer loads); scheduling barriers keep the two phases apart.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// The same after waiting until at most N of this wavefront's buffer loads are outstanding (they
+// retire in order): every wavefront's share of the tile due has then landed.
+template <int N>
+__device__ __forceinline__ void barrier_after_loads() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
+  phase_barrier();
+}
+
+template <int ROT, bool NORM, bool CAP, bool WS>
+__global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, int nqb) {
   const AttnArgs& a = sa.a;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = w >> 2;  // 0: matrix phase first; 1: one phase later
   const int ql = lane & 31, hg = lane >> 5;
   // Work item of this workgroup.  Workgroups are dealt to the 8 XCDs round-robin by id; map ids
   // so that every query block of one (b, g) lands on the same XCD (its K/V then stay in that
@@ -362,7 +316,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_stream_kernel(StreamArgs sa, in
   const int64_t f0 = (int64_t)qb * ROWS;
 
   // ---- this lane's query row (flattened position-major (position, head) index) ----
-  const int64_t f = f0 + w * 32 + ql;
+  const int64_t f = f0 + WROWS * w + ql;
   const bool qvalid = f < nrows;
   const int qi = qvalid ? (int)(f / G) : 0;
   const int qh = g * G + (qvalid ? (int)(f % G) : 0);
@@ -374,7 +328,6 @@ __global__ __launch_bounds__(NT, 2) void prefill_stream_kernel(StreamArgs sa, in
   const int32_t* kpos_b = a.kpos + (int64_t)b * a.kpos_b;
   const int i_lo = (int)(f0 / G);
   const int i_hi = (int)min<int64_t>((f0 + ROWS - 1) / G, (int64_t)a.L - 1);
-  // (at most ROWS positions; every load is issued, at a clamped index, before any is used)
   int32_t prange[ROWS / 64];
 #pragma unroll
   for (int k = 0; k < ROWS / 64; ++k) prange[k] = qpos_b[min(i_lo + lane + 64 * k, i_hi)];
@@ -387,64 +340,52 @@ __global__ __launch_bounds__(NT, 2) void prefill_stream_kernel(StreamArgs sa, in
   }
   const int32_t kp0 = kpos_b[0];
 
-  // ---- buffer descriptors of this (b, g): cached keys, prepared keys, values ----
+  // ---- buffer descriptors of this (b, g): cached keys, prepared keys, values, key positions ----
   const int row_bytes = (int)(a.k_j * 2);  // bytes between consecutive keys of one head
   const int64_t kv_base = (int64_t)b * a.k_b + (int64_t)g * a.k_h;
-  // Without a workspace nothing needs preparing and every key comes from k.  With one, a tile
-  // whose keys all lie below nc comes from k as stored and any other from the workspace, which
-  // starts at row w0 <= (first row of any tile reaching past nc).  The choice is uniform per
-  // tile, so each load names one descriptor.
-  const int nc = sa.kprep ? a.n_cached : a.S;
+  // Without a workspace (WS false) nothing needs preparing and every key comes from k.  With
+  // one, a tile whose keys all lie below nc comes from k as stored and any other from the
+  // workspace, which starts at row w0 <= (first row of any tile reaching past nc).  The choice is
+  // uniform per tile, so each load names one descriptor.
+  const int nc = WS ? a.n_cached : a.S;
   const int w0 = nc > BN - 1 ? nc - (BN - 1) : 0;
   const int nws = a.S - w0;
   const i32x4 rk = rsrc_words((const uint16_t*)a.k + kv_base,
                               nc > 0 ? (nc - 1) * row_bytes + HD * 2 : 0);
   const i32x4 rw = rsrc_words(
-      sa.kprep ? sa.kprep + (int64_t)b * nws * a.k_j + (int64_t)g * a.k_h : nullptr,
-      (sa.kprep && nws > 0) ? (nws - 1) * row_bytes + HD * 2 : 0);
+      WS ? sa.kprep + (int64_t)b * nws * a.k_j + (int64_t)g * a.k_h : nullptr,
+      (WS && nws > 0) ? (nws - 1) * row_bytes + HD * 2 : 0);
   const i32x4 rv = rsrc_words((const uint16_t*)a.v + kv_base, (a.S - 1) * row_bytes + HD * 2);
-  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.kpos + (int64_t)b * a.kpos_b), (short)0, a.S * 4, kBufFlags);
+  const i32x4 rp = rsrc_words(kpos_b, a.S * 4);
 
-  uint32_t kp_pend = 0;
-  bool kp_pend_ok = false;
   // Tile loader: wave w, round i fills LDS rows 4*(w + NW i) .. +3 (1 KB); lane -> row
   // 4(w + NW i) + lane/16, LDS chunk lane%16, which holds source chunk (lane%16) ^ swz(row).
-  // Lane constants of the tile loader (offset of the lane's 16 bytes within a tile); a tile adds
-  // jt rows.  Rows at or past S fall outside the descriptors' ranges and read as zero.
-  int lk[kTileRounds], lv[kTileRounds];
+  // Rows at or past S fall outside the descriptors' ranges and read as zero.  Wave 0 also loads
+  // the tile's key positions (64 entries: the tile's 32 and the next 32, unused).
+  const uint32_t lds_w = (uint32_t)(4 * w * HD * sizeof(uint16_t));  // this wave's rows of a tile
+  uint32_t lk[kTileRounds], lv[kTileRounds];
 #pragma unroll
   for (int i = 0; i < kTileRounds; ++i) {
     const int r = 4 * (w + NW * i) + (lane >> 4);
     lk[i] = r * row_bytes + (((lane & 15) ^ kswz(r)) << 4);
     lv[i] = r * row_bytes + (((lane & 15) ^ vswz(r)) << 4);
   }
-  auto issue_tile = [&](int jt, auto bufc) {
+  // the tile starting at key jt (live) or an out-of-range one (no memory access) into buffer buf
+  auto issue_tile = [&](int jt, bool live, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
-    const int tb = jt * row_bytes;  // values (and cached keys): rows from 0
-    const bool from_k = sa.kprep == nullptr || jt + BN <= nc;
+    const bool from_k = !WS || jt + BN <= nc;
     const i32x4 rks = from_k ? rk : rw;
-    const int kb0 = from_k ? tb : (jt - w0) * row_bytes;
+    const uint32_t tb = live ? (uint32_t)(jt * row_bytes) : kNullOfs;
+    const uint32_t kb0 = live ? (uint32_t)((from_k ? jt : jt - w0) * row_bytes) : kNullOfs;
 #pragma unroll
     for (int i = 0; i < kTileRounds; ++i) {
-      lds_void* kdst = (lds_void*)(kbuf<buf>() + 4 * (w + NW * i) * HD);
-      lds_void* vdst = (lds_void*)(vbuf<buf>() + 4 * (w + NW * i) * HD);
-      tile_dma16(rv, vdst, lv[i] + tb);
-      tile_dma16(rks, kdst, lk[i] + kb0);
+      tile_dma16_at(rv, (lds_void*)(g_lds.v[buf] + 4 * NW * i * HD), lds_w, lv[i] + tb);
+      tile_dma16_at(rks, (lds_void*)(g_lds.k[buf] + 4 * NW * i * HD), lds_w, lk[i] + kb0);
     }
-    // key positions of the tile: loaded by wave 0 into a register and written to LDS by
-    // commit_kpos once the tile's loads are complete, with INT32_MAX past the last key so that the
-    // position test alone masks the ragged tail
-    if (w == 0) {
-      kp_pend = __builtin_amdgcn_raw_buffer_load_b32(rp, (jt + lane) * 4, 0, 0);
-      kp_pend_ok = lane < BN && jt + lane < a.S;
-    }
+    // (the other wavefronts issue it with an out-of-range offset: same count of loads everywhere)
+    tile_dma4(rp, (lds_void*)g_lds.kp[buf][w],
+              live && w == 0 ? (uint32_t)((jt + lane) * 4) : kNullOfs + 4 * lane);
   };
-  auto commit_kpos = [&](auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    if (w == 0 && lane < BN) pbuf<buf>()[lane] = kp_pend_ok ? (int32_t)kp_pend : INT32_MAX;
-  };
-
 
   // ---- band guesses: with consecutive key positions the band edges are known from the query
   // positions; the two keys around each guess are loaded now (clamped indices) and checked below
@@ -459,29 +400,28 @@ __global__ __launch_bounds__(NT, 2) void prefill_stream_kernel(StreamArgs sa, in
   const int64_t x_hi = qmax + 1, x_lo = key_floor(a, qmin);
   // a tile needs no mask when every query may see its first key (and its last is causal for all)
   const int32_t floor_max = (int32_t)max<int64_t>(key_floor(a, qmax), INT32_MIN);
+  const int32_t qmin32 = (int32_t)qmin;
   const int g_hi = (int)min<int64_t>(max<int64_t>(x_hi - kp0, 0), a.S);
   const int g_lo = (int)min<int64_t>(max<int64_t>(x_lo - kp0, 0), a.S);
   // The first tile's loads go out now -- at key 0 without a window or chunks, else at the guessed
-  // band start (loaded again below if the guess is wrong) -- after the waits for the position
-  // loads above (a wait for those placed behind the tile's loads would wait for the tile too) and
-  // beside the band and query-prep loads below.
+  // band start (loaded again below if the guess is wrong) -- beside the band and query-prep loads.
   const int j_first = a.has_floor() ? g_lo : 0;
   __builtin_amdgcn_sched_barrier(0);
-  issue_tile(j_first, std::integral_constant<int, 0>());
+  issue_tile(j_first, true, std::integral_constant<int, 0>());
   const int32_t hi_l = kpos_b[max(g_hi - 1, 0)], hi_r = kpos_b[min(g_hi, a.S - 1)];
   const int32_t lo_l = kpos_b[max(g_lo - 1, 0)], lo_r = kpos_b[min(g_lo, a.S - 1)];
   // smallest key position the row may see (window, chunks); INT32_MAX for rows past the end
   const int32_t qlo32 = !qvalid ? INT32_MAX
                         : a.has_floor() ? (int32_t)max<int64_t>(key_floor(a, qp), INT32_MIN)
                                         : INT32_MIN;
+  const int32_t qp32 = qvalid ? qp : INT32_MIN;
 
   // ---- query prep, per wavefront and in registers: lane (ql, hg) loads, for its row, exactly the
   // features its MFMA operands hold -- 16 s + 8 hg .. + 7 for s = 0..7 -- RMS-norms the row (the
   // other 64 features are in lane ql + 32), rotates it at its position and scales it into log2
   // units.  With half-split rotation at R = 32, 64 or 128 a feature's partner (R/2 further on)
   // lies R/32 operand chunks further in the same lane; at R = 16 it is in lane l ^ 32.
-  // Interleaved pairs are adjacent.  No LDS and no barrier: the waves prep independently, in two
-  // memory round trips (rows, gains and the position; then the table entries at the position).
+  // Interleaved pairs are adjacent.
   bf16x8 qop[8];
   {
     const uint16_t* qrow = (const uint16_t*)a.q + (int64_t)b * a.q_b + (int64_t)qi * a.q_i +
@@ -610,13 +550,22 @@ __global__ __launch_bounds__(NT, 2) void prefill_stream_kernel(StreamArgs sa, in
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  // Running max m (log2 units; kNegBig until the row has seen an allowed key) and sum.  Scores
-  // are kept relative to m_eff = (m set ? m : 0): the S^T accumulators start at -m_eff, so the
-  // MFMAs deliver s - m_eff directly.  (Soft-capping needs the raw score: there they start at 0
-  // and m_eff is subtracted after the cap.)
+  // Running reference m (log2 units; kNegBig until the row has seen an allowed key) and sum.  The
+  // S^T chains start from -m_eff (m_eff = m once set, else 0), so the scores arrive relative to
+  // the reference: between a softmax phase and the next S^T the score registers hold that start
+  // value.  (Soft-capping needs the raw score: there the chains start from 0 and m_eff is
+  // subtracted with the cap.)
   float m = kNegBig, lsum = 0.f;
+  // The row's rescale threshold and chain start value, changed only when the reference moves:
+  // -inf and 0 until the row has a reference, then kRescaleThreshold and -m.  tmpl holds the start
+  // value in all 16 places, ready as the first MFMA's accumulator input.
+  float thr = -INFINITY, mstart = 0.f;
+  const f32x16 zero16 = {};
+  f32x16 tmpl = zero16;
   const float cap2 = a.softcap * kLog2e;
-  const float inv_cap2 = CAP ? 1.0f / cap2 : 0.f;
+  // cap2 tanh(s / cap2) = 2 cap2 / (1 + 2^(k s)) - cap2 with k = -2 log2(e) / cap2: one exp2, one
+  // reciprocal and one fma per score, with the limits +-cap2 reached exactly for large |s|
+  const float cap_k = CAP ? -2.0f * kLog2e / cap2 : 0.f;
 
   // per-lane LDS read offsets (elements).  K: row ql, chunk 2s + hg.  V^T (transposing reads):
   // rows 4*hgv + s16/4 (+8 for items 4..7) of each 16-key group, columns db*32 + 16*(gi&1) +
@@ -627,125 +576,123 @@ __global__ __launch_bounds__(NT, 2) void prefill_stream_kernel(StreamArgs sa, in
   int koff[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) koff[s] = ql * HD + (((2 * s + hg) ^ kswz(ql)) << 3);
-  int voff[2][4];
+  // V reads: LDS byte addresses in buffer 0, hidden from the compiler so that each read adds a
+  // constant (buffer and key half) below 64 KB to one of these eight registers
+  uint32_t vaddr[2][4];
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
     const int row = 4 * hgv + (s16 >> 2) + 8 * h2;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int col = db * 32 + 16 * (gi & 1) + 4 * (s16 & 3);
-      voff[h2][db] = row * HD + (((col >> 3) ^ vswz(row)) << 3) + (col & 7);
+      const int voff = row * HD + (((col >> 3) ^ vswz(row)) << 3) + (col & 7);
+      vaddr[h2][db] = (uint32_t)(uintptr_t)(lds_void*)(g_lds.v[0] + voff);
+      asm volatile("" : "+v"(vaddr[h2][db]));
     }
   }
-  // mask bounds in int32: allowed <=> qlo32 <= key position <= qp32 (key positions past the last
-  // key read INT32_MAX, so the ragged tail fails the first test)
-  // (qlo32, the window/chunk bound, is computed once the band loads are out: earlier it would
-  // wait for this row's position before any other load is issued, later it costs registers)
-  const int32_t qp32 = qvalid ? (int32_t)qp : INT32_MIN;
 
-  // S^T - m_eff for the 32 keys of a buffered tile
-  auto qk = [&](auto bufc) {
+  f32x16 sc = zero16;  // the next tile's scores (S^T), or the start value of their chain
+  bf16x8 pw[2];       // the current tile's weights P, as the B operand of P V
+  // S^T of the K tile in buffer buf
+  auto qk = [&](auto bufc, const f32x16& c0) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
-    const uint16_t* ks = kbuf<buf>();
+    const uint16_t* ks = g_lds.k[buf];
     u32x4 kop[8];
 #pragma unroll
     for (int st = 0; st < 8; ++st) kop[st] = *(const u32x4*)(ks + koff[st]);
-    // all eight operand reads in flight before the first MFMA waits on one
-    __builtin_amdgcn_sched_barrier(0);
-    const float init = (CAP || m == kNegBig) ? 0.f : -m;
-    const uint64_t init2 = ((uint64_t)__float_as_uint(init) << 32) | __float_as_uint(init);
-    const u64x8 seed = {init2, init2, init2, init2, init2, init2, init2, init2};
-    f32x16 acc = __builtin_bit_cast(f32x16, seed);
+    f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[0]), qop[0], c0, 0, 0, 0);
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
+    for (int st = 1; st < 8; ++st)
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[st]), qop[st], acc, 0, 0, 0);
     return acc;
   };
-
-  // One step = one 32-key tile, software-pipelined: the step's own S^T was computed by the
-  // previous step; here the mask and running max come first, then the NEXT tile's S^T MFMAs are
-  // issued, then this step's exponentials and P V.  In program order the next S^T MFMAs therefore
-  // sit beside this step's exponentials, and this step's P V MFMAs beside the next step's mask and
-  // max, so the matrix unit and the vector ALU work at the same time.
-  // Tiles live in NBUF = 3 buffers: the barrier before the S^T of tile t+1 waits for tile t+1's
-  // loads, and once every wavefront is past it the buffer of tile t-1 is free for tile t+2's.
-  const int nsteps = n_tiles;
-  // two score sets that trade roles every step (a step reads one and fills the other), so no
-  // copy of the next step's scores has to wait for its MFMAs
-  f32x16 s_a, s_b;
-  auto step = [&](int s, auto phc, f32x16& sc, f32x16& s_next) {
-    constexpr int PH = decltype(phc)::value;  // position in the 6-step cycle (buffers x score sets)
-    constexpr int buf = PH % NBUF;
-    constexpr int nbuf = (buf + 1) % NBUF;
-    const int t = s;
-    const int jt = j_lo + t * BN;
-    const int32_t* kpt = pbuf<buf>();
-    const int32_t kfirst = kpt[0];
-    const int32_t klast = kpt[BN - 1];
-    const bool full = (jt + BN <= j_hi) && ((int64_t)klast <= qmin) &&
-                      (kfirst >= floor_max);
-
-    // ---- soft-cap, mask, running max ----
-    const bool unset = m == kNegBig;
+  // O^T += V^T P^T over the V tile in buffer buf
+  auto pv = [&](auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint32_t ofs = (uint32_t)((buf * TILE_ELEMS + 16 * u * HD) * sizeof(uint16_t));
+        const i16x4 vlo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vaddr[0][db] + ofs));
+        const i16x4 vhi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vaddr[1][db] + ofs));
+        const i16x8 va = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pw[u],
+                                                        o[db], 0, 0, 0);
+      }
+  };
+  // The tile starting at key jt needs no mask when all its keys are in range, none is newer than
+  // the oldest query, and every query may see its first key.
+  auto tile_full = [&](int jt, auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    const int32_t kfirst = g_lds.kp[buf][0][0], klast = g_lds.kp[buf][0][BN - 1];
+    return (jt + BN <= j_hi) & (klast <= qmin32) & (kfirst >= floor_max);
+  };
+  // Softmax of the freshly computed scores of the tile at key jt (buffer buf): soft-cap, mask
+  // (allowed <=> key index < j_hi and qlo32 <= key position <= qp32), row max, rare rescale,
+  // exp2, bf16 weights P into pw and the row sum of those weights.
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  auto softmax = [&](int jt, auto bufc, bool full) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
     if (CAP) {
-      const float meff = unset ? 0.f : m;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float x = sc[r] * inv_cap2;
-        const float e = fast_exp2(-2.0f * kLog2e * fabsf(x));
-        sc[r] = copysignf(cap2 * (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e), x) - meff;
+        const float e = fast_exp2(sc[r] * cap_k);
+        sc[r] = __builtin_fmaf(__builtin_amdgcn_rcpf(1.0f + e), 2.0f * cap2, mstart - cap2);
       }
     }
     if (!full) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int32_t kp = kpt[8 * (r >> 2) + 4 * hg + (r & 3)];
-        if (!(kp <= qp32 && kp >= qlo32)) sc[r] = -INFINITY;
+      for (int gq = 0; gq < 4; ++gq) {
+        const int idx0 = 8 * gq + 4 * hg;
+        const i32x4 k4 = *(const i32x4*)(g_lds.kp[buf][0] + idx0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = jt + idx0 + e < j_hi && k4[e] <= qp32 && k4[e] >= qlo32;
+          if (!ok) sc[4 * gq + e] = -INFINITY;
+        }
       }
     }
+    // row max (scores relative to m_eff); the reference moves only when a score exceeds it by
+    // more than the threshold, or on the row's first allowed key
     float mt = sc[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
     mt = fmaxf(mt, swap_halves(mt));
-    // lazy rescale: the reference moves only when a score exceeds it by more than the threshold
-    // (or on the row's first allowed key)
-    const bool upd = unset ? (mt > -INFINITY) : (mt > kRescaleThreshold);
-    if (__ballot(upd) != 0) {
-      const float delta = unset ? (mt > -INFINITY ? mt : 0.f) : fmaxf(mt, 0.f);
-      const float alpha = unset ? 1.f : fast_exp2(-delta);
+    if (__ballot(mt > thr) != 0) {
+      const bool upd = mt > thr;
+      const bool unset = m == kNegBig;
+      const float meff = -mstart;
+      const float mnew = upd ? meff + mt : m;
+      const float alpha = unset ? 1.f : fast_exp2(m - mnew);
+      const bool set_new = mnew != kNegBig;
+      const float meff_new = set_new ? mnew : 0.f;
       lsum *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      m = unset ? (mt > -INFINITY ? mt : kNegBig) : m + delta;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] -= delta;
+      for (int r = 0; r < 16; ++r) sc[r] += meff - meff_new;
+      m = mnew;
+      mstart = -meff_new;
+      thr = set_new ? kRescaleThreshold : -INFINITY;
+      if (!CAP) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmpl[r] = mstart;
+      }
     }
-
-    // ---- the next tile's S^T, after the crossing into it ----
-    if (s + 1 < nsteps) {
-      __builtin_amdgcn_s_waitcnt(0);
-      commit_kpos(std::integral_constant<int, nbuf>());
-      __syncthreads();
-      if (t + 2 < n_tiles) issue_tile(jt + 2 * BN, std::integral_constant<int, (buf + 2) % NBUF>());
-    }
-    // Issued unconditionally so that it shares one basic block with the exponentials and P V
-    // below (the scheduler interleaves only within a block); after the last step it reads a
-    // stale buffer and its result is unused.
-    s_next = qk(std::integral_constant<int, nbuf>());
-
-    // ---- P = exp2(s - m); row sums of the bf16 weights the P V product uses, two per
-    // v_dot2_f32_bf16 against (1, 1) ----
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    // P = exp2(s); row sums of the bf16 weights the P V product uses, two per v_dot2_f32_bf16
     const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
-    bf16x8 pb[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) p[e] = fast_exp2(sc[8 * u + e]);
-      pb[u] = as_bf16x8(pack8(p));
+      pw[u] = as_bf16x8(pack8(p));
       // (each pair is built from its two floats: taking it out of the packed vector with a bit
       // cast made the compiler feed the first pair to all four dot products)
 #pragma unroll
@@ -754,47 +701,94 @@ __global__ __launch_bounds__(NT, 2) void prefill_stream_kernel(StreamArgs sa, in
         lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, lsum, false);
       }
     }
-
-    // ---- O^T += V^T P^T ----
-    const uint16_t* vs = vbuf<buf>();
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int base = 16 * u * HD;
-        const i16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vs + base + voff[0][db]));
-        const i16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vs + base + voff[1][db]));
-        const i16x8 va = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pb[u],
-                                                        o[db], 0, 0, 0);
-      }
   };
-
+  // Matrix phase: O^T += V(buffer b0)^T P^T and S^T of the K tile in buffer b1.  The 24 LDS
+  // operand reads run four MFMAs ahead of their use (each MFMA is 32 cycles, an LDS read's
+  // latency several times that), and no further, so that only a few operands are live at a time
+  // (two wavefronts share each SIMD's registers).
+  // The phase also reads the next tile's first and last key positions and decides whether its
+  // softmax needs the mask (that tile's loads have landed: its K is read here).
+  auto mphase = [&](auto b0c, auto b1c, int jt1, bool& full1) __attribute__((always_inline)) {
+    constexpr int b1 = decltype(b1c)::value;
+    const int32_t kfirst = g_lds.kp[b1][0][0], klast = g_lds.kp[b1][0][BN - 1];
+    pv(b0c);
+    sc = qk(b1c, CAP ? zero16 : tmpl);
+    full1 = (jt1 + BN <= j_hi) & (__builtin_amdgcn_readfirstlane(klast) <= qmin32) &
+            (__builtin_amdgcn_readfirstlane(kfirst) >= floor_max);
+    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);     // V operands of P V 0-3, positions
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // P V i
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // V operand of P V i+4
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // P V 4-7, then S^T 0-3
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // K operand of S^T i
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);      // S^T 4-7
+  };
+  // ---- first tiles: 0 .. NBUF-2 issued, 0 and 1 landed; S(0) and its weights ----
   if (j_lo != j_first && n_tiles > 0) {
-    __builtin_amdgcn_s_waitcnt(0);  // the guessed tile's loads land before the right tile's
-    issue_tile(j_lo, std::integral_constant<int, 0>());
+    asm volatile("s_waitcnt vmcnt(0)");  // the guessed tile's loads land before the right tile's
+    issue_tile(j_lo, true, std::integral_constant<int, 0>());
   }
-  __builtin_amdgcn_s_waitcnt(0);  // also retires the early first-tile loads when n_tiles == 0
-  commit_kpos(std::integral_constant<int, 0>());
-  __syncthreads();  // the first tile and its key positions are visible to every wave
-  if (n_tiles > 1) issue_tile(j_lo + BN, std::integral_constant<int, 1>());
-  if (nsteps > 0) s_a = qk(std::integral_constant<int, 0>());
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  using P2 = std::integral_constant<int, 2>;
-  using P3 = std::integral_constant<int, 3>;
-  using P4 = std::integral_constant<int, 4>;
-  using P5 = std::integral_constant<int, 5>;
-  for (int s = 0; s < nsteps; s += 6) {
-    step(s, P0(), s_a, s_b);
-    if (s + 1 < nsteps) step(s + 1, P1(), s_b, s_a);
-    if (s + 2 < nsteps) step(s + 2, P2(), s_a, s_b);
-    if (s + 3 < nsteps) step(s + 3, P3(), s_b, s_a);
-    if (s + 4 < nsteps) step(s + 4, P4(), s_a, s_b);
-    if (s + 5 < nsteps) step(s + 5, P5(), s_b, s_a);
+  issue_tile(j_lo + 1 * BN, 1 < n_tiles, std::integral_constant<int, 1>());
+  issue_tile(j_lo + 2 * BN, 2 < n_tiles, std::integral_constant<int, 2>());
+  issue_tile(j_lo + 3 * BN, 3 < n_tiles, std::integral_constant<int, 3>());
+  issue_tile(j_lo + 4 * BN, 4 < n_tiles, std::integral_constant<int, 4>());
+  issue_tile(j_lo + 5 * BN, 5 < n_tiles, std::integral_constant<int, 5>());
+  issue_tile(j_lo + 6 * BN, 6 < n_tiles, std::integral_constant<int, 6>());
+  barrier_after_loads<(NBUF - 3) * kDmaPerTile>();
+  sc = qk(std::integral_constant<int, 0>(), zero16);
+  softmax(j_lo, std::integral_constant<int, 0>(), tile_full(j_lo, std::integral_constant<int, 0>()));
+
+  // Tile t sits in buffer t mod NBUF.  Both groups run the same sequence -- M(t), barrier, refill
+  // of tile t-1's buffer with tile t+NBUF-1, V(t+1), barrier -- group 1 one phase behind group 0:
+  // it passes one extra barrier before its first phase, group 0 one after its last.  So group 0's
+  // M(t) and group 1's V(t) share a phase, as do group 0's V(t+1) and group 1's M(t).  Tile t-1
+  // was last read by group 1's M(t-1), which ended before either group passes M(t)'s barrier;
+  // the refill is issued in the softmax phase, off the matrix path.  Before a barrier each
+  // wavefront waits until at most its newest NBUF-4 (after M) or NBUF-3 (after V) tiles'
+  // loads are outstanding: its share of the tile that the next phase's S^T reads has then landed
+  // (loads retire in issue order).
+  auto iter = [&](int t, auto phc) __attribute__((always_inline)) {
+    constexpr int PH = decltype(phc)::value;
+    using B0 = std::integral_constant<int, PH>;
+    using B1 = std::integral_constant<int, (PH + 1) % NBUF>;
+    using BR = std::integral_constant<int, (PH + NBUF - 1) % NBUF>;
+    const int jt1 = j_lo + (t + 1) * BN;
+    bool full1;
+    mphase(B0(), B1(), jt1, full1);
+    barrier_after_loads<(NBUF - 4) * kDmaPerTile>();
+    issue_tile(j_lo + (t + NBUF - 1) * BN, t + NBUF - 1 < n_tiles, BR());
+    softmax(jt1, B1(), full1);
+    barrier_after_loads<(NBUF - 3) * kDmaPerTile>();
+  };
+  if (grp == 1) barrier_after_loads<(NBUF - 4) * kDmaPerTile>();
+  // (exits after any iteration: the unrolled body stays one straight path with no joins inside)
+  for (int t = 0; t < n_tiles;) {
+    iter(t, std::integral_constant<int, 0>());
+    if (++t >= n_tiles) break;
+    iter(t, std::integral_constant<int, 1>());
+    if (++t >= n_tiles) break;
+    iter(t, std::integral_constant<int, 2>());
+    if (++t >= n_tiles) break;
+    iter(t, std::integral_constant<int, 3>());
+    if (++t >= n_tiles) break;
+    iter(t, std::integral_constant<int, 4>());
+    if (++t >= n_tiles) break;
+    iter(t, std::integral_constant<int, 5>());
+    if (++t >= n_tiles) break;
+    iter(t, std::integral_constant<int, 6>());
+    if (++t >= n_tiles) break;
+    iter(t, std::integral_constant<int, 7>());
+    ++t;
   }
+  static_assert(NBUF == 8, "the loop above is unrolled by NBUF");
+  if (grp == 0) phase_barrier();
+  // every wavefront's loads retire before the workgroup ends (the last ones were out of range)
+  asm volatile("s_waitcnt vmcnt(0)");
 
   const float ltot = lsum + swap_halves(lsum);
   // a learned sink joins the denominator only (log2 units, relative to the running max m, which
@@ -818,18 +812,23 @@ __global__ __launch_bounds__(NT, 2) void prefill_stream_kernel(StreamArgs sa, in
   }
 }
 
-template <int ROT, bool NORM, bool CAP>
+template <int ROT, bool NORM, bool CAP, bool WS>
 hipError_t launch_attn(const StreamArgs& sa, hipStream_t stream) {
   const AttnArgs& a = sa.a;
   const int64_t nrows = (int64_t)a.L * a.G;
   const int nqb = (int)((nrows + ROWS - 1) / ROWS);
-  hipLaunchKernelGGL((prefill_stream_kernel<ROT, NORM, CAP>), dim3(nqb * a.Hkv * a.B), dim3(NT),
-                     0, stream, sa, nqb);
+  hipLaunchKernelGGL((prefill_stream_kernel<ROT, NORM, CAP, WS>), dim3(nqb * a.Hkv * a.B),
+                     dim3(NT), 0, stream, sa, nqb);
   return hipGetLastError();
+}
+template <int ROT, bool NORM, bool CAP>
+hipError_t launch_attn_ws(const StreamArgs& sa, hipStream_t s) {
+  return sa.kprep ? launch_attn<ROT, NORM, CAP, true>(sa, s) : launch_attn<ROT, NORM, CAP, false>(sa, s);
 }
 template <int ROT, bool NORM>
 hipError_t launch_attn_cap(const StreamArgs& sa, hipStream_t s) {
-  return sa.a.softcap > 0.f ? launch_attn<ROT, NORM, true>(sa, s) : launch_attn<ROT, NORM, false>(sa, s);
+  return sa.a.softcap > 0.f ? launch_attn_ws<ROT, NORM, true>(sa, s)
+                            : launch_attn_ws<ROT, NORM, false>(sa, s);
 }
 template <int ROT>
 hipError_t launch_attn_norm(const StreamArgs& sa, hipStream_t s) {
@@ -948,7 +947,24 @@ bool prefill_stream_supported(const AttnArgs& a) {
   return prefill_mfma_supported(a) && ((int64_t)a.S + BN) * a.k_j * 2 < (int64_t)INT32_MAX;
 }
 
-hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t stream) {
+// Keys one workgroup of the eight-wavefront kernel visits on average, taking positions as
+// consecutive: its own query positions plus those below them that it may see -- the window, the
+// visible chunks, or on average half of the causal range.
+static int64_t mean_band_keys(const AttnArgs& a) {
+  const int64_t span = (ROWS + a.G - 1) / a.G;
+  int64_t below = (int64_t)a.n_cached + a.L / 2;
+  if (a.window > 0) below = std::min<int64_t>(below, a.window);
+  if (a.chunk > 0) below = std::min<int64_t>(below, (int64_t)a.chunk * a.chunk_lb + a.chunk / 2);
+  return below + span;
+}
+// Below this many keys per workgroup (24 tiles) the four-wavefront kernel, two workgroups per CU,
+// is faster: the eight-wavefront kernel's longer pipeline start and its one workgroup per CU cost
+// more than its faster loop saves (measured: 0.28 against 0.33 ms for a 128-key window, level at
+// about 1000 keys, 6% slower at 4096).
+constexpr int64_t kShortBandKeys = 24 * BN;
+
+hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t stream,
+                                 StreamKernel which) {
   if (a.B == 0 || a.L == 0) return hipSuccess;
   StreamArgs sa;
   sa.a = a;
@@ -964,6 +980,9 @@ hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t
     if (e != hipSuccess) return e;
     sa.kprep = po.p;
   }
+  if (which == StreamKernel::kShort ||
+      (which == StreamKernel::kAuto && mean_band_keys(a) < kShortBandKeys))
+    return stream::launch_attn_short(sa, stream);
   switch (a.R == 0 ? 0 : (a.style == 0 ? 1 : 2)) {
     case 0: return launch_attn_norm<0>(sa, stream);
     case 1: return launch_attn_norm<1>(sa, stream);

@@ -229,8 +229,8 @@ gqa_status check_cfg(const gqa_attn_cfg* c) {
   if (c->chunk_size < 0 || c->chunk_lookback < 0)
     return fail(GQA_E_SHAPE, "chunk_size and chunk_lookback must be >= 0, got %d, %d",
                 c->chunk_size, c->chunk_lookback);
-  if (c->kernel < GQA_KERNEL_AUTO || c->kernel > GQA_KERNEL_DECODE_LONG)
-    return fail(GQA_E_VALUE, "kernel must be a gqa_kernel_select value in [0, 3], got %d", c->kernel);
+  if (c->kernel < GQA_KERNEL_AUTO || c->kernel > GQA_KERNEL_PREFILL_SHORT)
+    return fail(GQA_E_VALUE, "kernel must be a gqa_kernel_select value in [0, 5], got %d", c->kernel);
   if (c->reserved != 0) return fail(GQA_E_VALUE, "cfg reserved field must be 0");
   return ok();
 }
@@ -396,7 +396,13 @@ gqa_status gqa_attn_prefill(const gqa_attn_cfg* cfg, const void* q, const void* 
   if (prefill_stream_applies(cfg, a)) {
     const size_t need = gqa::prefill_stream_workspace_bytes(a);
     if (need == 0 || (workspace && workspace_bytes >= need))
-      return hip_status(gqa::launch_prefill_stream(a, workspace, stream), "prefill (stream) launch");
+      return hip_status(
+          gqa::launch_prefill_stream(a, workspace, stream,
+                                     cfg->kernel == GQA_KERNEL_PREFILL_LONG ? gqa::StreamKernel::kLong
+                                     : cfg->kernel == GQA_KERNEL_PREFILL_SHORT
+                                         ? gqa::StreamKernel::kShort
+                                         : gqa::StreamKernel::kAuto),
+          "prefill (stream) launch");
     if (workspace)
       return fail(GQA_E_WORKSPACE, "prefill workspace needs %zu bytes, got %zu", need,
                   workspace_bytes);

@@ -28,7 +28,10 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);
 bool prefill_needs_kprep(const AttnArgs& a);
 bool prefill_stream_supported(const AttnArgs& a);
 size_t prefill_stream_workspace_bytes(const AttnArgs& a);
-hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t stream);
+// Which streaming attention kernel runs: chosen from the mean key band per workgroup, or forced.
+enum class StreamKernel { kAuto = 0, kLong = 1, kShort = 2 };
+hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t stream,
+                                 StreamKernel which = StreamKernel::kAuto);
 // The key-preparation pass on its own: rows [n_cached, S) of a.k, normed and rotated, written to
 // k_out with k's layout [B, S, Hkv, D].
 bool prep_keys_supported(const AttnArgs& a);

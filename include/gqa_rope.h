@@ -137,12 +137,20 @@ typedef struct gqa_attn_cfg {
  *   GQA_KERNEL_DECODE_SHORT  decode on the MFMA kernels with 1024-key splits for every walk
  *   GQA_KERNEL_DECODE_LONG   decode on the MFMA kernels with 2048-key splits for every walk
  *                            longer than 1024 keys (AUTO picks between the two by the batch's
- *                            size); for prefill calls the last two act as AUTO */
+ *                            size); for prefill calls the two act as AUTO
+ *   GQA_KERNEL_PREFILL_LONG  bf16 prefill with a workspace on the eight-wavefront streaming
+ *                            kernel (one workgroup per CU, deep tile pipeline)
+ *   GQA_KERNEL_PREFILL_SHORT bf16 prefill with a workspace on the four-wavefront streaming kernel
+ *                            (two workgroups per CU); AUTO picks between the two by the mean
+ *                            number of keys a workgroup visits (below 768: short); without a
+ *                            workspace, and for decode calls, the two act as AUTO */
 typedef enum gqa_kernel_select {
   GQA_KERNEL_AUTO = 0,
   GQA_KERNEL_GENERIC = 1,
   GQA_KERNEL_DECODE_SHORT = 2,
-  GQA_KERNEL_DECODE_LONG = 3
+  GQA_KERNEL_DECODE_LONG = 3,
+  GQA_KERNEL_PREFILL_LONG = 4,
+  GQA_KERNEL_PREFILL_SHORT = 5
 } gqa_kernel_select;
 
 /* Build cos/sin tables for positions 0 .. table_len-1 ([Models] "Scaled RoPE", rope_tables):

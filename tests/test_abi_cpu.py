@@ -74,7 +74,7 @@ def _prefill(c, B=1, L=4, S=4, n_cached=0, window=0, q=FAKE, k=FAKE, v=FAKE, pos
     (dict(sinks=FAKE + 2), 7, "sinks"),
     (dict(chunk_size=-1), 2, "chunk_size"),
     (dict(chunk_size=64, chunk_lookback=-1), 2, "chunk_lookback"),
-    (dict(kernel=4), 7, "kernel"),
+    (dict(kernel=6), 7, "kernel"),
     (dict(kernel=-1), 7, "kernel"),
     (dict(reserved=1), 7, "reserved"),
 ])

@@ -55,11 +55,13 @@ def cfg_of(*args, **kw):
     return g.AttnConfig(*args, **kw)
 
 
-@pytest.fixture(params=["stream", "fused", "generic"])
+@pytest.fixture(params=["stream", "stream_short", "fused", "generic"])
 def policy(request):
-    """Kernel path: stream (key-prep pass + streaming MFMA kernel), fused (MFMA kernel that
-    preps keys on the fly, no workspace), generic (one wave per row, fp32 math)."""
-    PATH["kernel"] = "generic" if request.param == "generic" else "auto"
+    """Kernel path: stream (key-prep pass + the eight-wavefront streaming MFMA kernel),
+    stream_short (key-prep pass + the four-wavefront one), fused (MFMA kernel that preps keys on
+    the fly, no workspace), generic (one wave per row, fp32 math)."""
+    PATH["kernel"] = {"stream": "prefill_long", "stream_short": "prefill_short",
+                      "fused": "auto", "generic": "generic"}[request.param]
     PATH["path"] = request.param
     yield request.param
     PATH["kernel"] = "auto"
