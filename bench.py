@@ -86,6 +86,11 @@ def decode_bytes(wl, lens):
             + 2 * wl.B * wl.Hq * wl.D * eb + 4 * wl.B)
 
 
+# symbol names of the prefill kernels, by gqa_prefill_kernel's answer
+PREFILL_KERNEL_NAMES = {"stream_long": "prefill_stream_kernel", "stream_short": "prefill_short_kernel",
+                        "fused": "prefill_mfma_kernel", "generic": "attn_generic_kernel"}
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` on `workload` from the committed counter runs
     (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE scaled by a known-size copy), or None when
@@ -237,10 +242,13 @@ def prefill_record(wl, steps, warmup, torch, g, graph, cpu, budget_s):
         + ", ".join(f"{k} {v:.4f}" for k, v in parts.items())
         + f") -> step {value:.1f}, attention {achieved:.1f} TFLOP/s")
     if bf16:
-        roof = {"bound": "mfma", "kernel": "prefill_stream_kernel", "achieved": round(achieved, 2),
+        # the kernel the attention call runs (it reads prepared keys: n_cached = S, no workspace)
+        kern = PREFILL_KERNEL_NAMES[g.prefill_kernel(x["cfg"], wl.B, wl.L, wl.S, wl.S, wl.window,
+                                                     workspace=False)]
+        roof = {"bound": "mfma", "kernel": kern, "achieved": round(achieved, 2),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic("prefill_stream_kernel", wl.name),
+                "traffic": measured_traffic(kern, wl.name),
                 "kernel_ms_mean": round(kern_ms, 4), "algorithmic_flop": flops}
     else:
         # 16 query rows: far too small to load any unit of the chip; reported against the fp32

@@ -21,7 +21,8 @@ __all__ = [
     "rope_attention_factor", "rope_softmax_scale",
     "attn_prefill", "attn_decode", "decode_workspace_bytes", "PagedKV", "paged_append",
     "paged_decode_workspace_bytes", "attn_decode_paged", "mla_decode_workspace_bytes",
-    "mla_decode", "prefill_workspace_bytes", "prep_keys", "last_error", "KERNELS",
+    "mla_decode", "prefill_workspace_bytes", "prefill_kernel", "PREFILL_KERNELS", "prep_keys",
+    "last_error", "KERNELS",
     "hip_runtimes_mapped", "attn_decode_noalloc", "DECODE_NOALLOC_MAX_BYTES", "LIB_PATH",
     "EXPORTS",
 ]
@@ -89,6 +90,8 @@ EXPORTS = {
                                       ctypes.POINTER(ctypes.c_double)]),
     "gqa_prep_keys": (_I32, [ctypes.POINTER(_AttnCfg), _P, _P, _I64, _I32, _I32, _I32, _P, _P]),
     "gqa_prefill_workspace_bytes": (_SZ, [ctypes.POINTER(_AttnCfg), _I32, _I32, _I32]),
+    "gqa_prefill_kernel": (_I32, [ctypes.POINTER(_AttnCfg), _I32, _I32, _I32, _I32, _I32, _I32,
+                                  ctypes.POINTER(_I32)]),
     "gqa_attn_prefill": (_I32, [ctypes.POINTER(_AttnCfg), _P, _P, _P, _P, _I64, _P, _I64, _I32,
                                 _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "gqa_decode_workspace_bytes": (_SZ, [ctypes.POINTER(_AttnCfg), _I32, _I32]),
@@ -368,6 +371,19 @@ def prefill_workspace_bytes(cfg: AttnConfig, B: int, S: int, n_cached: int = 0) 
     if n == 0 and err:
         raise GQAError(2, err)
     return int(n)
+
+
+PREFILL_KERNELS = {0: "generic", 1: "fused", 2: "stream_long", 3: "stream_short"}
+
+
+def prefill_kernel(cfg: AttnConfig, B: int, L: int, S: int, n_cached: int = 0, window: int = 0,
+                   workspace: bool = True) -> str:
+    """Name of the kernel gqa_attn_prefill runs for these sizes (host-only query)."""
+    c = cfg.c_struct()
+    which = ctypes.c_int32(-1)
+    _check(library().gqa_prefill_kernel(ctypes.byref(c), int(B), int(L), int(S), int(n_cached),
+                                        int(window), int(bool(workspace)), ctypes.byref(which)))
+    return PREFILL_KERNELS[which.value]
 
 
 def attn_prefill(cfg: AttnConfig, q, k, v, positions, key_positions, n_cached=0, window=0,

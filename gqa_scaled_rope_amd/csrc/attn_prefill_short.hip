@@ -45,7 +45,7 @@ __device__ __forceinline__ int32_t* pbuf() { return BUF == 0 ? g_p0 : BUF == 1 ?
 template <int ROT, bool NORM, bool CAP>
 // Two workgroups per CU (3 x 16 KB tiles of LDS and up to 256 VGPRs each): one's query prep and
 // first tiles overlap the other's loop, and each barrier holds only the four waves of one group.
-__global__ __launch_bounds__(NT, 2) void prefill_stream_kernel(StreamArgs sa, int nqb) {
+__global__ __launch_bounds__(NT, 2) void prefill_short_kernel(StreamArgs sa, int nqb) {
   const AttnArgs& a = sa.a;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -537,7 +537,7 @@ hipError_t launch_attn(const StreamArgs& sa, hipStream_t stream) {
   const AttnArgs& a = sa.a;
   const int64_t nrows = (int64_t)a.L * a.G;
   const int nqb = (int)((nrows + ROWS - 1) / ROWS);
-  hipLaunchKernelGGL((prefill_stream_kernel<ROT, NORM, CAP>), dim3(nqb * a.Hkv * a.B), dim3(NT),
+  hipLaunchKernelGGL((prefill_short_kernel<ROT, NORM, CAP>), dim3(nqb * a.Hkv * a.B), dim3(NT),
                      0, stream, sa, nqb);
   return hipGetLastError();
 }

@@ -948,11 +948,12 @@ bool prefill_stream_supported(const AttnArgs& a) {
 }
 
 // Keys one workgroup of the eight-wavefront kernel visits on average, taking positions as
-// consecutive: its own query positions plus those below them that it may see -- the window, the
-// visible chunks, or on average half of the causal range.
+// consecutive with the queries at the last L of the S key positions (a fresh prefill or a chunk
+// appended to a cache): its own query positions plus those below them that it may see -- the
+// window, the visible chunks, or on average S - L/2 keys of the causal range.
 static int64_t mean_band_keys(const AttnArgs& a) {
   const int64_t span = (ROWS + a.G - 1) / a.G;
-  int64_t below = (int64_t)a.n_cached + a.L / 2;
+  int64_t below = std::max<int64_t>((int64_t)a.S - a.L / 2, 0);
   if (a.window > 0) below = std::min<int64_t>(below, a.window);
   if (a.chunk > 0) below = std::min<int64_t>(below, (int64_t)a.chunk * a.chunk_lb + a.chunk / 2);
   return below + span;
@@ -962,6 +963,11 @@ static int64_t mean_band_keys(const AttnArgs& a) {
 // more than its faster loop saves (measured: 0.28 against 0.33 ms for a 128-key window, level at
 // about 1000 keys, 6% slower at 4096).
 constexpr int64_t kShortBandKeys = 24 * BN;
+
+bool prefill_stream_short(const AttnArgs& a, StreamKernel which) {
+  return which == StreamKernel::kShort ||
+         (which == StreamKernel::kAuto && mean_band_keys(a) < kShortBandKeys);
+}
 
 hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t stream,
                                  StreamKernel which) {
@@ -980,9 +986,7 @@ hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t
     if (e != hipSuccess) return e;
     sa.kprep = po.p;
   }
-  if (which == StreamKernel::kShort ||
-      (which == StreamKernel::kAuto && mean_band_keys(a) < kShortBandKeys))
-    return stream::launch_attn_short(sa, stream);
+  if (prefill_stream_short(a, which)) return stream::launch_attn_short(sa, stream);
   switch (a.R == 0 ? 0 : (a.style == 0 ? 1 : 2)) {
     case 0: return launch_attn_norm<0>(sa, stream);
     case 1: return launch_attn_norm<1>(sa, stream);

@@ -341,6 +341,12 @@ static bool prefill_stream_applies(const gqa_attn_cfg* cfg, const gqa::AttnArgs&
          gqa::prefill_stream_supported(t);
 }
 
+static gqa::StreamKernel stream_kernel(const gqa_attn_cfg* cfg) {
+  return cfg->kernel == GQA_KERNEL_PREFILL_LONG    ? gqa::StreamKernel::kLong
+         : cfg->kernel == GQA_KERNEL_PREFILL_SHORT ? gqa::StreamKernel::kShort
+                                                   : gqa::StreamKernel::kAuto;
+}
+
 size_t gqa_prefill_workspace_bytes(const gqa_attn_cfg* cfg, int32_t B, int32_t S, int32_t n_cached) {
   if (check_cfg(cfg) != GQA_OK) return 0;
   if (B < 0 || S < 0 || n_cached < 0 || n_cached > S) {
@@ -396,13 +402,8 @@ gqa_status gqa_attn_prefill(const gqa_attn_cfg* cfg, const void* q, const void* 
   if (prefill_stream_applies(cfg, a)) {
     const size_t need = gqa::prefill_stream_workspace_bytes(a);
     if (need == 0 || (workspace && workspace_bytes >= need))
-      return hip_status(
-          gqa::launch_prefill_stream(a, workspace, stream,
-                                     cfg->kernel == GQA_KERNEL_PREFILL_LONG ? gqa::StreamKernel::kLong
-                                     : cfg->kernel == GQA_KERNEL_PREFILL_SHORT
-                                         ? gqa::StreamKernel::kShort
-                                         : gqa::StreamKernel::kAuto),
-          "prefill (stream) launch");
+      return hip_status(gqa::launch_prefill_stream(a, workspace, stream, stream_kernel(cfg)),
+                        "prefill (stream) launch");
     if (workspace)
       return fail(GQA_E_WORKSPACE, "prefill workspace needs %zu bytes, got %zu", need,
                   workspace_bytes);
@@ -410,6 +411,33 @@ gqa_status gqa_attn_prefill(const gqa_attn_cfg* cfg, const void* q, const void* 
   if (bf16 && cfg->kernel != GQA_KERNEL_GENERIC && S > 0 && gqa::prefill_mfma_supported(a))
     return hip_status(gqa::launch_prefill_mfma(a, stream), "prefill (fused) launch");
   return hip_status(gqa::launch_attn_generic(a, bf16, stream), "prefill (generic) launch");
+}
+
+gqa_status gqa_prefill_kernel(const gqa_attn_cfg* cfg, int32_t B, int32_t L, int32_t S,
+                              int32_t n_cached, int32_t window, int32_t with_workspace,
+                              int32_t* which) {
+  gqa_status st = check_cfg(cfg);
+  if (st != GQA_OK) return st;
+  if (which == nullptr) return fail(GQA_E_NULL, "which must not be null");
+  if (B < 0 || L < 0 || S < 0 || n_cached < 0 || n_cached > S || window < 0)
+    return fail(GQA_E_SHAPE, "need B, L, S, window >= 0 and 0 <= n_cached <= S, got B=%d L=%d "
+                "S=%d n_cached=%d window=%d", B, L, S, n_cached, window);
+  gqa::AttnArgs a = prefill_args(cfg, B, L, S, n_cached);
+  a.window = window;
+  static const int32_t dummy = 0;  // the support checks look at the position pointers only
+  a.qpos = &dummy;
+  a.kpos = &dummy;
+  const bool bf16 = cfg->dtype == GQA_BF16;
+  if (prefill_stream_applies(cfg, a) &&
+      (gqa::prefill_stream_workspace_bytes(a) == 0 || with_workspace)) {
+    *which = gqa::prefill_stream_short(a, stream_kernel(cfg)) ? GQA_PREFILL_STREAM_SHORT
+                                                              : GQA_PREFILL_STREAM_LONG;
+  } else if (bf16 && cfg->kernel != GQA_KERNEL_GENERIC && S > 0 && gqa::prefill_mfma_supported(a)) {
+    *which = GQA_PREFILL_FUSED;
+  } else {
+    *which = GQA_PREFILL_GENERIC;
+  }
+  return ok();
 }
 
 gqa_status gqa_prep_keys(const gqa_attn_cfg* cfg, const void* k, const int32_t* key_positions,

@@ -32,6 +32,8 @@ size_t prefill_stream_workspace_bytes(const AttnArgs& a);
 enum class StreamKernel { kAuto = 0, kLong = 1, kShort = 2 };
 hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t stream,
                                  StreamKernel which = StreamKernel::kAuto);
+// True when launch_prefill_stream runs the four-wavefront kernel for this call.
+bool prefill_stream_short(const AttnArgs& a, StreamKernel which);
 // The key-preparation pass on its own: rows [n_cached, S) of a.k, normed and rotated, written to
 // k_out with k's layout [B, S, Hkv, D].
 bool prep_keys_supported(const AttnArgs& a);

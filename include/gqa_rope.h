@@ -192,6 +192,20 @@ gqa_status gqa_prep_keys(const gqa_attn_cfg* cfg, const void* k, const int32_t* 
  * Returns 0 and sets the error on invalid arguments. */
 size_t gqa_prefill_workspace_bytes(const gqa_attn_cfg* cfg, int32_t B, int32_t S, int32_t n_cached);
 
+/* Which kernel a gqa_attn_prefill call with these sizes runs (host-only, no device work), for
+ * tools that label measurements: with_workspace != 0 means a workspace of at least
+ * gqa_prefill_workspace_bytes() bytes is passed.  *which (host int32) receives a
+ * gqa_prefill_kernel_id.  Errors as gqa_attn_prefill's argument checks. */
+typedef enum gqa_prefill_kernel_id {
+  GQA_PREFILL_GENERIC = 0,       /* one wavefront per query row and head, fp32 arithmetic */
+  GQA_PREFILL_FUSED = 1,         /* MFMA kernel preparing new keys on the fly (no workspace) */
+  GQA_PREFILL_STREAM_LONG = 2,   /* key-preparation pass + eight-wavefront streaming kernel */
+  GQA_PREFILL_STREAM_SHORT = 3   /* key-preparation pass + four-wavefront streaming kernel */
+} gqa_prefill_kernel_id;
+gqa_status gqa_prefill_kernel(const gqa_attn_cfg* cfg, int32_t B, int32_t L, int32_t S,
+                              int32_t n_cached, int32_t window, int32_t with_workspace,
+                              int32_t* which);
+
 /* Causal prefill ([Models] "What differs between model families", DecoderAttention.forward;
  * [Guide] section 3.4 "Attention").
  *   q   device [B, L, Hq, D]  new queries (contiguous)

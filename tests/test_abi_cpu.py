@@ -271,6 +271,40 @@ def test_kernel_choice_is_per_call():
     assert lib.gqa_prefill_workspace_bytes(ctypes.byref(_cfg(kernel=1, **cr)), 2, 300, 100) == 0
 
 
+def _prefill_kernel(c, B, L, S, n_cached=0, window=0, ws=1):
+    which = ctypes.c_int32(-1)
+    assert lib.gqa_prefill_kernel(ctypes.byref(c), B, L, S, n_cached, window, ws,
+                                  ctypes.byref(which)) == 0, g.last_error()
+    return g.PREFILL_KERNELS[which.value]
+
+
+def test_prefill_kernel_choice():
+    # the benchmark prefill shapes: long key bands on the eight-wavefront streaming kernel, the
+    # 128-key window (about 160 keys per workgroup) on the four-wavefront one
+    from synth import WORKLOADS
+    want = {"qwen3_prefill_bf16": "stream_long", "mistral_swa_prefill_bf16": "stream_long",
+            "chunked_prefill_bf16_w4096": "stream_long", "chunked_prefill_bf16_full": "stream_long",
+            "sinks_swa128_prefill_bf16": "stream_short"}
+    for name, kern in want.items():
+        wl = WORKLOADS[name]
+        c = _cfg(num_q_heads=wl.Hq, num_kv_heads=wl.Hkv, rotary_dim=wl.rotary_dim,
+                 rot_style=0 if wl.style == "half" else 1, cos_table=FAKE, sin_table=FAKE,
+                 table_len=8, qk_norm=int(wl.qk_norm), q_norm_w=FAKE if wl.qk_norm else None,
+                 k_norm_w=FAKE if wl.qk_norm else None)
+        assert _prefill_kernel(c, wl.B, wl.L, wl.S, wl.n_cached, wl.window) == kern, name
+    cr = dict(rotary_dim=128, cos_table=FAKE, sin_table=FAKE, table_len=8)
+    # forced either way; without a workspace the fused kernel; generic and fp32 on generic
+    assert _prefill_kernel(_cfg(kernel=5, **cr), 2, 8192, 8192, 0, 4096) == "stream_short"
+    assert _prefill_kernel(_cfg(kernel=4, **cr), 4, 4096, 4096, 0, 128) == "stream_long"
+    assert _prefill_kernel(_cfg(**cr), 2, 8192, 8192, 0, 4096, ws=0) == "fused"
+    assert _prefill_kernel(_cfg(kernel=1, **cr), 2, 8192, 8192, 0, 4096) == "generic"
+    assert _prefill_kernel(_cfg(dtype=0, **cr), 2, 64, 64) == "generic"
+    # nothing to prepare (no rotation, no norm): the stream kernels need no workspace
+    assert _prefill_kernel(_cfg(), 2, 8192, 8192, 0, 0, ws=0) == "stream_long"
+    which = ctypes.c_int32(-1)
+    assert lib.gqa_prefill_kernel(ctypes.byref(_cfg()), 1, 4, 4, 5, 0, 1, ctypes.byref(which)) == 2
+
+
 def test_second_hip_runtime_is_detected():
     # two different libamdhip64 files mapped into one process is the state in which torch's
     # streams are invalid for the library; the loader refuses it
