@@ -147,8 +147,12 @@ def _prefill_setup(wl, torch, g):
                        wl.qk_norm, wl.eps, qw, kw, 0.0, wl.softcap, **_mask_cfg(wl, torch))
     out = torch.empty_like(q)
     kcache = k.clone()   # rows < n_cached: the cache as stored; the rest is rewritten each step
+    # the attention call's workspace (its keys are prepared: n_cached = S), allocated once: room
+    # for the split key walks of a last, partial round of query blocks
+    nws = g.prefill_workspace_bytes(cfg, wl.B, wl.S, wl.S) if wl.dtype == "bf16" else 0
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
     return dict(q=q, k=k, v=v, qw=qw, kw=kw, pos=pos, kpos=kpos, cos=cos, sin=sin, cfg=cfg,
-                out=out, table_len=table_len, kcache=kcache)
+                out=out, table_len=table_len, kcache=kcache, ws=ws)
 
 
 def _time_calls(fn, n, torch):
@@ -183,7 +187,7 @@ def run_prefill(wl, steps, warmup, torch, g, graph=True):
     def attention():
         if bf16:
             g.attn_prefill(x["cfg"], x["q"], x["kcache"], x["v"], x["pos"], x["kpos"], wl.S,
-                           wl.window, x["out"], workspace=None)
+                           wl.window, x["out"], workspace=x["ws"])
         else:
             g.attn_prefill(x["cfg"], x["q"], x["k"], x["v"], x["pos"], x["kpos"], wl.n_cached,
                            wl.window, x["out"], workspace=None)
@@ -242,9 +246,9 @@ def prefill_record(wl, steps, warmup, torch, g, graph, cpu, budget_s):
         + ", ".join(f"{k} {v:.4f}" for k, v in parts.items())
         + f") -> step {value:.1f}, attention {achieved:.1f} TFLOP/s")
     if bf16:
-        # the kernel the attention call runs (it reads prepared keys: n_cached = S, no workspace)
+        # the kernel the attention call runs (it reads prepared keys: n_cached = S)
         kern = PREFILL_KERNEL_NAMES[g.prefill_kernel(x["cfg"], wl.B, wl.L, wl.S, wl.S, wl.window,
-                                                     workspace=False)]
+                                                     workspace=True)]
         roof = {"bound": "mfma", "kernel": kern, "achieved": round(achieved, 2),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),

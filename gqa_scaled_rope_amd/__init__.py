@@ -391,8 +391,9 @@ def attn_prefill(cfg: AttnConfig, q, k, v, positions, key_positions, n_cached=0,
     """q [B, L, Hq, D], k/v [B, S, Hkv, D], positions [B, L] or [L], key_positions [B, S] or [S]
     (int32, nondecreasing).  Returns out [B, L, Hq, D].
 
-    workspace: "auto" allocates the key-preparation workspace when the streaming kernel can use
-    it; None selects the fused kernel (no workspace); or a uint8 device tensor."""
+    workspace: "auto" allocates gqa_prefill_workspace_bytes (prepared keys and room for split
+    key walks) when the streaming kernels apply; None runs without one (the fused kernel when
+    keys need preparing); or a uint8 device tensor."""
     torch = _torch()
     B, L, Hq, D = q.shape
     S = k.shape[1]

@@ -19,6 +19,7 @@
 //     1 KB of LDS in lane order; choosing the source chunk per lane produces the XOR-swizzled
 //     layout the MFMA operand reads want.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "stream_tiles.hpp"
@@ -282,6 +283,38 @@ __device__ __forceinline__ void barrier_after_loads() {
   phase_barrier();
 }
 
+// Query block, KV head and sequence of work item L.  Workgroups are dealt to the 8 XCDs
+// round-robin by id; items are numbered so that every query block of one (b, g) lands on the
+// same XCD (its K/V then stay in that XCD's L2), heaviest (latest) query blocks first.
+struct WorkItem {
+  int qb, g, b;
+};
+__device__ __forceinline__ WorkItem work_item(const AttnArgs& a, int L, int nqb) {
+  const int npairs = a.B * a.Hkv;
+  int pair, rank;
+  if (npairs % kXcds == 0) {
+    const int per = npairs / kXcds;
+    const int x = L % kXcds, k = L / kXcds;
+    pair = x + kXcds * (k % per);
+    rank = k / per;
+  } else {
+    pair = L % npairs;
+    rank = L / npairs;
+  }
+  return WorkItem{nqb - 1 - rank, pair % a.Hkv, pair / a.Hkv};
+}
+
+// Split key walks.  When the query blocks leave a last, partial round of the GPU (R items over
+// C CUs, 2R <= C), each of those R items is walked by two workgroups, one per half of its key
+// tiles; each writes its partial (O relative to its reference m, m, and each lane's share of the
+// row sum) to the workspace and prefill_split_combine_kernel merges the two ([Guide] 3.4's
+// softmax is a ratio of sums, so halves merge exactly up to rounding).  A partial is kept
+// thread-major: value v of thread t at v * NT + t.
+constexpr int kSplitMax = 128;                         // items that may be split
+constexpr int kPartialVals = 66;                       // 64 of O, m, the lane's sum
+constexpr size_t kPartialFloats = (size_t)kPartialVals * NT;
+constexpr size_t kSplitBytes = (size_t)kSplitMax * 2 * kPartialFloats * sizeof(float);
+
 template <int ROT, bool NORM, bool CAP, bool WS>
 __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, int nqb) {
   const AttnArgs& a = sa.a;
@@ -290,27 +323,15 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = w >> 2;  // 0: matrix phase first; 1: one phase later
   const int ql = lane & 31, hg = lane >> 5;
-  // Work item of this workgroup.  Workgroups are dealt to the 8 XCDs round-robin by id; map ids
-  // so that every query block of one (b, g) lands on the same XCD (its K/V then stay in that
-  // XCD's L2), heaviest (latest) query blocks first within each XCD.
-  int qb, g, b;
-  {
-    const int L = blockIdx.x;
-    const int npairs = a.B * a.Hkv;
-    int pair, rank;
-    if (npairs % kXcds == 0) {
-      const int per = npairs / kXcds;
-      const int x = L % kXcds, k = L / kXcds;
-      pair = x + kXcds * (k % per);
-      rank = k / per;
-    } else {
-      pair = L % npairs;
-      rank = L / npairs;
-    }
-    qb = nqb - 1 - rank;
-    b = pair / a.Hkv;
-    g = pair % a.Hkv;
+  // Work item of this workgroup; past the first nfull workgroups, two per item, one per half of
+  // its key tiles (half 0 or 1; -1: the whole walk).
+  int item = blockIdx.x, half = -1;
+  if (item >= sa.nfull) {
+    half = (item - sa.nfull) & 1;
+    item = sa.nfull + ((item - sa.nfull) >> 1);
   }
+  const WorkItem wi = work_item(a, item, nqb);
+  const int qb = wi.qb, g = wi.g, b = wi.b;
   const int G = a.G;
   const int64_t nrows = (int64_t)a.L * G;
   const int64_t f0 = (int64_t)qb * ROWS;
@@ -323,6 +344,19 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   const int32_t* qpos_b = a.qpos + (int64_t)b * a.qpos_b;
   const int32_t qp_raw = qpos_b[qi];  // qi is a valid index even for rows past the end
   const int32_t qp = qvalid ? qp_raw : 0;
+  // The row's query features (and the norm weights) do not depend on any position: their loads
+  // go out now, beside the position loads, and land while the band is worked out.
+  u32x4 xw[8], ww[8];
+  {
+    const uint16_t* qrow = (const uint16_t*)a.q + (int64_t)b * a.q_b + (int64_t)qi * a.q_i +
+                           (int64_t)qh * a.q_h + 8 * hg;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) xw[s] = ld16(qrow + 16 * s);
+    if (NORM) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) ww[s] = ld16((const uint16_t*)a.qw + 16 * s + 8 * hg);
+    }
+  }
 
   // ---- key band of the workgroup's query positions (loads issued here, used after Q prep) ----
   const int32_t* kpos_b = a.kpos + (int64_t)b * a.kpos_b;
@@ -405,7 +439,11 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   const int g_lo = (int)min<int64_t>(max<int64_t>(x_lo - kp0, 0), a.S);
   // The first tile's loads go out now -- at key 0 without a window or chunks, else at the guessed
   // band start (loaded again below if the guess is wrong) -- beside the band and query-prep loads.
-  const int j_first = a.has_floor() ? g_lo : 0;
+  int j_first = a.has_floor() ? g_lo : 0;
+  if (half == 1) {  // the second half starts after the first ceil(n/2) tiles of the guessed band
+    const int gt = (max(g_hi, j_first) - j_first + BN - 1) / BN;
+    j_first += ((gt + 1) >> 1) * BN;
+  }
   __builtin_amdgcn_sched_barrier(0);
   issue_tile(j_first, true, std::integral_constant<int, 0>());
   const int32_t hi_l = kpos_b[max(g_hi - 1, 0)], hi_r = kpos_b[min(g_hi, a.S - 1)];
@@ -424,15 +462,6 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   // Interleaved pairs are adjacent.
   bf16x8 qop[8];
   {
-    const uint16_t* qrow = (const uint16_t*)a.q + (int64_t)b * a.q_b + (int64_t)qi * a.q_i +
-                           (int64_t)qh * a.q_h + 8 * hg;
-    u32x4 xw[8], ww[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) xw[s] = ld16(qrow + 16 * s);
-    if (NORM) {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) ww[s] = ld16((const uint16_t*)a.qw + 16 * s + 8 * hg);
-    }
     const int P = a.R >> 4;  // half-split: partner distance in 8-feature chunks
     const int halfp = a.R >> 1;
     const int64_t tp = min<int64_t>(max<int64_t>(qp, 0), a.table_len - 1);
@@ -543,7 +572,20 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   int j_hi = ok_hi ? g_hi : wave_lower_bound(kpos_b, a.S, x_hi);
   int j_lo = !a.has_floor() ? 0 : ok_lo ? g_lo : wave_lower_bound(kpos_b, a.S, x_lo);
   j_lo = min(j_lo, j_hi);
-  const int n_tiles = (j_hi - j_lo + BN - 1) / BN;
+  int n_tiles = (j_hi - j_lo + BN - 1) / BN;
+  if (half >= 0) {  // this workgroup's half of the walk
+    const int n0 = (n_tiles + 1) >> 1;
+    if (half == 0) {
+      n_tiles = n0;
+    } else {
+      j_lo += n0 * BN;
+      n_tiles -= n0;
+    }
+  }
+  // first key index past this walk: the band's end, or the first half's last tile.  The loop
+  // scores one tile past its walk (its weights are never used against V); key indices from j_end
+  // on are masked, so that tile adds nothing to the row sums.
+  const int j_end = min(j_hi, j_lo + n_tiles * BN);
 
   f32x16 o[4];
 #pragma unroll
@@ -629,10 +671,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   auto tile_full = [&](int jt, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     const int32_t kfirst = g_lds.kp[buf][0][0], klast = g_lds.kp[buf][0][BN - 1];
-    return (jt + BN <= j_hi) & (klast <= qmin32) & (kfirst >= floor_max);
+    return (jt + BN <= j_end) & (klast <= qmin32) & (kfirst >= floor_max);
   };
   // Softmax of the freshly computed scores of the tile at key jt (buffer buf): soft-cap, mask
-  // (allowed <=> key index < j_hi and qlo32 <= key position <= qp32), row max, rare rescale,
+  // (allowed <=> key index < j_end and qlo32 <= key position <= qp32), row max, rare rescale,
   // exp2, bf16 weights P into pw and the row sum of those weights.
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   auto softmax = [&](int jt, auto bufc, bool full) __attribute__((always_inline)) {
@@ -651,7 +693,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
         const i32x4 k4 = *(const i32x4*)(g_lds.kp[buf][0] + idx0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool ok = jt + idx0 + e < j_hi && k4[e] <= qp32 && k4[e] >= qlo32;
+          const bool ok = jt + idx0 + e < j_end && k4[e] <= qp32 && k4[e] >= qlo32;
           if (!ok) sc[4 * gq + e] = -INFINITY;
         }
       }
@@ -713,7 +755,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     const int32_t kfirst = g_lds.kp[b1][0][0], klast = g_lds.kp[b1][0][BN - 1];
     pv(b0c);
     sc = qk(b1c, CAP ? zero16 : tmpl);
-    full1 = (jt1 + BN <= j_hi) & (__builtin_amdgcn_readfirstlane(klast) <= qmin32) &
+    full1 = (jt1 + BN <= j_end) & (__builtin_amdgcn_readfirstlane(klast) <= qmin32) &
             (__builtin_amdgcn_readfirstlane(kfirst) >= floor_max);
     __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);     // V operands of P V 0-3, positions
 #pragma unroll
@@ -789,6 +831,16 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   if (grp == 0) phase_barrier();
   // every wavefront's loads retire before the workgroup ends (the last ones were out of range)
   asm volatile("s_waitcnt vmcnt(0)");
+  if (half >= 0) {
+    float* pp = sa.part + ((size_t)(item - sa.nfull) * 2 + half) * kPartialFloats + tid;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pp[(size_t)(db * 16 + r) * NT] = o[db][r];
+    pp[(size_t)64 * NT] = m;
+    pp[(size_t)65 * NT] = lsum;
+    return;
+  }
 
   const float ltot = lsum + swap_halves(lsum);
   // a learned sink joins the denominator only (log2 units, relative to the running max m, which
@@ -812,13 +864,56 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   }
 }
 
+// Merge of a split item's two partials (one workgroup per split item, the attention kernel's
+// thread layout): O = O0 2^(m0-m) + O1 2^(m1-m), likewise the sums, m = max(m0, m1); a half that
+// saw no allowed key (m = kNegBig) contributes nothing.  Then the same normalisation, sink and
+// bf16 output as the attention kernel's epilogue.
+__global__ __launch_bounds__(NT) void prefill_split_combine_kernel(StreamArgs sa, int nqb) {
+  const AttnArgs& a = sa.a;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int ql = lane & 31, hg = lane >> 5;
+  const WorkItem wi = work_item(a, sa.nfull + blockIdx.x, nqb);
+  const int64_t f = (int64_t)wi.qb * ROWS + WROWS * w + ql;
+  const bool qvalid = f < (int64_t)a.L * a.G;
+  const float* p0 = sa.part + (size_t)blockIdx.x * 2 * kPartialFloats + tid;
+  const float* p1 = p0 + kPartialFloats;
+  const float m0 = p0[(size_t)64 * NT], m1 = p1[(size_t)64 * NT];
+  const float mm = fmaxf(m0, m1);
+  const float a0 = m0 == kNegBig ? 0.f : fast_exp2(m0 - mm);
+  const float a1 = m1 == kNegBig ? 0.f : fast_exp2(m1 - mm);
+  const float lsum = p0[(size_t)65 * NT] * a0 + p1[(size_t)65 * NT] * a1;
+  const float ltot = lsum + swap_halves(lsum);
+  if (!qvalid) return;
+  const int qi = (int)(f / a.G);
+  const int qh = wi.g * a.G + (int)(f % a.G);
+  const float lden =
+      (a.sinks != nullptr && ltot > 0.f) ? ltot + fast_exp2(a.sinks[qh] * kLog2e - mm) : ltot;
+  const float inv = ltot > 0.f ? 1.0f / lden : 0.f;
+  uint16_t* orow = (uint16_t*)a.out + (int64_t)wi.b * a.o_b + (int64_t)qi * a.o_i +
+                   (int64_t)qh * a.o_h;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d = db * 32 + 8 * rq + 4 * hg;
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const size_t v = (size_t)(db * 16 + 4 * rq + e) * NT;
+        x[e] = (p0[v] * a0 + p1[v] * a1) * inv;
+      }
+      u32x2 w2;
+      w2[0] = pack_bf16x2(x[0], x[1]);
+      w2[1] = pack_bf16x2(x[2], x[3]);
+      *(u32x2*)(orow + d) = w2;
+    }
+}
+
 template <int ROT, bool NORM, bool CAP, bool WS>
 hipError_t launch_attn(const StreamArgs& sa, hipStream_t stream) {
-  const AttnArgs& a = sa.a;
-  const int64_t nrows = (int64_t)a.L * a.G;
-  const int nqb = (int)((nrows + ROWS - 1) / ROWS);
-  hipLaunchKernelGGL((prefill_stream_kernel<ROT, NORM, CAP, WS>), dim3(nqb * a.Hkv * a.B),
-                     dim3(NT), 0, stream, sa, nqb);
+  hipLaunchKernelGGL((prefill_stream_kernel<ROT, NORM, CAP, WS>), dim3(sa.grid), dim3(NT), 0,
+                     stream, sa, sa.nqb);
   return hipGetLastError();
 }
 template <int ROT, bool NORM, bool CAP>
@@ -937,9 +1032,28 @@ bool prefill_needs_kprep(const AttnArgs& a) { return (a.qk_norm || a.R > 0) && a
 // workspace and every tile reads one source.
 static int kprep_first_row(const AttnArgs& a) { return a.n_cached > BN - 1 ? a.n_cached - (BN - 1) : 0; }
 
-size_t prefill_stream_workspace_bytes(const AttnArgs& a) {
+size_t prefill_stream_required_bytes(const AttnArgs& a) {
   if (!prefill_needs_kprep(a)) return 0;
   return (size_t)a.B * (a.S - kprep_first_row(a)) * a.Hkv * HD * sizeof(uint16_t);
+}
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+size_t prefill_stream_workspace_bytes(const AttnArgs& a) {
+  return align256(prefill_stream_required_bytes(a)) + kSplitBytes;
+}
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 bool prefill_stream_supported(const AttnArgs& a) {
@@ -969,12 +1083,13 @@ bool prefill_stream_short(const AttnArgs& a, StreamKernel which) {
          (which == StreamKernel::kAuto && mean_band_keys(a) < kShortBandKeys);
 }
 
-hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t stream,
-                                 StreamKernel which) {
+hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream, StreamKernel which) {
   if (a.B == 0 || a.L == 0) return hipSuccess;
   StreamArgs sa;
   sa.a = a;
   sa.kprep = nullptr;
+  sa.part = nullptr;
   if (prefill_needs_kprep(a)) {
     PrepOut po;
     po.p = (uint16_t*)workspace;
@@ -987,11 +1102,28 @@ hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t
     sa.kprep = po.p;
   }
   if (prefill_stream_short(a, which)) return stream::launch_attn_short(sa, stream);
+  // a last, partial round of query blocks has its key walks split when the workspace has room
+  const int64_t nrows = (int64_t)a.L * a.G;
+  const int nqb = (int)((nrows + ROWS - 1) / ROWS);
+  const int64_t items = (int64_t)nqb * a.Hkv * a.B;
+  const int cus = device_cus();
+  const int64_t rest = items % cus;
+  const bool split = workspace != nullptr && workspace_bytes >= prefill_stream_workspace_bytes(a) &&
+                     rest > 0 && 2 * rest <= cus && rest <= kSplitMax;
+  sa.nqb = nqb;
+  sa.nfull = (int)(split ? items - rest : items);
+  sa.grid = (int)(split ? items + rest : items);
+  if (split) sa.part = (float*)((char*)workspace + align256(prefill_stream_required_bytes(a)));
+  hipError_t e;
   switch (a.R == 0 ? 0 : (a.style == 0 ? 1 : 2)) {
-    case 0: return launch_attn_norm<0>(sa, stream);
-    case 1: return launch_attn_norm<1>(sa, stream);
-    default: return launch_attn_norm<2>(sa, stream);
+    case 0: e = launch_attn_norm<0>(sa, stream); break;
+    case 1: e = launch_attn_norm<1>(sa, stream); break;
+    default: e = launch_attn_norm<2>(sa, stream); break;
   }
+  if (e != hipSuccess || !split) return e;
+  hipLaunchKernelGGL(prefill_split_combine_kernel, dim3((unsigned)rest), dim3(NT), 0, stream, sa,
+                     nqb);
+  return hipGetLastError();
 }
 
 }  // namespace gqa

@@ -400,9 +400,10 @@ gqa_status gqa_attn_prefill(const gqa_attn_cfg* cfg, const void* q, const void* 
   a.window = window;
   const bool bf16 = cfg->dtype == GQA_BF16;
   if (prefill_stream_applies(cfg, a)) {
-    const size_t need = gqa::prefill_stream_workspace_bytes(a);
+    const size_t need = gqa::prefill_stream_required_bytes(a);
     if (need == 0 || (workspace && workspace_bytes >= need))
-      return hip_status(gqa::launch_prefill_stream(a, workspace, stream, stream_kernel(cfg)),
+      return hip_status(gqa::launch_prefill_stream(a, workspace, workspace ? workspace_bytes : 0,
+                                                   stream, stream_kernel(cfg)),
                         "prefill (stream) launch");
     if (workspace)
       return fail(GQA_E_WORKSPACE, "prefill workspace needs %zu bytes, got %zu", need,
@@ -429,7 +430,7 @@ gqa_status gqa_prefill_kernel(const gqa_attn_cfg* cfg, int32_t B, int32_t L, int
   a.kpos = &dummy;
   const bool bf16 = cfg->dtype == GQA_BF16;
   if (prefill_stream_applies(cfg, a) &&
-      (gqa::prefill_stream_workspace_bytes(a) == 0 || with_workspace)) {
+      (gqa::prefill_stream_required_bytes(a) == 0 || with_workspace)) {
     *which = gqa::prefill_stream_short(a, stream_kernel(cfg)) ? GQA_PREFILL_STREAM_SHORT
                                                               : GQA_PREFILL_STREAM_LONG;
   } else if (bf16 && cfg->kernel != GQA_KERNEL_GENERIC && S > 0 && gqa::prefill_mfma_supported(a)) {

@@ -28,10 +28,14 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);
 bool prefill_needs_kprep(const AttnArgs& a);
 bool prefill_stream_supported(const AttnArgs& a);
 size_t prefill_stream_workspace_bytes(const AttnArgs& a);
+size_t prefill_stream_required_bytes(const AttnArgs& a);
 // Which streaming attention kernel runs: chosen from the mean key band per workgroup, or forced.
 enum class StreamKernel { kAuto = 0, kLong = 1, kShort = 2 };
-hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, hipStream_t stream,
-                                 StreamKernel which = StreamKernel::kAuto);
+// workspace: the prepared keys (prefill_stream_required_bytes; required when keys need
+// preparing), then room for split partials (the rest of prefill_stream_workspace_bytes; used when
+// present).
+hipError_t launch_prefill_stream(const AttnArgs& a, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream, StreamKernel which = StreamKernel::kAuto);
 // True when launch_prefill_stream runs the four-wavefront kernel for this call.
 bool prefill_stream_short(const AttnArgs& a, StreamKernel which);
 // The key-preparation pass on its own: rows [n_cached, S) of a.k, normed and rotated, written to

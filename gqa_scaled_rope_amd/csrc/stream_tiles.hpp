@@ -116,6 +116,10 @@ struct StreamArgs {
   AttnArgs a;
   const uint16_t* kprep;   // [B, S - w0, Hkv, D] keys from row w0 = max(n_cached - (BN-1), 0) on,
                            // new ones prepared (null if nothing needs preparing)
+  float* part;             // split partials (eight-wavefront kernel; null: no item is split)
+  int32_t nqb;             // query blocks per (b, g)
+  int32_t nfull;           // items walked whole; workgroups past them take half an item each
+  int32_t grid;            // workgroups of the launch
 };
 
 // The four-wavefront kernel over the same prepared keys (attn_prefill_short.hip).

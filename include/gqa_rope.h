@@ -187,9 +187,13 @@ gqa_status gqa_prep_keys(const gqa_attn_cfg* cfg, const void* k, const int32_t* 
                          int64_t kpos_batch_stride, int32_t B, int32_t S, int32_t n_cached,
                          void* k_out, hipStream_t stream);
 
-/* Bytes of device workspace that lets gqa_attn_prefill prepare the new keys once instead of in
- * every key tile (0 when nothing needs preparing: no norm and no rotation, or n_cached == S).
- * Returns 0 and sets the error on invalid arguments. */
+/* Bytes of device workspace for gqa_attn_prefill's streaming kernels (0 where they do not apply:
+ * fp32, the generic kernel, shapes the MFMA kernels do not cover).  It holds (1) the new keys,
+ * normed and rotated once instead of in every key tile -- needed whenever some key must be
+ * prepared (a norm or a rotation, and n_cached < S) -- and (2) about 35 MB into which, when the
+ * query blocks leave a last, partial round of the GPU, those blocks' key walks are split over
+ * two workgroups each and their partial results merged.  Returns 0 and sets the error on
+ * invalid arguments. */
 size_t gqa_prefill_workspace_bytes(const gqa_attn_cfg* cfg, int32_t B, int32_t S, int32_t n_cached);
 
 /* Which kernel a gqa_attn_prefill call with these sizes runs (host-only, no device work), for
@@ -217,12 +221,15 @@ gqa_status gqa_prefill_kernel(const gqa_attn_cfg* cfg, int32_t B, int32_t L, int
  *   window         0 = full causal; w > 0: a query at position p sees keys at positions
  *                  p-w+1 .. p ([Models] "Sliding windows": keys more than w-1 back are masked)
  *   out  device [B, L, Hq, D] (contiguous, caller-owned), never aliasing the inputs.
- *   workspace  optional device scratch of >= gqa_prefill_workspace_bytes() bytes, 256-byte
- *              aligned, caller-owned, contents ignored: the new keys are normed and rotated once
- *              into it (one pass) and the attention kernel streams them.  Null (with 0 bytes)
- *              selects the fused kernel, which normalises and rotates new keys on the fly; both
- *              give the same result up to rounding order.  Calls sharing a workspace must be
- *              ordered on one stream.
+ *   workspace  optional device scratch, 256-byte aligned, caller-owned, contents ignored.  With
+ *              gqa_prefill_workspace_bytes() bytes the streaming kernels run: the new keys are
+ *              normed and rotated once into it (one pass) and, when the query blocks leave a
+ *              last, partial round of the GPU, those blocks' key walks are split in two and
+ *              merged through it.  A smaller workspace that still holds the prepared keys runs
+ *              them without the split (GQA_E_WORKSPACE when it does not).  Null: the streaming
+ *              kernels when no key needs preparing, else the fused kernel, which normalises and
+ *              rotates new keys on the fly.  All give the same result up to rounding order.
+ *              Calls sharing a workspace must be ordered on one stream.
  * Result per (b, i, h): softmax over allowed keys of scale*<q', k'> (soft-capped if set), times
  * v; a row with no allowed key is 0.  B, L, S >= 0 (an empty problem is a no-op); n_cached in
  * [0, S]. */

@@ -102,11 +102,16 @@ def test_prefill_rejects_bad_sizes_and_pointers():
     assert _prefill(c, ws=FAKE + 16, ws_bytes=1 << 20) == 5
     cr = _cfg(rotary_dim=128, cos_table=FAKE, sin_table=FAKE, table_len=8)
     need = lib.gqa_prefill_workspace_bytes(ctypes.byref(cr), 2, 300, 100)
-    # new keys plus the last 31 cached rows (so that a 32-key tile reads one source), bf16
-    assert need == 2 * (200 + 31) * 8 * 128 * 2
-    assert _prefill(cr, B=2, L=300, S=300, n_cached=100, ws=FAKE, ws_bytes=need - 2) == 5
-    assert lib.gqa_prefill_workspace_bytes(ctypes.byref(cr), 2, 300, 300) == 0  # all cached
-    assert lib.gqa_prefill_workspace_bytes(ctypes.byref(_cfg()), 2, 300, 0) == 0  # nothing to prep
+    # new keys plus the last 31 cached rows (so that a 32-key tile reads one source), bf16,
+    # rounded up to 256 bytes; then room for split partials: 128 query blocks x 2 halves x 66
+    # values x 512 threads x 4 bytes
+    keys = 2 * (200 + 31) * 8 * 128 * 2
+    split = 128 * 2 * 66 * 512 * 4
+    assert need == (keys + 255) // 256 * 256 + split
+    # too small for the prepared keys: refused (a size between the two would run, unsplit)
+    assert _prefill(cr, B=2, L=300, S=300, n_cached=100, ws=FAKE, ws_bytes=keys - 2) == 5
+    assert lib.gqa_prefill_workspace_bytes(ctypes.byref(cr), 2, 300, 300) == split  # all cached
+    assert lib.gqa_prefill_workspace_bytes(ctypes.byref(_cfg()), 2, 300, 0) == split  # no prep
     assert lib.gqa_prefill_workspace_bytes(ctypes.byref(cr), 2, 300, 301) == 0
     assert "n_cached" in g.last_error()
 

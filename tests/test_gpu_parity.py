@@ -191,6 +191,47 @@ def test_prefill_variants(name, policy):
     check(gpu_prefill(wl, x), ref_prefill(wl, x))
 
 
+# room the workspace keeps for the split key walks of a last, partial round of query blocks:
+# 128 query blocks x 2 halves x 66 values x 512 threads x 4 bytes
+SPLIT_BYTES = 128 * 2 * 66 * 512 * 4
+
+
+@pytest.mark.parametrize("name", ["qknorm_half128", "sinks_interleaved_cap_cached",
+                                  "chunk50_lookback1_sinks"])
+def test_split_walk_matches_whole_walk(name):
+    # 20-30 query blocks on a 256-CU GPU: with the full workspace every block's key walk is split
+    # over two workgroups and merged; with only the prepared keys' room (or none) each block is
+    # walked whole.  Both must match the oracle and each other up to rounding.
+    wl = VARIANTS[name]
+    say("split against whole walks", name)
+    x = prefill_inputs(wl, seed=zlib.crc32(name.encode()) % 1000)
+    PATH["kernel"] = "prefill_long"
+    try:
+        split = gpu_prefill(wl, x)
+        dt = tdt(wl)
+        tl = int(max(x["positions"].max(), x["key_positions"].max())) + 1
+        cos, sin = g.rope_tables(spec(wl), tl) if wl.rotary_dim else (None, None)
+        cfg = cfg_of(wl.dtype, wl.D, wl.Hq, wl.Hkv, wl.rotary_dim, wl.style, cos, sin,
+                     wl.qk_norm, wl.eps,
+                     dev(x["q_norm_w"], dt) if wl.qk_norm else None,
+                     dev(x["k_norm_w"], dt) if wl.qk_norm else None, 0.0, wl.softcap,
+                     **cfg_extra(wl))
+        need = g.prefill_workspace_bytes(cfg, wl.B, wl.S, wl.n_cached) - SPLIT_BYTES
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need > 0 else None
+        whole = g.attn_prefill(cfg, dev(x["q"], dt), dev(x["k"], dt), dev(x["v"], dt),
+                               dev(x["positions"], torch.int32),
+                               dev(x["key_positions"], torch.int32), wl.n_cached, wl.window,
+                               workspace=ws)
+        torch.cuda.synchronize()
+        whole = whole.float().cpu().numpy()
+    finally:
+        PATH["kernel"] = "auto"
+    ref = ref_prefill(wl, x)
+    check(split, ref)
+    check(whole, ref)
+    assert np.abs(split - whole).max() <= 1e-2
+
+
 @pytest.mark.parametrize("name,kw", [
     ("peaky_q4_offset_norm", dict(q_scale=4.0, offset=0.3)),
     ("peaky_k4", dict(k_scale=4.0)),
