@@ -633,6 +633,12 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     }
   }
 
+  // Without the soft cap the softmax phase is much shorter than the matrix phase, so the V^T
+  // operands of the next P V's first four MFMAs are read at its end and the matrix phase starts
+  // on MFMAs at once.  With the cap both phases take about as long, and the reads would lengthen
+  // the softmax one: there all operands are read in the matrix phase.
+  constexpr bool kPrefetchV = !CAP;
+  i16x8 vpre[4];       // (kPrefetchV) V^T operands of the first four MFMAs of the next P V
   f32x16 sc = zero16;  // the next tile's scores (S^T), or the start value of their chain
   bf16x8 pw[2];       // the current tile's weights P, as the B operand of P V
   // S^T of the K tile in buffer buf
@@ -656,15 +662,36 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const uint32_t ofs = (uint32_t)((buf * TILE_ELEMS + 16 * u * HD) * sizeof(uint16_t));
-        const i16x4 vlo =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vaddr[0][db] + ofs));
-        const i16x4 vhi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vaddr[1][db] + ofs));
-        const i16x8 va = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
+        i16x8 va;
+        if (kPrefetchV && u == 0) {
+          va = vpre[db];
+        } else {
+          const uint32_t ofs = (uint32_t)((buf * TILE_ELEMS + 16 * u * HD) * sizeof(uint16_t));
+          const i16x4 vlo =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vaddr[0][db] + ofs));
+          const i16x4 vhi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vaddr[1][db] + ofs));
+          va = i16x8{vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
+        }
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pw[u],
                                                         o[db], 0, 0, 0);
       }
+  };
+  // The V^T operands of the first four P V MFMAs (keys 0-15) of the V tile in buffer buf, read
+  // ahead into vpre.  That tile has been visible to every wavefront since the barrier before the
+  // matrix phase that scored its K, and its buffer is refilled only several phases later.
+  auto vprefetch = [&](auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const uint32_t ofs = (uint32_t)(buf * TILE_ELEMS * sizeof(uint16_t));
+      const i16x4 vlo =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vaddr[0][db] + ofs));
+      const i16x4 vhi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vaddr[1][db] + ofs));
+      vpre[db] = i16x8{vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
+    }
   };
   // The tile starting at key jt needs no mask when all its keys are in range, none is newer than
   // the oldest query, and every query may see its first key.
@@ -744,10 +771,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
       }
     }
   };
-  // Matrix phase: O^T += V(buffer b0)^T P^T and S^T of the K tile in buffer b1.  The 24 LDS
-  // operand reads run four MFMAs ahead of their use (each MFMA is 32 cycles, an LDS read's
-  // latency several times that), and no further, so that only a few operands are live at a time
-  // (two wavefronts share each SIMD's registers).
+  // Matrix phase: O^T += V(buffer b0)^T P^T and S^T of the K tile in buffer b1.  The LDS operand
+  // reads (24, or 20 after a prefetch) run four MFMAs ahead of their use (each MFMA is 32 cycles,
+  // an LDS read's latency several times that), and no further, so that only a few operands are
+  // live at a time (two wavefronts share each SIMD's registers).
   // The phase also reads the next tile's first and last key positions and decides whether its
   // softmax needs the mask (that tile's loads have landed: its K is read here).
   auto mphase = [&](auto b0c, auto b1c, int jt1, bool& full1) __attribute__((always_inline)) {
@@ -757,11 +784,20 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     sc = qk(b1c, CAP ? zero16 : tmpl);
     full1 = (jt1 + BN <= j_end) & (__builtin_amdgcn_readfirstlane(klast) <= qmin32) &
             (__builtin_amdgcn_readfirstlane(kfirst) >= floor_max);
-    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);     // V operands of P V 0-3, positions
+    if (kPrefetchV) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // positions, V operand of P V 4
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // P V i
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // V operand of P V i+4
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // P V i
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V operands of P V 5-7, K of S^T 0
+      }
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);   // V operands of P V 0-3, positions
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // P V i
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V operand of P V i+4
+      }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -784,6 +820,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   barrier_after_loads<(NBUF - 3) * kDmaPerTile>();
   sc = qk(std::integral_constant<int, 0>(), zero16);
   softmax(j_lo, std::integral_constant<int, 0>(), tile_full(j_lo, std::integral_constant<int, 0>()));
+  if (kPrefetchV) vprefetch(std::integral_constant<int, 0>());
 
   // Tile t sits in buffer t mod NBUF.  Both groups run the same sequence -- M(t), barrier, refill
   // of tile t-1's buffer with tile t+NBUF-1, V(t+1), barrier -- group 1 one phase behind group 0:
@@ -805,6 +842,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     barrier_after_loads<(NBUF - 4) * kDmaPerTile>();
     issue_tile(j_lo + (t + NBUF - 1) * BN, t + NBUF - 1 < n_tiles, BR());
     softmax(jt1, B1(), full1);
+    if (kPrefetchV) vprefetch(B1());
     barrier_after_loads<(NBUF - 3) * kDmaPerTile>();
   };
   if (grp == 1) barrier_after_loads<(NBUF - 4) * kDmaPerTile>();
