@@ -555,7 +555,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
         }
       }
     }
-    const float qscale = a.scale * kLog2e;
+    // log2 units; with the soft cap the rows also carry the cap's factor k (below), so the
+    // products arrive as k s, ready for the cap's exp2
+    const float qscale = CAP ? -2.0f * a.scale * kLog2e / a.softcap : a.scale * kLog2e;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
 #pragma unroll
@@ -606,8 +608,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   f32x16 tmpl = zero16;
   const float cap2 = a.softcap * kLog2e;
   // cap2 tanh(s / cap2) = 2 cap2 / (1 + 2^(k s)) - cap2 with k = -2 log2(e) / cap2: one exp2, one
-  // reciprocal and one fma per score, with the limits +-cap2 reached exactly for large |s|
-  const float cap_k = CAP ? -2.0f * kLog2e / cap2 : 0.f;
+  // reciprocal and one fma per score, with the limits +-cap2 reached exactly for large |s|.  The
+  // query rows are scaled by k as well, so the S^T chains deliver k s.
 
   // per-lane LDS read offsets (elements).  K: row ql, chunk 2s + hg.  V^T (transposing reads):
   // rows 4*hgv + s16/4 (+8 for items 4..7) of each 16-key group, columns db*32 + 16*(gi&1) +
@@ -709,7 +711,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     if (CAP) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(sc[r] * cap_k);
+        const float e = fast_exp2(sc[r]);
         sc[r] = __builtin_fmaf(__builtin_amdgcn_rcpf(1.0f + e), 2.0f * cap2, mstart - cap2);
       }
     }
@@ -776,9 +778,12 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   // an LDS read's latency several times that), and no further, so that only a few operands are
   // live at a time (two wavefronts share each SIMD's registers).
   // The phase also reads the next tile's first and last key positions and decides whether its
-  // softmax needs the mask (that tile's loads have landed: its K is read here).
+  // softmax needs the mask (that tile's loads have landed: its K is read here).  It runs at raised
+  // wavefront priority, so that when both wavefronts of a SIMD have an instruction ready the
+  // MFMA issue of this one goes before the softmax arithmetic of the other.
   auto mphase = [&](auto b0c, auto b1c, int jt1, bool& full1) __attribute__((always_inline)) {
     constexpr int b1 = decltype(b1c)::value;
+    __builtin_amdgcn_s_setprio(3);
     const int32_t kfirst = g_lds.kp[b1][0][0], klast = g_lds.kp[b1][0][BN - 1];
     pv(b0c);
     sc = qk(b1c, CAP ? zero16 : tmpl);
@@ -805,6 +810,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // K operand of S^T i
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);      // S^T 4-7
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
   };
   // ---- first tiles: 0 .. NBUF-2 issued, 0 and 1 landed; S(0) and its weights ----
   if (j_lo != j_first && n_tiles > 0) {
