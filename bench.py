@@ -612,10 +612,11 @@ def main(argv=None):
             "workload": mwl.name, "value": round(mgbs, 1), "unit": "GB/s",
             "ms_per_call": round(mms, 4), "algorithmic_bytes": mbytes, "algorithmic_flop": mflops,
             "roofline": {"bound": "hbm",
-                         "kernel": "mla_split_kernel + mla_combine_kernel (one gqa_mla_decode call)",
+                         "kernel": "mla_split32_kernel + mla_split16_kernel (flagged shares only) + "
+                                   "mla_combine_kernel (one gqa_mla_decode call)",
                          "achieved": round(mgbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(mgbs / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic("mla_split_kernel", mwl.name),
+                         "traffic": measured_traffic("mla_split32_kernel", mwl.name),
                          "mfma_tflops": round(mtf, 1),
                          "mfma_frac": round(mtf / MFMA_BF16_PEAK_TFLOPS, 4)}}
         del mx

@@ -335,7 +335,10 @@ gqa_status gqa_attn_decode_paged(const gqa_attn_cfg* cfg, const void* q, const g
  *   workspace  device, >= gqa_mla_decode_workspace_bytes(B, H, Smax) bytes, 256-byte aligned:
  *              partial results of the (256 + B) pieces the batch is cut into (its blocks of 32
  *              keys are dealt out in 256 equal shares; a share may hold pieces of several
- *              sequences), (256 + B) * H * (512 + 2) floats.
+ *              sequences), (256 + B) * H * (512 + 2) floats (each part 256-byte aligned),
+ *              then one int32 flag per (group of 128 heads, share, quarter of the group)
+ *              marking a share whose weights could pass 2^64 against its first block's
+ *              maximum, which a second kernel then computes again with rescaling.
  * Errors: GQA_E_SHAPE also when B * ceil(Smax / 32) >= 2^31.
  * Two calls that share a workspace must be ordered on one stream. */
 size_t gqa_mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t Smax);

@@ -474,8 +474,12 @@ def test_mla_validation_and_workspace():
     assert lib.gqa_mla_decode_workspace_bytes(2, 24, 100) == 0 and "multiple of 16" in g.last_error()
     assert lib.gqa_mla_decode_workspace_bytes(2, 16, 0) == 0
     n = lib.gqa_mla_decode_workspace_bytes(2, 16, 4096)
-    # per (piece slot, head) a 512-wide partial and (m, l); 256 shares + B sequences of slots
-    assert n == (256 + 2) * 16 * 512 * 4 + (256 + 2) * 16 * 2 * 4
+    # per (piece slot, head) a 512-wide partial and (m, l); 256 shares + B sequences of slots;
+    # then one recompute flag per (head group, share, wavefront of the 32-head kernel)
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert n == a256((256 + 2) * 16 * 512 * 4) + a256((256 + 2) * 16 * 2 * 4) + 1 * 256 * 4 * 4
+    assert lib.gqa_mla_decode_workspace_bytes(2, 144, 4096) == (
+        a256((256 + 2) * 144 * 512 * 4) + a256((256 + 2) * 144 * 2 * 4) + 2 * 256 * 4 * 4)
     assert lib.gqa_mla_decode_workspace_bytes(2, 16, 100000) == n  # independent of Smax
     call = lambda **kw: lib.gqa_mla_decode(*[kw.get(k, d) for k, d in (
         ("q", FAKE), ("c", FAKE), ("lens", FAKE), ("B", 2), ("H", 16), ("S", 4096),

@@ -838,6 +838,32 @@ def test_mla_decode_matches_oracle(H, Smax, B):
     check(got, ref, head_axis=1)
 
 
+# A key aligned with one head's query, scaled by c, scores far above everything before it in its
+# sequence: by about 40 log2 units at c = 0.5 (weights up to 2^40 against the reference the first
+# block set, taken in place) and by several hundred at c = 4 (past 2^64: the share is flagged and
+# computed again by the rescaling kernel).
+@pytest.mark.parametrize("c", [0.5, 4.0])
+def test_mla_decode_score_jump(c):
+    H, Smax, B = 32, 300, 2
+    wl = MLA.with_(B=B, Hq=H, S=Smax, lens_lo=1, lens_hi=Smax)
+    say("mla decode score jump", c)
+    lens, q, _ = decode_lens_q(wl, seed=37)
+    lens[:] = [Smax, 200]
+    cache = np.zeros((B, Smax, 576), np.float32)
+    for b in range(B):
+        kk, _ = decode_cache_seq(wl, b, int(lens[b]), seed=37)
+        cache[b, :lens[b]] = kk[0]
+        qb = torch.as_tensor(q[b, 5]).to(torch.bfloat16).float().numpy()
+        cache[b, lens[b] - 1] = c * qb
+    out = g.mla_decode(dev(q), dev(cache), dev(lens, torch.int32), MLA_SCALE)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    cache_b = torch.as_tensor(cache).to(torch.bfloat16).float().numpy()
+    ref = oracle.mla_decode(q, cache_b, lens, MLA_SCALE)
+    check(got, ref, head_axis=1)
+
+
 def test_full_size_mla_decode_sampled():
     # the bench's DeepSeek-V3-shaped batch and launch, sampled sequences checked by the oracle
     import bench
