@@ -706,11 +706,19 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   // (allowed <=> key index < j_end and qlo32 <= key position <= qp32), row max, rare rescale,
   // exp2, bf16 weights P into pw and the row sum of those weights.
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  auto softmax = [&](int jt, auto bufc, bool full) __attribute__((always_inline)) {
+  // soft cap of score r (the products arrive as k s, see cap_k's note)
+  auto cap_score = [&](int r) __attribute__((always_inline)) {
+    const float e = fast_exp2(sc[r]);
+    sc[r] = __builtin_fmaf(__builtin_amdgcn_rcpf(1.0f + e), 2.0f * cap2, mstart - cap2);
+  };
+  // (lo_capped: the matrix phase has already capped scores 0-7)
+  auto softmax = [&](int jt, auto bufc, bool full, bool lo_capped = false)
+      __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     if (CAP) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        if (lo_capped && r < 8) continue;
         const float e = fast_exp2(sc[r]);
         sc[r] = __builtin_fmaf(__builtin_amdgcn_rcpf(1.0f + e), 2.0f * cap2, mstart - cap2);
       }
@@ -785,11 +793,33 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     constexpr int b1 = decltype(b1c)::value;
     __builtin_amdgcn_s_setprio(3);
     const int32_t kfirst = g_lds.kp[b1][0][0], klast = g_lds.kp[b1][0][BN - 1];
-    pv(b0c);
-    sc = qk(b1c, CAP ? zero16 : tmpl);
+    if (CAP) {
+      // With the soft cap the softmax phase is the longer one: S^T goes first here, and the cap
+      // of its first eight scores runs beside the P V MFMAs (the rest in the softmax phase).
+      sc = qk(b1c, zero16);
+      pv(b0c);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) cap_score(r);
+    } else {
+      pv(b0c);
+      sc = qk(b1c, tmpl);
+    }
     full1 = (jt1 + BN <= j_end) & (__builtin_amdgcn_readfirstlane(klast) <= qmin32) &
             (__builtin_amdgcn_readfirstlane(kfirst) >= floor_max);
-    if (kPrefetchV) {
+    if (CAP) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);    // positions, K of S^T 0-3
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // S^T i
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // K of S^T 4-7, V of P V 0-5
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // P V i
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // V of P V 6-7
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // cap of the first scores
+      }
+    } else if (kPrefetchV) {
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // positions, V operand of P V 4
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -804,12 +834,14 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V operand of P V i+4
       }
     }
+    if (!CAP) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // P V 4-7, then S^T 0-3
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // K operand of S^T i
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // P V 4-7, then S^T 0-3
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // K operand of S^T i
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);    // S^T 4-7
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);      // S^T 4-7
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
   };
@@ -848,7 +880,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     mphase(B0(), B1(), jt1, full1);
     barrier_after_loads<(NBUF - 4) * kDmaPerTile>();
     issue_tile(j_lo + (t + NBUF - 1) * BN, t + NBUF - 1 < n_tiles, BR());
-    softmax(jt1, B1(), full1);
+    softmax(jt1, B1(), full1, true);
     if (kPrefetchV) vprefetch(B1());
     barrier_after_loads<(NBUF - 3) * kDmaPerTile>();
   };
