@@ -91,10 +91,9 @@ PREFILL_KERNEL_NAMES = {"stream_long": "prefill_stream_kernel", "stream_short": 
                         "fused": "prefill_mfma_kernel", "generic": "attn_generic_kernel"}
 
 
-def measured_traffic(kernel, workload):
-    """HBM bytes per launch of `kernel` on `workload` from the committed counter runs
-    (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE scaled by a known-size copy), or None when
-    no counters were taken on that workload or the kernel's source has changed since."""
+def profile_record(kernel, workload):
+    """The committed counter summary of `kernel` on `workload` (profiles/traffic.json), or None
+    when no counters were taken on that workload or the kernel's source has changed since."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
@@ -103,9 +102,26 @@ def measured_traffic(kernel, workload):
         with open(os.path.join(ROOT, rec["source"]), "rb") as f:
             if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
                 return None
-        return int(rec["hbm_bytes_per_launch"])
+        return rec
     except (OSError, KeyError, ValueError, TypeError):
         return None
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter runs
+    (FETCH_SIZE and WRITE_SIZE scaled by a known-size copy), or None (see profile_record)."""
+    rec = profile_record(kernel, workload)
+    try:
+        return int(rec["hbm_bytes_per_launch"]) if rec else None
+    except (KeyError, ValueError, TypeError):
+        return None
+
+
+def measured_mfma(kernel, workload):
+    """MFMA busy share of SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x GRBM_GUI_ACTIVE
+    per XCD) and the clock of that counter run, from the committed counters, or (None, None)."""
+    rec = profile_record(kernel, workload) or {}
+    return rec.get("mfma_busy"), rec.get("clock_ghz_counter_run")
 
 
 # ---- helpers ---------------------------------------------------------------------------------
@@ -254,6 +270,9 @@ def prefill_record(wl, steps, warmup, torch, g, graph, cpu, budget_s):
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(kern, wl.name),
                 "kernel_ms_mean": round(kern_ms, 4), "algorithmic_flop": flops}
+        # MFMA busy as rocprof counts it (at the clock the chip runs under this load, below the
+        # 2.4 GHz of the peak figure)
+        roof["mfma_busy_rocprof"], roof["clock_ghz_counter_run"] = measured_mfma(kern, wl.name)
     else:
         # 16 query rows: far too small to load any unit of the chip; reported against the fp32
         # vector peak for completeness, no roofline claim
@@ -617,6 +636,7 @@ def main(argv=None):
                          "achieved": round(mgbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(mgbs / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("mla_split32_kernel", mwl.name),
+                         "mfma_busy_rocprof": measured_mfma("mla_split32_kernel", mwl.name)[0],
                          "mfma_tflops": round(mtf, 1),
                          "mfma_frac": round(mtf / MFMA_BF16_PEAK_TFLOPS, 4)}}
         del mx
