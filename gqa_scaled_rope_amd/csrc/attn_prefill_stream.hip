@@ -925,19 +925,34 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
   const float lden =
       (a.sinks != nullptr && ltot > 0.f) ? ltot + fast_exp2(a.sinks[qh] * kLog2e - m) : ltot;
   const float inv = ltot > 0.f ? 1.0f / lden : 0.f;
-  if (qvalid) {
-    uint16_t* orow = (uint16_t*)a.out + (int64_t)b * a.o_b + (int64_t)qi * a.o_i +
-                     (int64_t)qh * a.o_h;
+  // The output goes out through LDS: each wavefront writes its 32 rows (bf16, 128 features) into
+  // a staging area of 264-byte rows, then stores whole rows, 16 bytes per lane, four rows per
+  // store instruction (in place of 8 bytes from each of 32 rows).  The padding puts the 8-byte
+  // writes of each half wavefront, and the reads of each group of 16 lanes, in distinct banks.
+  // The tile buffers are free once every wavefront's last (out-of-range) tile loads have landed
+  // (the wait above): one more barrier.
+  phase_barrier();
+  constexpr int kStagePitch = HD + 4;  // elements
+  uint16_t* const stage = (uint16_t*)&g_lds + w * (WROWS * kStagePitch);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d = db * 32 + 8 * rq + 4 * hg;
-        u32x2 w2;
-        w2[0] = pack_bf16x2(o[db][4 * rq + 0] * inv, o[db][4 * rq + 1] * inv);
-        w2[1] = pack_bf16x2(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
-        *(u32x2*)(orow + d) = w2;
-      }
+    for (int rq = 0; rq < 4; ++rq) {
+      u32x2 w2;
+      w2[0] = pack_bf16x2(o[db][4 * rq + 0] * inv, o[db][4 * rq + 1] * inv);
+      w2[1] = pack_bf16x2(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
+      *(u32x2*)(stage + ql * kStagePitch + db * 32 + 8 * rq + 4 * hg) = w2;
+    }
+  // element offset of this lane's row in out (-1: past the end), fetched by the storing lanes
+  const int64_t orow = qvalid ? (int64_t)b * a.o_b + (int64_t)qi * a.o_i + (int64_t)qh * a.o_h : -1;
+  const int c16 = lane & 15;
+#pragma unroll
+  for (int j = 0; j < WROWS / 4; ++j) {
+    const int rr = 4 * j + (lane >> 4);
+    const int64_t dst = __shfl(orow, rr, 64);
+    const uint16_t* src = stage + rr * kStagePitch + 8 * c16;
+    const u32x2 lo = *(const u32x2*)src, hi = *(const u32x2*)(src + 4);
+    if (dst >= 0) *(u32x4*)((uint16_t*)a.out + dst + 8 * c16) = u32x4{lo[0], lo[1], hi[0], hi[1]};
   }
 }
 
