@@ -584,9 +584,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
       n_tiles -= n0;
     }
   }
-  // first key index past this walk: the band's end, or the first half's last tile.  The loop
-  // scores one tile past its walk (its weights are never used against V); key indices from j_end
-  // on are masked, so that tile adds nothing to the row sums.
+  // first key index past this walk: the band's end, or the first half's last tile.  Key indices
+  // from j_end on are masked (the walk's last tile may reach past it).
   const int j_end = min(j_hi, j_lo + n_tiles * BN);
 
   f32x16 o[4];
@@ -884,26 +883,53 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     if (kPrefetchV) vprefetch(B1());
     barrier_after_loads<(NBUF - 3) * kDmaPerTile>();
   };
+  // The walk's last tile (buffer PH) has no next tile to score: its matrix phase is the P V
+  // product alone, and one barrier ends it.  With group 1 one phase behind, that barrier pairs
+  // with group 0's closing one below, so group 1's last V reads are done before any wavefront
+  // moves on; tiles still in flight then all lie past the walk, in other buffers.
+  auto tail = [&](int buf) __attribute__((always_inline)) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const uint32_t bofs = (uint32_t)(buf * TILE_ELEMS * sizeof(uint16_t));
+    __builtin_amdgcn_s_setprio(3);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint32_t ofs = bofs + (uint32_t)(16 * u * HD * sizeof(uint16_t));
+        const i16x4 vlo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vaddr[0][db] + ofs));
+        const i16x4 vhi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vaddr[1][db] + ofs));
+        const i16x8 va = i16x8{vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pw[u],
+                                                        o[db], 0, 0, 0);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    phase_barrier();
+  };
   if (grp == 1) barrier_after_loads<(NBUF - 4) * kDmaPerTile>();
   // (exits after any iteration: the unrolled body stays one straight path with no joins inside)
-  for (int t = 0; t < n_tiles;) {
+  const int t_last = n_tiles - 1;
+  for (int t = 0; t < t_last;) {
     iter(t, std::integral_constant<int, 0>());
-    if (++t >= n_tiles) break;
+    if (++t >= t_last) break;
     iter(t, std::integral_constant<int, 1>());
-    if (++t >= n_tiles) break;
+    if (++t >= t_last) break;
     iter(t, std::integral_constant<int, 2>());
-    if (++t >= n_tiles) break;
+    if (++t >= t_last) break;
     iter(t, std::integral_constant<int, 3>());
-    if (++t >= n_tiles) break;
+    if (++t >= t_last) break;
     iter(t, std::integral_constant<int, 4>());
-    if (++t >= n_tiles) break;
+    if (++t >= t_last) break;
     iter(t, std::integral_constant<int, 5>());
-    if (++t >= n_tiles) break;
+    if (++t >= t_last) break;
     iter(t, std::integral_constant<int, 6>());
-    if (++t >= n_tiles) break;
+    if (++t >= t_last) break;
     iter(t, std::integral_constant<int, 7>());
     ++t;
   }
+  if (n_tiles > 0) tail(t_last & (NBUF - 1));
   static_assert(NBUF == 8, "the loop above is unrolled by NBUF");
   if (grp == 0) phase_barrier();
   // every wavefront's loads retire before the workgroup ends (the last ones were out of range)
