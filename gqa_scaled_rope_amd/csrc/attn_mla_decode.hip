@@ -336,19 +336,21 @@ __global__ __launch_bounds__(4 * 64, 1) void mla_split32_kernel(MlaArgs m) {
     mt = fmaxf(mt, swap_halves(mt)) * m.qscale;
     if (mr == kNegBig) mr = mt;
     over |= mt > mr + kRefLimit;
+    // weights of keys 0-15 now; those of keys 16-31 beside the first P V MFMAs, which use only
+    // the first half
     bf16x8 pw[2];
-#pragma unroll
-    for (int uh = 0; uh < 2; ++uh) {
+    float p1[8];
+    {
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = fast_exp2(__builtin_fmaf(sc[8 * uh + e], m.qscale, -mr));
+        p[e] = fast_exp2(__builtin_fmaf(sc[e], m.qscale, -mr));
         lsum += p[e];
       }
       u32x4 w4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) w4[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
-      pw[uh] = as_bf16x8(w4);
+      pw[0] = as_bf16x8(w4);
     }
     // O^T += V^T P^T over keys 16 uh .. 16 uh + 15 (step i = 16 uh + db); operands VLA steps
     // ahead in a ring, as above
@@ -368,6 +370,15 @@ __global__ __launch_bounds__(4 * 64, 1) void mla_split32_kernel(MlaArgs m) {
       if (i + VLA < LAT / 16) vring[i % VLA] = vread(i + VLA);
       o[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
                                                           pw[i >> 4], o[i & 15], 0, 0, 0);
+      if (i < 8) {  // weight 8 + i of this lane
+        p1[i] = fast_exp2(__builtin_fmaf(sc[8 + i], m.qscale, -mr));
+        lsum += p1[i];
+      } else if (i == 8) {
+        u32x4 w4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w4[e] = pack_bf16x2(p1[2 * e], p1[2 * e + 1]);
+        pw[1] = as_bf16x8(w4);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
