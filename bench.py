@@ -17,7 +17,9 @@ under "extras".
 Prints ONE JSON line on stdout (progress goes to stderr).  FLOPs count only allowed
 (query, key) pairs, 4 * D per pair per head; decode bytes are the K and V rows each sequence
 actually reads plus q, out and lens.  Kernel times come from HIP events recorded on the stream
-the kernels are launched on, around K back-to-back launches of the timed call.
+the kernels are launched on, around K back-to-back launches of the timed call.  Before each timed
+region the W warmup calls run, continued until at least 50 ms of GPU work has run back to back
+(the clock's ramp after an idle gap; "warmup_min_gpu_ms" in the line).
 """
 from __future__ import annotations
 
@@ -171,6 +173,22 @@ def _prefill_setup(wl, torch, g):
                 out=out, table_len=table_len, kcache=kcache, ws=ws)
 
 
+SETTLE_MS = 50.0   # least GPU time of untimed warmup before a timed region
+
+
+def _warm_up(fn, warmup, torch):
+    """The W untimed warmup calls, continued in batches until at least SETTLE_MS of GPU time has
+    run back to back: after an idle gap (a graph capture, a check, the CPU baseline) MI355X
+    raises its clock over the first tens of milliseconds of load, and a timed region that starts
+    inside that ramp reads up to 15% slow (measured: 0.94 ms for the first Mistral-style steps
+    after 0.5 s idle, 0.79 ms after 40 steps)."""
+    n, ms = 0, 0.0
+    while n < warmup or ms < SETTLE_MS:
+        ms += _time_calls(fn, 4, torch) * 4
+        n += 4
+    return n
+
+
 def _time_calls(fn, n, torch):
     """Average ms of n back-to-back calls of fn, from HIP events on the current stream (the
     stream every library call here is launched on)."""
@@ -240,6 +258,7 @@ def run_prefill(wl, steps, warmup, torch, g, graph=True):
                 raise RuntimeError("graph replay differs from the eager step")
         x["graph"] = hg
         step_fn = hg.replay
+    _warm_up(step_fn, warmup, torch)
     step_ms = _time_calls(step_fn, steps, torch)
     # each call alone, back to back (the attention call reads the cache the step left)
     parts = {"rope_tables": _time_calls(tables, steps, torch)}
@@ -318,9 +337,7 @@ def run_decode(wl, steps, warmup, torch, g):
     def call():
         g.attn_decode(cfg, x["q"], x["k"], x["v"], x["lens"], wl.window, out, ws)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
+    _warm_up(call, warmup, torch)
     ms = _time_calls(call, steps, torch)
     x.update(cfg=cfg, out=out, cos=cos, sin=sin)
     return x, ms
@@ -371,9 +388,7 @@ def run_decode_paged(wl, dx, block_size, steps, warmup, torch, g):
     def call():
         g.attn_decode_paged(cfg, dx["q"], kv, dx["lens"], wl.window, out, ws)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
+    _warm_up(call, warmup, torch)
     ms = _time_calls(call, steps, torch)
     same = bool(torch.equal(out, dx["out"]))
     del kv, ws
@@ -407,9 +422,7 @@ def run_mla(wl, steps, warmup, torch, g):
     def call():
         g.mla_decode(q, cache, dl, scale, out, ws)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
+    _warm_up(call, warmup, torch)
     ms = _time_calls(call, steps, torch)
     keys = int(lens.sum())
     nbytes = keys * MLA_ROW_BYTES + wl.B * wl.Hq * (576 + 512) * 2 + 4 * wl.B
@@ -591,6 +604,8 @@ def main(argv=None):
                    "launch": "eager" if args.no_graph else "HIP graph of the step's kernels"},
         "roofline": head["roofline"],
         "step_parts_ms": head["step_parts_ms"],
+        # every timed region follows its W warmup calls, continued until this much GPU time ran
+        "warmup_min_gpu_ms": SETTLE_MS,
     }
     if cpu:
         line["cpu_baseline"] = head["cpu_baseline"]
