@@ -63,6 +63,56 @@ def build(verbose=True):
     return LIB
 
 
+# Host sanitizers: the C-ABI layer (argument checks, the host-side rotary frequencies) rebuilt
+# with AddressSanitizer and UndefinedBehaviorSanitizer on its host code only (each -fsanitize=
+# goes to the host compilation; the device code is unchanged) and linked with the kernel objects
+# of the normal build, for the CPU tests of the ABI (no kernel is launched there).
+SANITIZED_SOURCES = ("gqa_api.hip", "rope_tables.hip")
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime():
+    """Path of the AddressSanitizer runtime of hipcc's clang (to preload into a host process)."""
+    base = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(HIPCC))), "lib", "llvm",
+                        "lib", "clang")
+    for root in (base, "/opt/rocm/llvm/lib/clang"):
+        if os.path.isdir(root):
+            for ver in sorted(os.listdir(root), reverse=True):
+                p = os.path.join(root, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+                if os.path.exists(p):
+                    return p
+    return None
+
+
+def build_sanitized(dest):
+    """libgqa_rope with sanitized host code in directory dest (the normal build's objects are
+    reused for the other sources); returns the library's path."""
+    os.makedirs(dest, exist_ok=True)
+    objs = []
+    for src in sources():
+        name = os.path.basename(src)
+        if name in SANITIZED_SOURCES:
+            obj = os.path.join(dest, name[:-4] + ".o")
+            cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(name, []), *SANITIZE_FLAGS, "-c", src, "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        else:
+            obj = os.path.join(OBJ, name[:-4] + ".o")
+            if not os.path.exists(obj):
+                raise RuntimeError(f"{obj} missing: run build() first")
+        objs.append(obj)
+    lib = os.path.join(dest, "libgqa_rope_sanitized.so")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", *objs, "-o", lib]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     build()
     sys.exit(0)
