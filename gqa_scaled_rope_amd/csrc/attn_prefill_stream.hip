@@ -634,6 +634,11 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     }
   }
 
+  // The mask's key positions are read from one per-lane base address, hidden from the compiler,
+  // plus a constant below 64 KB, so that no address per buffer is kept.
+  uint32_t kpaddr = (uint32_t)(uintptr_t)(lds_void*)(g_lds.kp[0][0] + 4 * hg);
+  asm volatile("" : "+v"(kpaddr));
+
   // Without the soft cap the softmax phase is much shorter than the matrix phase, so the V^T
   // operands of the next P V's first four MFMAs are read at its end and the matrix phase starts
   // on MFMAs at once.  With the cap both phases take about as long, and the reads would lengthen
@@ -726,7 +731,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int idx0 = 8 * gq + 4 * hg;
-        const i32x4 k4 = *(const i32x4*)(g_lds.kp[buf][0] + idx0);
+        typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+        const i32x4 k4 = *(const lds_i32x4*)(uintptr_t)(
+            kpaddr + (uint32_t)((buf * NW * 64 + 8 * gq) * sizeof(int32_t)));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool ok = jt + idx0 + e < j_end && k4[e] <= qp32 && k4[e] >= qlo32;
@@ -799,6 +806,55 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
       pv(b0c);
 #pragma unroll
       for (int r = 0; r < 8; ++r) cap_score(r);
+    } else if (kPrefetchV) {
+      // S^T step i and P V step i+3 alternate (P V 0-2 first: their operands are in registers),
+      // so that each MFMA of the dependent S^T chain has an independent one before it.  Each
+      // step is fenced, with the operand reads two steps ahead in the step before.
+      constexpr int b0 = decltype(b0c)::value;
+      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+      const uint16_t* ks = g_lds.k[b1];
+      auto kread = [&](int st) __attribute__((always_inline)) {
+        return *(const u32x4*)(ks + koff[st]);
+      };
+      auto vread = [&](int db) __attribute__((always_inline)) {  // key half 1, feature block db
+        const uint32_t ofs = (uint32_t)((b0 * TILE_ELEMS + 16 * HD) * sizeof(uint16_t));
+        const i16x4 vlo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vaddr[0][db] + ofs));
+        const i16x4 vhi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vaddr[1][db] + ofs));
+        return i16x8{vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
+      };
+      auto pvs = [&](int i, const i16x8& v) __attribute__((always_inline)) {
+        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v),
+                                                            pw[i >> 2], o[i & 3], 0, 0, 0);
+      };
+      u32x4 kop[8];
+      i16x8 va[4];
+      kop[0] = kread(0);
+      kop[1] = kread(1);
+      __builtin_amdgcn_sched_barrier(0);
+      pvs(0, vpre[0]);
+      kop[2] = kread(2);
+      va[0] = vread(0);
+      __builtin_amdgcn_sched_barrier(0);
+      pvs(1, vpre[1]);
+      kop[3] = kread(3);
+      va[1] = vread(1);
+      __builtin_amdgcn_sched_barrier(0);
+      pvs(2, vpre[2]);
+      kop[4] = kread(4);
+      va[2] = vread(2);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 acc = tmpl;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[i]), qop[i], acc, 0, 0, 0);
+        if (i + 3 < 8) pvs(i + 3, i == 0 ? vpre[3] : va[i - 1]);
+        if (i + 5 < 8) kop[i + 5] = kread(i + 5);
+        if (i == 0) va[3] = vread(3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sc = acc;
     } else {
       pv(b0c);
       sc = qk(b1c, tmpl);
@@ -819,12 +875,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
         __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // cap of the first scores
       }
     } else if (kPrefetchV) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // positions, V operand of P V 4
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // P V i
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V operands of P V 5-7, K of S^T 0
-      }
+      // (each step fenced above)
     } else {
       __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);   // V operands of P V 0-3, positions
 #pragma unroll
@@ -833,7 +884,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V operand of P V i+4
       }
     }
-    if (!CAP) {
+    if (!CAP && !kPrefetchV) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // P V 4-7, then S^T 0-3
