@@ -806,7 +806,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
       pv(b0c);
 #pragma unroll
       for (int r = 0; r < 8; ++r) cap_score(r);
-    } else if (kPrefetchV) {
+    } else {
+      static_assert(kPrefetchV == !CAP, "the matrix phase without the cap starts from vpre");
       // S^T step i and P V step i+3 alternate (P V 0-2 first: their operands are in registers),
       // so that each MFMA of the dependent S^T chain has an independent one before it.  Each
       // step is fenced, with the operand reads two steps ahead in the step before.
@@ -855,9 +856,6 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
         __builtin_amdgcn_sched_barrier(0);
       }
       sc = acc;
-    } else {
-      pv(b0c);
-      sc = qk(b1c, tmpl);
     }
     full1 = (jt1 + BN <= j_end) & (__builtin_amdgcn_readfirstlane(klast) <= qmin32) &
             (__builtin_amdgcn_readfirstlane(kfirst) >= floor_max);
@@ -874,24 +872,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // V of P V 6-7
         __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // cap of the first scores
       }
-    } else if (kPrefetchV) {
-      // (each step fenced above)
-    } else {
-      __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);   // V operands of P V 0-3, positions
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // P V i
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V operand of P V i+4
-      }
-    }
-    if (!CAP && !kPrefetchV) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // P V 4-7, then S^T 0-3
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // K operand of S^T i
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);    // S^T 4-7
-    }
+    }  // (without the cap each step is fenced above)
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
   };
