@@ -788,9 +788,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_stream_kernel(StreamArgs sa, in
     }
   };
   // Matrix phase: O^T += V(buffer b0)^T P^T and S^T of the K tile in buffer b1.  The LDS operand
-  // reads (24, or 20 after a prefetch) run four MFMAs ahead of their use (each MFMA is 32 cycles,
-  // an LDS read's latency several times that), and no further, so that only a few operands are
-  // live at a time (two wavefronts share each SIMD's registers).
+  // reads run a few MFMAs ahead of their use (four with the soft cap; two S^T/P V step pairs
+  // without it, where the first four V operands were read in the softmax phase), and no further,
+  // so that only a few operands are live at a time (two wavefronts share each SIMD's registers).
   // The phase also reads the next tile's first and last key positions and decides whether its
   // softmax needs the mask (that tile's loads have landed: its K is read here).  It runs at raised
   // wavefront priority, so that when both wavefronts of a SIMD have an instruction ready the
