@@ -518,6 +518,9 @@ def _blas_threads():
 
 CONFIGS = ("tiny_causal_f32", "qwen3_prefill_bf16", "chunked_prefill_bf16_w4096",
            "chunked_prefill_bf16_full")
+# the widened rows' workloads: gpt-oss-style sinks with a 128-key window, Llama-4-style chunks of
+# 8192, and the Llama-3.1-style decode with chunks of 8192 and sinks
+WIDENED = ("sinks_swa128_prefill_bf16", "llama4_chunked_prefill_bf16", "sinks_chunk_decode_bf16")
 DECODE_CONFIG = "llama31_decode_bf16"
 
 
@@ -556,6 +559,9 @@ def main(argv=None):
                     help="launch the step's kernels one by one instead of replaying a HIP graph")
     ap.add_argument("--mla-workload", default="deepseek_mla_decode_bf16",
                     help="latent-attention decode workload timed as an extra ('' to skip)")
+    ap.add_argument("--widened", default=",".join(WIDENED),
+                    help="workloads of the widened rows (sinks, chunked masks) timed as extras, "
+                         "each with its roofline and an oracle check on a bounded sample")
     ap.add_argument("--paged-block", type=int, default=16, metavar="N",
                     help="also time the decode workload through a paged pool of N-slot blocks "
                          "(0: skip)")
@@ -655,6 +661,18 @@ def main(argv=None):
                          "mfma_tflops": round(mtf, 1),
                          "mfma_frac": round(mtf / MFMA_BF16_PEAK_TFLOPS, 4)}}
         del mx
+    for name in filter(None, args.widened.split(",")):
+        wwl = WORKLOADS[name]
+        log(f"[bench] widened row {name}")
+        if wwl.kind == "decode":
+            rec, wdx, _ = decode_record(wwl, args.steps, args.warmup, torch, g, cpu,
+                                        args.cpu_budget / 3)
+            del wdx
+        else:
+            rec = prefill_record(wwl, args.steps, args.warmup, torch, g, graph, cpu,
+                                 args.cpu_budget / 3)
+        extras[name] = rec
+        torch.cuda.empty_cache()
     line["extras"] = extras
     print(json.dumps(line), flush=True)
     return 0
