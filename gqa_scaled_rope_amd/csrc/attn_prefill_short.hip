@@ -1,5 +1,5 @@
 // bf16 MFMA prefill attention over prepared keys, head_dim 128, gfx950 -- the short-band kernel.
-// Four wavefronts of 32 query rows of one KV head per workgroup and three K/V tile buffers (48 KB
+// Four wavefronts of 32 query rows of one KV head per workgroup and four K/V tile buffers (68 KB
 // of LDS), so two workgroups share a CU: one's query preparation and first tile loads overlap the
 // other's loop.  With few key tiles per workgroup (a short sliding window, early causal blocks)
 // that overlap matters more than the longer pipeline of the eight-wavefront kernel in
@@ -19,36 +19,44 @@ constexpr int ROWS = NW * 32;
 constexpr int kTileRounds = BN / (4 * NW);  // 1 KB loads per wave per K (or V) tile
 static_assert(BN % (4 * NW) == 0 && BN <= 64, "tile loader and key-position loader layout");
 
-// Triple-buffered K/V/key-position tiles.  Each buffer is its own LDS object and the step loop
-// is unrolled over the buffer cycle, so every access names its buffer at compile time: the
-// compiler can then see that reads of the current tiles never alias the asynchronous HBM->LDS
-// loads of a later one and does not make them wait for those loads.
-constexpr int NBUF = 3;
+// Four K/V/key-position tile buffers: while a step works on tiles t and t + 1, tiles t + 2 and
+// t + 3 are in flight, so a band of a few tiles is loaded almost whole before the loop starts.
+// Each buffer is its own LDS object and the step loop is unrolled over the buffer cycle, so every
+// access names its buffer at compile time: the compiler can then see that reads of the current
+// tiles never alias the asynchronous HBM->LDS loads of a later one and does not make them wait
+// for those loads.  Every wavefront loads the tile's key positions into its own row, so each
+// wavefront issues the same number of loads per tile and a counted wait retires exactly the
+// tiles due.
+constexpr int NBUF = 4;
+constexpr int kDmaPerTile = 2 * kTileRounds + 1;  // per wavefront: K, V and the key positions
 __shared__ __attribute__((aligned(16))) uint16_t g_k0[TILE_ELEMS];
 __shared__ __attribute__((aligned(16))) uint16_t g_k1[TILE_ELEMS];
 __shared__ __attribute__((aligned(16))) uint16_t g_k2[TILE_ELEMS];
+__shared__ __attribute__((aligned(16))) uint16_t g_k3[TILE_ELEMS];
 __shared__ __attribute__((aligned(16))) uint16_t g_v0[TILE_ELEMS];
 __shared__ __attribute__((aligned(16))) uint16_t g_v1[TILE_ELEMS];
 __shared__ __attribute__((aligned(16))) uint16_t g_v2[TILE_ELEMS];
-__shared__ __attribute__((aligned(16))) int32_t g_p0[BN];
-__shared__ __attribute__((aligned(16))) int32_t g_p1[BN];
-__shared__ __attribute__((aligned(16))) int32_t g_p2[BN];
+__shared__ __attribute__((aligned(16))) uint16_t g_v3[TILE_ELEMS];
+__shared__ __attribute__((aligned(16))) int32_t g_p[NBUF][NW][64];
 
 template <int BUF>
-__device__ __forceinline__ uint16_t* kbuf() { return BUF == 0 ? g_k0 : BUF == 1 ? g_k1 : g_k2; }
+__device__ __forceinline__ uint16_t* kbuf() {
+  return BUF == 0 ? g_k0 : BUF == 1 ? g_k1 : BUF == 2 ? g_k2 : g_k3;
+}
 template <int BUF>
-__device__ __forceinline__ uint16_t* vbuf() { return BUF == 0 ? g_v0 : BUF == 1 ? g_v1 : g_v2; }
-template <int BUF>
-__device__ __forceinline__ int32_t* pbuf() { return BUF == 0 ? g_p0 : BUF == 1 ? g_p1 : g_p2; }
+__device__ __forceinline__ uint16_t* vbuf() {
+  return BUF == 0 ? g_v0 : BUF == 1 ? g_v1 : BUF == 2 ? g_v2 : g_v3;
+}
 
 
 template <int ROT, bool NORM, bool CAP>
-// Two workgroups per CU (3 x 16 KB tiles of LDS and up to 256 VGPRs each): one's query prep and
+// Two workgroups per CU (4 x 17 KB tiles of LDS and up to 256 VGPRs each): one's query prep and
 // first tiles overlap the other's loop, and each barrier holds only the four waves of one group.
 __global__ __launch_bounds__(NT, 2) void prefill_short_kernel(StreamArgs sa, int nqb) {
   const AttnArgs& a = sa.a;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: a scalar register
   const int ql = lane & 31, hg = lane >> 5;
   // Work item of this workgroup.  Workgroups are dealt to the 8 XCDs round-robin by id; map ids
   // so that every query block of one (b, g) lands on the same XCD (its K/V then stay in that
@@ -117,11 +125,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_short_kernel(StreamArgs sa, int
       sa.kprep ? sa.kprep + (int64_t)b * nws * a.k_j + (int64_t)g * a.k_h : nullptr,
       (sa.kprep && nws > 0) ? (nws - 1) * row_bytes + HD * 2 : 0);
   const i32x4 rv = rsrc_words((const uint16_t*)a.v + kv_base, (a.S - 1) * row_bytes + HD * 2);
-  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.kpos + (int64_t)b * a.kpos_b), (short)0, a.S * 4, kBufFlags);
+  const i32x4 rp = rsrc_words(kpos_b, a.S * 4);
 
-  uint32_t kp_pend = 0;
-  bool kp_pend_ok = false;
   // Tile loader: wave w, round i fills LDS rows 4*(w + NW i) .. +3 (1 KB); lane -> row
   // 4(w + NW i) + lane/16, LDS chunk lane%16, which holds source chunk (lane%16) ^ swz(row).
   // Lane constants of the tile loader (offset of the lane's 16 bytes within a tile); a tile adds
@@ -146,17 +151,16 @@ __global__ __launch_bounds__(NT, 2) void prefill_short_kernel(StreamArgs sa, int
       tile_dma16(rv, vdst, lv[i] + tb);
       tile_dma16(rks, kdst, lk[i] + kb0);
     }
-    // key positions of the tile: loaded by wave 0 into a register and written to LDS by
-    // commit_kpos once the tile's loads are complete, with INT32_MAX past the last key so that the
-    // position test alone masks the ragged tail
-    if (w == 0) {
-      kp_pend = __builtin_amdgcn_raw_buffer_load_b32(rp, (jt + lane) * 4, 0, 0);
-      kp_pend_ok = lane < BN && jt + lane < a.S;
-    }
+    // the tile's key positions (and the next tile's, unused) into this wavefront's own row;
+    // positions past the last key read as zero and are masked by key index
+    tile_dma4(rp, (lds_void*)g_p[buf][w], (uint32_t)((jt + lane) * 4));
   };
-  auto commit_kpos = [&](auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    if (w == 0 && lane < BN) pbuf<buf>()[lane] = kp_pend_ok ? (int32_t)kp_pend : INT32_MAX;
+  // tiles 0 .. n - 1 (n < NBUF) of a band starting at key j0, into buffers 0 .. n - 1
+  auto issue_first = [&](int j0, int n) {
+    static_assert(NBUF == 4, "first-tile loads are written out for four buffers");
+    if (n > 0) issue_tile(j0, std::integral_constant<int, 0>());
+    if (n > 1) issue_tile(j0 + BN, std::integral_constant<int, 1>());
+    if (n > 2) issue_tile(j0 + 2 * BN, std::integral_constant<int, 2>());
   };
 
 
@@ -175,13 +179,14 @@ __global__ __launch_bounds__(NT, 2) void prefill_short_kernel(StreamArgs sa, int
   const int32_t floor_max = (int32_t)max<int64_t>(key_floor(a, qmax), INT32_MIN);
   const int g_hi = (int)min<int64_t>(max<int64_t>(x_hi - kp0, 0), a.S);
   const int g_lo = (int)min<int64_t>(max<int64_t>(x_lo - kp0, 0), a.S);
-  // The first tile's loads go out now -- at key 0 without a window or chunks, else at the guessed
-  // band start (loaded again below if the guess is wrong) -- after the waits for the position
-  // loads above (a wait for those placed behind the tile's loads would wait for the tile too) and
-  // beside the band and query-prep loads below.
+  // The first NBUF - 1 tiles' loads go out now -- from key 0 without a window or chunks, else from
+  // the guessed band start (loaded again below if the guess is wrong) -- after the waits for the
+  // position loads above (a wait for those placed behind the tiles' loads would wait for the
+  // tiles too) and beside the band and query-prep loads below.
   const int j_first = a.has_floor() ? g_lo : 0;
+  const int n_first = min((max(g_hi, j_first) - j_first + BN - 1) / BN, NBUF - 1);
   __builtin_amdgcn_sched_barrier(0);
-  issue_tile(j_first, std::integral_constant<int, 0>());
+  issue_first(j_first, n_first);
   const int32_t hi_l = kpos_b[max(g_hi - 1, 0)], hi_r = kpos_b[min(g_hi, a.S - 1)];
   const int32_t lo_l = kpos_b[max(g_lo - 1, 0)], lo_r = kpos_b[min(g_lo, a.S - 1)];
   // smallest key position the row may see (window, chunks); INT32_MAX for rows past the end
@@ -351,8 +356,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_short_kernel(StreamArgs sa, int
       voff[h2][db] = row * HD + (((col >> 3) ^ vswz(row)) << 3) + (col & 7);
     }
   }
-  // mask bounds in int32: allowed <=> qlo32 <= key position <= qp32 (key positions past the last
-  // key read INT32_MAX, so the ragged tail fails the first test)
+  // mask bounds in int32: allowed <=> key index < j_hi and qlo32 <= key position <= qp32
   // (qlo32, the window/chunk bound, is computed once the band loads are out: earlier it would
   // wait for this row's position before any other load is issued, later it costs registers)
   const int32_t qp32 = qvalid ? (int32_t)qp : INT32_MIN;
@@ -381,19 +385,20 @@ __global__ __launch_bounds__(NT, 2) void prefill_short_kernel(StreamArgs sa, int
   // issued, then this step's exponentials and P V.  In program order the next S^T MFMAs therefore
   // sit beside this step's exponentials, and this step's P V MFMAs beside the next step's mask and
   // max, so the matrix unit and the vector ALU work at the same time.
-  // Tiles live in NBUF = 3 buffers: the barrier before the S^T of tile t+1 waits for tile t+1's
-  // loads, and once every wavefront is past it the buffer of tile t-1 is free for tile t+2's.
+  // Tiles live in NBUF = 4 buffers: the barrier before the S^T of tile t+1 waits for tile t+1's
+  // loads (tile t+2's may still be in flight), and once every wavefront is past it the buffer of
+  // tile t-1 is free for tile t+3's.
   const int nsteps = n_tiles;
   // two score sets that trade roles every step (a step reads one and fills the other), so no
   // copy of the next step's scores has to wait for its MFMAs
   f32x16 s_a, s_b;
   auto step = [&](int s, auto phc, f32x16& sc, f32x16& s_next) {
-    constexpr int PH = decltype(phc)::value;  // position in the 6-step cycle (buffers x score sets)
+    constexpr int PH = decltype(phc)::value;  // position in the 4-step cycle (buffers x score sets)
     constexpr int buf = PH % NBUF;
     constexpr int nbuf = (buf + 1) % NBUF;
     const int t = s;
     const int jt = j_lo + t * BN;
-    const int32_t* kpt = pbuf<buf>();
+    const int32_t* kpt = g_p[buf][w];
     const int32_t kfirst = kpt[0];
     const int32_t klast = kpt[BN - 1];
     const bool full = (jt + BN <= j_hi) && ((int64_t)klast <= qmin) &&
@@ -411,10 +416,11 @@ __global__ __launch_bounds__(NT, 2) void prefill_short_kernel(StreamArgs sa, int
       }
     }
     if (!full) {
+      const int lim = j_hi - jt - 4 * hg;  // this lane's key r is in the band iff 8(r/4) + r%4 < lim
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int32_t kp = kpt[8 * (r >> 2) + 4 * hg + (r & 3)];
-        if (!(kp <= qp32 && kp >= qlo32)) sc[r] = -INFINITY;
+        if (!(kp <= qp32 && kp >= qlo32 && 8 * (r >> 2) + (r & 3) < lim)) sc[r] = -INFINITY;
       }
     }
     float mt = sc[0];
@@ -439,10 +445,9 @@ __global__ __launch_bounds__(NT, 2) void prefill_short_kernel(StreamArgs sa, int
 
     // ---- the next tile's S^T, after the crossing into it ----
     if (s + 1 < nsteps) {
-      __builtin_amdgcn_s_waitcnt(0);
-      commit_kpos(std::integral_constant<int, nbuf>());
-      __syncthreads();
-      if (t + 2 < n_tiles) issue_tile(jt + 2 * BN, std::integral_constant<int, (buf + 2) % NBUF>());
+      if (t + 2 < n_tiles) barrier_after_loads<kDmaPerTile>();  // tile t+2 may stay in flight
+      else barrier_after_loads<0>();
+      if (t + 3 < n_tiles) issue_tile(jt + 3 * BN, std::integral_constant<int, (buf + 3) % NBUF>());
     }
     // Issued unconditionally so that it shares one basic block with the exponentials and P V
     // below (the scheduler interleaves only within a block); after the last step it reads a
@@ -486,28 +491,27 @@ __global__ __launch_bounds__(NT, 2) void prefill_short_kernel(StreamArgs sa, int
       }
   };
 
-  if (j_lo != j_first && n_tiles > 0) {
-    __builtin_amdgcn_s_waitcnt(0);  // the guessed tile's loads land before the right tile's
-    issue_tile(j_lo, std::integral_constant<int, 0>());
+  // The loop's counted waits assume exactly the tiles 0 .. min(n_tiles, NBUF - 1) - 1 of the band
+  // in flight: when the guess issued others, they land first and the right ones are issued.
+  const int n_pre = min(n_tiles, NBUF - 1);
+  if (j_lo != j_first || n_first != n_pre) {
+    __builtin_amdgcn_s_waitcnt(0);
+    issue_first(j_lo, n_pre);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // also retires the early first-tile loads when n_tiles == 0
-  commit_kpos(std::integral_constant<int, 0>());
-  __syncthreads();  // the first tile and its key positions are visible to every wave
-  if (n_tiles > 1) issue_tile(j_lo + BN, std::integral_constant<int, 1>());
+  // the first tile and its key positions are then visible to every wavefront
+  if (n_pre > 2) barrier_after_loads<2 * kDmaPerTile>();
+  else if (n_pre > 1) barrier_after_loads<kDmaPerTile>();
+  else barrier_after_loads<0>();
   if (nsteps > 0) s_a = qk(std::integral_constant<int, 0>());
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   using P2 = std::integral_constant<int, 2>;
   using P3 = std::integral_constant<int, 3>;
-  using P4 = std::integral_constant<int, 4>;
-  using P5 = std::integral_constant<int, 5>;
-  for (int s = 0; s < nsteps; s += 6) {
+  for (int s = 0; s < nsteps; s += 4) {
     step(s, P0(), s_a, s_b);
     if (s + 1 < nsteps) step(s + 1, P1(), s_b, s_a);
     if (s + 2 < nsteps) step(s + 2, P2(), s_a, s_b);
     if (s + 3 < nsteps) step(s + 3, P3(), s_b, s_a);
-    if (s + 4 < nsteps) step(s + 4, P4(), s_a, s_b);
-    if (s + 5 < nsteps) step(s + 5, P5(), s_b, s_a);
   }
 
   const float ltot = lsum + swap_halves(lsum);

@@ -254,35 +254,6 @@ struct StreamLds {
 __shared__ __attribute__((aligned(16))) StreamLds g_lds;
 
 
-// One HBM -> LDS copy of 4 bytes per lane (buffer_load_dword ... lds: lane l's dword lands at
-// dst + 4 l).  Same hazards as tile_dma16.
-__device__ __forceinline__ void tile_dma4(i32x4 rsrc, const lds_void* dst, uint32_t voff) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 4\n\t"
-      "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(rsrc));
-}
-
-// Workgroup barrier ordering LDS accesses only (the fences wait for this wavefront's LDS
-// operations, not for its buffer loads); scheduling barriers keep the two phases apart.
-__device__ __forceinline__ void phase_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  __builtin_amdgcn_sched_barrier(0);
-}
-// The same after waiting until at most N of this wavefront's buffer loads are outstanding (they
-// retire in order): every wavefront's share of the tile due has then landed.
-template <int N>
-__device__ __forceinline__ void barrier_after_loads() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
-  phase_barrier();
-}
-
 // Query block, KV head and sequence of work item L.  Workgroups are dealt to the 8 XCDs
 // round-robin by id; items are numbered so that every query block of one (b, g) lands on the
 // same XCD (its K/V then stay in that XCD's L2), heaviest (latest) query blocks first.

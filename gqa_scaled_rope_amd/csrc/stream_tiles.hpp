@@ -63,6 +63,35 @@ __device__ __forceinline__ void tile_dma16_at(i32x4 rsrc, const lds_void* base, 
       : "scc");
 }
 
+// One HBM -> LDS copy of 4 bytes per lane (buffer_load_dword ... lds: lane l's dword lands at
+// dst + 4 l).  Same hazards as tile_dma16.
+__device__ __forceinline__ void tile_dma4(i32x4 rsrc, const lds_void* dst, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 4\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(rsrc));
+}
+
+// Workgroup barrier ordering LDS accesses only (the fences wait for this wavefront's LDS
+// operations, not for its buffer loads); scheduling barriers keep the two phases apart.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// The same after waiting until at most N of this wavefront's buffer loads are outstanding (they
+// retire in order): every wavefront's share of the tile due has then landed.
+template <int N>
+__device__ __forceinline__ void barrier_after_loads() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
+  phase_barrier();
+}
+
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& w) { return __builtin_bit_cast(bf16x8, w); }
 
