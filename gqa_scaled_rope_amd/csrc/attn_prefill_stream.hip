@@ -1195,8 +1195,8 @@ static int64_t mean_band_keys(const AttnArgs& a) {
 }
 // Below this many keys per workgroup (24 tiles) the four-wavefront kernel, two workgroups per CU,
 // is faster: the eight-wavefront kernel's longer pipeline start and its one workgroup per CU cost
-// more than its faster loop saves (measured: 0.28 against 0.33 ms for a 128-key window, level at
-// about 1000 keys, 6% slower at 4096).
+// more than its faster loop saves (measured: 0.25 against 0.27 ms for a 128-key window at B4,
+// L 4096, Hq 64, Hkv 8; level at about 1000 keys, 6% slower at 4096).
 constexpr int64_t kShortBandKeys = 24 * BN;
 
 bool prefill_stream_short(const AttnArgs& a, StreamKernel which) {
