@@ -1,7 +1,8 @@
 // Pieces shared by the two streaming prefill attention kernels -- attn_prefill_stream.hip (eight
 // wavefronts per workgroup, one workgroup per CU, for long key bands) and attn_prefill_short.hip
 // (four wavefronts, two workgroups per CU, for short ones): tile geometry, buffer descriptors,
-// the HBM -> LDS tile copies, the LDS swizzles, the key-band search and the argument block.
+// the HBM -> LDS tile copies and the counted-wait barriers that hand tiles to their readers,
+// the LDS swizzles, the key-band search and the argument block.
 #pragma once
 
 #include "launch.hpp"
